@@ -1,0 +1,151 @@
+"""Seeded synthetic inputs for exact attention, shared by the oracle tests,
+the GPU parity tests and the benchmark.
+
+This module holds no attention arithmetic. It only draws Gaussian tensors,
+rounds them to the stored dtype and names the workloads.
+
+The workloads follow the attention shapes the pages discuss: the
+(batch, seq_len, num_heads, head_dim) tensor layout of the PyTorch usage
+example ("FlashAttention for Efficient Training", section 4.2 "Integration
+with Popular Frameworks"), long-context causal training (section 4.1, and the
+"Impact on Long-Context AI Training" section of "How FlashAttention Optimizes
+GPU Memory for Fast AI Training"), and attention dropout fused into the
+kernel (section 3.1 "Fused Kernel Design"). No dataset or trained weights are
+involved: Q, K, V and the upstream gradient dO are i.i.d. normal draws.
+
+Recipe (fixed; the parity tests and stored expected values depend on it):
+  rng = numpy.random.default_rng(1000 + config_id)
+  q, k, v, do = four draws of rng.standard_normal([B, N, H, d], float32),
+                in that order, each multiplied by `amp` in float32
+  bf16 configs: each tensor rounded to bfloat16, round-to-nearest-even.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "workload",
+    "f32_to_bf16_bits",
+    "bf16_bits_to_f32",
+    "make_inputs",
+    "make_tensor",
+    "counted_flops",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One attention problem: shapes, dtype, mask, dropout and the seed recipe."""
+
+    config_id: int
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str  # "f32" or "bf16"
+    causal: bool
+    dropout_p: float  # stored as fp32 by the kernels and the oracle alike
+    backward: bool  # whether the workload includes the backward pass
+    amp: float = 1.0
+    dropout_seed: int = 2026
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(d) rounded to fp32, the value both sides receive."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.config_id
+
+    @property
+    def shape(self) -> tuple:
+        return (self.B, self.N, self.H, self.d)
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    1: Workload(1, "f32_B1_H1_N256_d64_full_fwd", 1, 1, 256, 64, "f32", False, 0.0, False),
+    2: Workload(2, "bf16_B4_H16_N2048_d64_causal_fwd", 4, 16, 2048, 64, "bf16", True, 0.0, False),
+    3: Workload(3, "bf16_B2_H16_N8192_d128_causal_fwdbwd", 2, 16, 8192, 128, "bf16", True, 0.0, True),
+    4: Workload(4, "bf16_B1_H16_N32768_d80_causal_fwdbwd_amp0.5", 1, 16, 32768, 80, "bf16", True, 0.0, True,
+                amp=0.5),
+    5: Workload(5, "bf16_B1_H8_N65536_d128_causal_dropout0.1_fwdbwd", 1, 8, 65536, 128, "bf16", True, 0.1, True),
+}
+
+
+def workload(config_id: int) -> Workload:
+    return WORKLOADS[config_id]
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even).
+
+    Returns the 16-bit patterns as uint16. NaN stays NaN (quiet bit set).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint32)
+    nan = np.isnan(x)
+    if nan.any():
+        r = np.where(nan, ((u >> 16) | 0x40).astype(np.uint32), r)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def make_tensor(rng: np.random.Generator, shape, amp: float, dtype: str):
+    """One Gaussian tensor in the stored dtype.
+
+    Returns (stored, values): `stored` is float32 (f32) or uint16 bf16 bit
+    patterns (bf16); `values` is the exact float32 value of each stored
+    element, which is what the oracle upcasts.
+    """
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if amp != 1.0:
+        x = (x * np.float32(amp)).astype(np.float32)
+    if dtype == "f32":
+        return x, x
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(x)
+        return bits, bf16_bits_to_f32(bits)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def make_inputs(w: Workload, with_grad: bool | None = None, N: int | None = None):
+    """Draw q, k, v (and dO) for workload `w`.
+
+    Returns a dict with keys 'q', 'k', 'v' (and 'do'), each a pair
+    (stored, values) as in `make_tensor`. `N` overrides the sequence length
+    (same seed recipe, smaller problem) for tests that need a short variant.
+    """
+    if with_grad is None:
+        with_grad = w.backward
+    shape = (w.B, N if N is not None else w.N, w.H, w.d)
+    rng = np.random.default_rng(w.seed)
+    out = {}
+    for name in ("q", "k", "v") + (("do",) if with_grad else ()):
+        out[name] = make_tensor(rng, shape, w.amp, w.dtype)
+    return out
+
+
+def counted_flops(B: int, H: int, N: int, d: int, causal: bool, backward: bool) -> tuple:
+    """FLOP convention of the headline metric: forward 4*B*H*N^2*d, halved
+    when causal; backward 2.5x forward. Returns (forward, backward)."""
+    fwd = 4.0 * B * H * N * N * d
+    if causal:
+        fwd /= 2.0
+    return fwd, (2.5 * fwd if backward else 0.0)
