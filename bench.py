@@ -1,0 +1,211 @@
+"""Benchmark: causal bf16 attention forward + backward on one MI355X.
+
+One step = the whole hot path once: fa_forward, then the three backward
+steps fa_backward runs (D preprocess, dK/dV, dQ), called individually so that
+HIP events between them time each kernel. Inputs are resident in HBM before
+the timed region. Prints one JSON line.
+
+Workload: B=2, H=16, N=8192, d=128, causal, bf16 (the N=8K headline shape);
+the N=32K, d=80 shape is reported alongside under "also".
+FLOP convention: forward 4*B*H*N^2*d, halved for causal; backward 2.5x.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import WORKLOADS, counted_flops, make_inputs  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+METRIC = "attention fwd+bwd TFLOP/s & % of bf16 MFMA peak, causal, N=8K/32K"
+
+
+def _device_inputs(w, torch):
+    inp = make_inputs(w, with_grad=True)
+    return {k: torch.from_numpy(v[0].view(np.int16)).view(torch.bfloat16).cuda() for k, v in inp.items()}
+
+
+def kernel_units(w):
+    """Algorithmic MFMA FLOPs per launch of each kernel: 2*d per matrix
+    product per counted score element (B*H*N^2, halved when causal).
+    forward: S and P V (2 products); dK/dV: S, dP, dV, dK (4);
+    dQ: S, dP, dQ (3). The D preprocess is bandwidth-bound: its bytes are
+    O and dO read plus D written."""
+    elems = w.B * w.H * float(w.N) * w.N / (2.0 if w.causal else 1.0)
+    tensor_bytes = w.B * w.N * w.H * w.d * 2
+    return {
+        "forward": ("mfma", 2 * 2 * w.d * elems),
+        "bwd_preprocess": ("hbm", 2 * tensor_bytes + 4 * w.B * w.H * w.N),
+        "bwd_dkdv": ("mfma", 4 * 2 * w.d * elems),
+        "bwd_dq": ("mfma", 3 * 2 * w.d * elems),
+    }
+
+
+def run_gpu(w, steps, warmup, torch, fa):
+    dev = _device_inputs(w, torch)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    args = (w.causal, w.dropout_p, w.dropout_seed, w.scale)
+    names = ("forward", "bwd_preprocess", "bwd_dkdv", "bwd_dq")
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        fa.forward(q, k, v, *args, out=o, lse=lse)
+        if ev:
+            ev[1].record()
+        fa.backward_preprocess(o, do, workspace=ws)
+        if ev:
+            ev[2].record()
+        fa.backward_dkdv(q, k, v, do, lse, ws, *args, dk=dk, dv=dv)
+        if ev:
+            ev[3].record()
+        fa.backward_dq(q, k, v, do, lse, ws, *args, dq=dq)
+        if ev:
+            ev[4].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = evs[0][0].elapsed_time(evs[-1][4]) / steps
+    per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    fwd_f, bwd_f = counted_flops(w.B, w.H, w.N, w.d, w.causal, True)
+    fwd_ms = per["forward"]
+    bwd_ms = per["bwd_preprocess"] + per["bwd_dkdv"] + per["bwd_dq"]
+    return {
+        "ms_per_step": ms_step,
+        "wall_s": wall,
+        "tflops": (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12,
+        "fwd_ms": fwd_ms,
+        "bwd_ms": bwd_ms,
+        "fwd_tflops": fwd_f / (fwd_ms * 1e-3) / 1e12,
+        "bwd_tflops": bwd_f / (bwd_ms * 1e-3) / 1e12,
+        "kernel_ms": per,
+    }
+
+
+def roofline(w, kernel_ms):
+    units = kernel_units(w)
+    name = max(kernel_ms, key=kernel_ms.get)
+    bound, work = units[name]
+    sec = kernel_ms[name] * 1e-3
+    if bound == "mfma":
+        achieved, peak, unit = work / sec / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = work / sec / 1e9, PEAK_HBM_GBS, "GB/s"
+    return {"kernel": name, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "avg_ms": kernel_ms[name], "work_per_launch": work,
+            "traffic": None}
+
+
+def cpu_baseline(w, seconds):
+    """The fp64 oracle (as it stands) on whole heads of the same workload,
+    one head at a time until about `seconds` have passed."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = None
+    inp = make_inputs(w, with_grad=True)
+    vals = {k: v[1] for k, v in inp.items()}
+    fwd_f, bwd_f = counted_flops(1, 1, w.N, w.d, w.causal, True)
+    done, t0 = 0, time.perf_counter()
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    for bh in heads:
+        oracle.forward(vals["q"], vals["k"], vals["v"], w.scale, w.causal, w.dropout_p, w.dropout_seed,
+                       heads=[bh])
+        oracle.backward(vals["q"], vals["k"], vals["v"], vals["do"], w.scale, w.causal, w.dropout_p,
+                        w.dropout_seed, heads=[bh], check_d=False)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done * (fwd_f + bwd_f) / el / 1e12, "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads (full N={w.N}, fwd+bwd, fp64 numpy) in {el:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--also", type=int, nargs="*", default=[4])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print("bench.py measures one GPU: the attention kernels run on a single device and this build "
+              "has no multi-GPU path (heads or sequence chunks would be sharded across GPUs); "
+              "run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_io_aware_72_amd as fa
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    fa.lib()  # fails loudly if the HIP library is missing
+
+    w = WORKLOADS[a.workload]
+    r = run_gpu(w, a.steps, a.warmup, torch, fa)
+    line = {
+        "metric": METRIC,
+        "value": r["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "dropout_p": w.dropout_p, "global_batch": w.B, "seq_len": w.N,
+                   "parallelism": "single-gpu"},
+        "pct_of_peak": 100.0 * r["tflops"] / PEAK_BF16_TFLOPS,
+        "fwd_ms": r["fwd_ms"], "bwd_ms": r["bwd_ms"],
+        "fwd_tflops": r["fwd_tflops"], "bwd_tflops": r["bwd_tflops"],
+        "kernel_ms": r["kernel_ms"],
+        "roofline": roofline(w, r["kernel_ms"]),
+    }
+    also = []
+    for cfg in a.also:
+        wa = WORKLOADS[cfg]
+        ra = run_gpu(wa, max(3, a.steps // 4), 2, torch, fa)
+        also.append({"workload": wa.name, "tflops": ra["tflops"], "ms_per_step": ra["ms_per_step"],
+                     "pct_of_peak": 100.0 * ra["tflops"] / PEAK_BF16_TFLOPS,
+                     "fwd_tflops": ra["fwd_tflops"], "bwd_tflops": ra["bwd_tflops"],
+                     "kernel_ms": ra["kernel_ms"], "roofline": roofline(wa, ra["kernel_ms"])})
+        torch.cuda.empty_cache()
+    line["also"] = also
+    line["cpu_baseline"] = None if a.no_cpu_baseline else cpu_baseline(w, a.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

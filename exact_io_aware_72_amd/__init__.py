@@ -1,0 +1,264 @@
+"""Exact IO-aware attention for AMD MI355X (gfx950): Python binding.
+
+This module only marshals arguments into libfa.so, the C-ABI library whose
+HIP kernels run every step of the forward and backward passes; torch supplies
+device memory and the current HIP stream. There is no fallback: if the
+library is missing, every call raises.
+
+Usage mirrors the drop-in PyTorch call of "FlashAttention for Efficient
+Training", section 4.2: tensors of shape (batch, seq_len, num_heads,
+head_dim), `flash_attention(q, k, v)` returns the attention output, and the
+autograd backward recomputes attention from the saved logsumexp.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FAError", "lib", "lib_path", "version", "forward", "backward", "backward_preprocess",
+    "backward_dkdv", "backward_dq", "workspace_bytes", "dropout_mask", "FlashAttnFunction",
+    "flash_attention", "EXPORTED_SYMBOLS", "STATUS",
+]
+
+FA_F32, FA_BF16 = 0, 1
+STATUS = {
+    0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_HEADDIM", -4: "FA_ERR_DTYPE",
+    -5: "FA_ERR_DROPOUT", -6: "FA_ERR_ALIGN", -7: "FA_ERR_UNSUPPORTED", -8: "FA_ERR_HIP",
+    -9: "FA_ERR_ARG",
+}
+EXPORTED_SYMBOLS = (
+    "fa_forward", "fa_backward", "fa_backward_workspace_bytes", "fa_backward_preprocess",
+    "fa_backward_dkdv", "fa_backward_dq", "fa_dropout_mask", "fa_status_string", "fa_version",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libfa.so")
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        name = STATUS.get(status, str(status))
+        super().__init__(f"{where}: {name} ({detail})" if detail else f"{where}: {name}")
+
+
+_vp, _i, _f, _u64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, ctypes.c_size_t
+_SIGS = {
+    "fa_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
+    "fa_backward_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "fa_backward": (_i, [_vp] * 10 + [_i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
+    "fa_backward_preprocess": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _i]),
+    "fa_backward_dkdv": (_i, [_vp] * 8 + [_i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
+    "fa_backward_dq": (_i, [_vp] * 7 + [_i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
+    "fa_dropout_mask": (_i, [_u64, _i, _i, _i, _f, _i, _i, _i, _i, _vp, _vp]),
+    "fa_status_string": (ctypes.c_char_p, [_i]),
+    "fa_version": (ctypes.c_char_p, []),
+}
+
+
+def lib():
+    """The loaded libfa.so (ctypes), with argument types set."""
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise FAError(-7, "load", f"{path} is not built; run __graft_entry__.build() "
+                                       "or python -m exact_io_aware_72_amd.build")
+        handle = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def version() -> str:
+    return lib().fa_version().decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise FAError(status, where, lib().fa_status_string(status).decode())
+
+
+def workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().fa_backward_workspace_bytes(B, H, N, d))
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers
+def _torch():
+    import torch
+    return torch
+
+
+def _code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _shape(q, *others):
+    if q.dim() != 4:
+        raise ValueError("expected tensors of shape (batch, seq_len, num_heads, head_dim)")
+    for t in (q,) + others:
+        if t.shape != q.shape:
+            raise ValueError(f"shape mismatch: {tuple(t.shape)} vs {tuple(q.shape)}")
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v (and o, dout) must share one dtype")
+        if t.device != q.device or t.device.type != "cuda":
+            raise ValueError("tensors must live on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    B, N, H, d = q.shape
+    return B, N, H, d
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _scale(scale, d):
+    return float(1.0 / math.sqrt(d)) if scale is None else float(scale)
+
+
+def forward(q, k, v, causal=False, dropout_p=0.0, seed=0, scale=None, out=None, lse=None):
+    """Returns (o, lse): o like q; lse float32 (B, H, N), natural log."""
+    torch = _torch()
+    B, N, H, d = _shape(q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _shape(q, o)
+    st = lib().fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
+                          B, H, N, d, _scale(scale, d), int(bool(causal)), float(dropout_p),
+                          int(seed), _stream(q), _code(q))
+    _check(st, "fa_forward")
+    return o, lse_t
+
+
+def backward(q, k, v, o, dout, lse, causal=False, dropout_p=0.0, seed=0, scale=None,
+             dq=None, dk=None, dv=None, workspace=None):
+    """Returns (dq, dk, dv) for L = sum(dout * o)."""
+    torch = _torch()
+    B, N, H, d = _shape(q, k, v, o, dout)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    ws = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if workspace is None else workspace
+    st = lib().fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                           ws.data_ptr(), B, H, N, d, _scale(scale, d), int(bool(causal)),
+                           float(dropout_p), int(seed), _stream(q), _code(q))
+    _check(st, "fa_backward")
+    return dq, dk, dv
+
+
+def backward_preprocess(o, dout, workspace=None):
+    """Step B1 alone: returns D = rowsum(dout * o) as float32 (B, H, N)."""
+    torch = _torch()
+    B, N, H, d = _shape(o, dout)
+    ws = torch.empty((B, H, N), dtype=torch.float32, device=o.device) if workspace is None else workspace
+    st = lib().fa_backward_preprocess(o.data_ptr(), dout.data_ptr(), ws.data_ptr(), B, H, N, d,
+                                      _stream(o), _code(o))
+    _check(st, "fa_backward_preprocess")
+    return ws
+
+
+def backward_dkdv(q, k, v, dout, lse, workspace, causal=False, dropout_p=0.0, seed=0, scale=None,
+                  dk=None, dv=None):
+    """Step B2 alone: returns (dk, dv)."""
+    torch = _torch()
+    B, N, H, d = _shape(q, k, v, dout)
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    st = lib().fa_backward_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                lse.data_ptr(), workspace.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                B, H, N, d, _scale(scale, d), int(bool(causal)), float(dropout_p),
+                                int(seed), _stream(q), _code(q))
+    _check(st, "fa_backward_dkdv")
+    return dk, dv
+
+
+def backward_dq(q, k, v, dout, lse, workspace, causal=False, dropout_p=0.0, seed=0, scale=None,
+                dq=None):
+    """Step B3 alone: returns dq."""
+    torch = _torch()
+    B, N, H, d = _shape(q, k, v, dout)
+    dq = torch.empty_like(q) if dq is None else dq
+    st = lib().fa_backward_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                              lse.data_ptr(), workspace.data_ptr(), dq.data_ptr(), B, H, N, d,
+                              _scale(scale, d), int(bool(causal)), float(dropout_p), int(seed),
+                              _stream(q), _code(q))
+    _check(st, "fa_backward_dq")
+    return dq
+
+
+def dropout_mask(seed, b, h, H, dropout_p, row0, col0, rows, cols, device="cuda"):
+    """Keep mask (uint8, rows x cols) of head (b, h), from the kernels' hash."""
+    torch = _torch()
+    out = torch.empty((rows, cols), dtype=torch.uint8, device=device)
+    st = lib().fa_dropout_mask(int(seed), b, h, H, float(dropout_p), row0, col0, rows, cols,
+                               out.data_ptr(), _stream(out))
+    _check(st, "fa_dropout_mask")
+    return out
+
+
+def _autograd_function():
+    torch = _torch()
+
+    class FlashAttnFunction(torch.autograd.Function):
+        """Autograd wrapper: forward saves (q, k, v, o, lse); backward
+        recomputes the attention probabilities from them."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, causal=False, dropout_p=0.0, seed=0, scale=None):
+            q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+            o, lse = forward(q, k, v, causal, dropout_p, seed, scale)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.args = (causal, dropout_p, seed, scale)
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, o, lse = ctx.saved_tensors
+            causal, dropout_p, seed, scale = ctx.args
+            dq, dk, dv = backward(q, k, v, o, do.contiguous(), lse, causal, dropout_p, seed, scale)
+            return dq, dk, dv, None, None, None, None
+
+    return FlashAttnFunction
+
+
+class _Lazy:
+    _fn = None
+
+    def __get__(self, obj, owner):
+        if _Lazy._fn is None:
+            _Lazy._fn = _autograd_function()
+        return _Lazy._fn
+
+
+class _Namespace:
+    FlashAttnFunction = _Lazy()
+
+
+def __getattr__(name):
+    if name == "FlashAttnFunction":
+        return _Namespace.FlashAttnFunction
+    raise AttributeError(name)
+
+
+def flash_attention(q, k, v, causal=False, dropout_p=0.0, seed=0, scale=None):
+    """O = softmax(q k^T * scale) v over (batch, seq_len, num_heads, head_dim)
+    tensors, differentiable through FlashAttnFunction."""
+    return _Namespace.FlashAttnFunction.apply(q, k, v, causal, dropout_p, seed, scale)

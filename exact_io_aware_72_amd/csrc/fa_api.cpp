@@ -1,0 +1,221 @@
+// C ABI of the attention library: argument validation, status codes and
+// dispatch to the gfx950 kernels. Every check runs before any HIP call, so a
+// rejected call launches nothing and writes nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "../../include/fa.h"
+#include "fa_kernels.h"
+
+#define FA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_hip_error = "no HIP error recorded";
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  g_hip_error = std::string("HIP error ") + std::to_string((int)e) + ": " + hipGetErrorString(e);
+  return FA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape, head-dim and dtype rules shared by every tensor entry point.
+int check_problem(int B, int H, int N, int d, int dtype) {
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 80 && d != 128) return FA_ERR_HEADDIM;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  // Element count must fit comfortably in 64-bit byte offsets, and grids
+  // (at most one work-group per 16 rows, or per 32-row block per head) in
+  // 32 bits.
+  const int64_t rows = (int64_t)B * N * H;
+  if (rows > (int64_t)1 << 36) return FA_ERR_SHAPE;
+  if ((rows + 15) / 16 > (int64_t)INT32_MAX) return FA_ERR_SHAPE;
+  if ((int64_t)((N + 31) / 32) * B * H > (int64_t)INT32_MAX) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_dropout(float p) {
+  if (!(p >= 0.0f && p < 1.0f)) return FA_ERR_DROPOUT;  // also rejects NaN
+  return FA_OK;
+}
+
+int check_scale(float scale) { return std::isfinite(scale) ? FA_OK : FA_ERR_ARG; }
+
+void set_dropout(fa::AttnArgs& a, float p, uint64_t seed) {
+  a.dropout = p > 0.0f;
+  a.seed = seed;
+  a.drop_threshold = (uint32_t)std::floor((double)p * 4294967296.0);
+  a.drop_rescale = (float)(1.0 / (1.0 - (double)p));
+}
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p == nullptr) return FA_ERR_NULL;
+  for (const void* p : ps)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+#define FA_TRY(x)             \
+  do {                        \
+    const int st_ = (x);      \
+    if (st_ != FA_OK) return st_; \
+  } while (0)
+
+}  // namespace
+
+FA_EXPORT int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int H, int N, int d, float scale, int causal, float dropout_p,
+                         uint64_t seed, void* stream, int dtype) {
+  FA_TRY(check_problem(B, H, N, d, dtype));
+  FA_TRY(check_dropout(dropout_p));
+  FA_TRY(check_scale(scale));
+  FA_TRY(check_ptrs({q, k, v, o, lse}));
+  fa::AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o_out = o;
+  a.lse_out = lse;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  set_dropout(a, dropout_p, seed);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(dtype == FA_BF16 ? fa::launch_forward_bf16(a, s)
+                                     : fa::launch_forward_f32(a, s));
+}
+
+FA_EXPORT size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
+  if (check_problem(B, H, N, d, FA_BF16) != FA_OK) return 0;
+  return (size_t)4 * (size_t)B * (size_t)H * (size_t)N;
+}
+
+FA_EXPORT int fa_backward_preprocess(const void* o, const void* dout, float* workspace, int B,
+                                     int H, int N, int d, void* stream, int dtype) {
+  FA_TRY(check_problem(B, H, N, d, dtype));
+  FA_TRY(check_ptrs({o, dout, workspace}));
+  fa::AttnArgs a;
+  a.o = o;
+  a.dout = dout;
+  a.dsum_out = workspace;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  return hip_status(fa::launch_bwd_preprocess(a, static_cast<hipStream_t>(stream),
+                                              dtype == FA_BF16));
+}
+
+namespace {
+int fill_bwd(fa::AttnArgs& a, const void* q, const void* k, const void* v, const void* dout,
+             const float* lse, const float* ws, int B, int H, int N, int d, float scale,
+             int causal, float dropout_p, uint64_t seed, int dtype) {
+  FA_TRY(check_problem(B, H, N, d, dtype));
+  FA_TRY(check_dropout(dropout_p));
+  FA_TRY(check_scale(scale));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.dsum = ws;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  set_dropout(a, dropout_p, seed);
+  return FA_OK;
+}
+}  // namespace
+
+FA_EXPORT int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                               const float* lse, const float* workspace, void* dk, void* dv, int B,
+                               int H, int N, int d, float scale, int causal, float dropout_p,
+                               uint64_t seed, void* stream, int dtype) {
+  fa::AttnArgs a;
+  FA_TRY(fill_bwd(a, q, k, v, dout, lse, workspace, B, H, N, d, scale, causal, dropout_p, seed,
+                  dtype));
+  FA_TRY(check_ptrs({q, k, v, dout, lse, workspace, dk, dv}));
+  a.dk = dk;
+  a.dv = dv;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(dtype == FA_BF16 ? fa::launch_bwd_dkdv_bf16(a, s)
+                                     : fa::launch_bwd_dkdv_f32(a, s));
+}
+
+FA_EXPORT int fa_backward_dq(const void* q, const void* k, const void* v, const void* dout,
+                             const float* lse, const float* workspace, void* dq, int B, int H,
+                             int N, int d, float scale, int causal, float dropout_p, uint64_t seed,
+                             void* stream, int dtype) {
+  fa::AttnArgs a;
+  FA_TRY(fill_bwd(a, q, k, v, dout, lse, workspace, B, H, N, d, scale, causal, dropout_p, seed,
+                  dtype));
+  FA_TRY(check_ptrs({q, k, v, dout, lse, workspace, dq}));
+  a.dq = dq;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(dtype == FA_BF16 ? fa::launch_bwd_dq_bf16(a, s)
+                                     : fa::launch_bwd_dq_f32(a, s));
+}
+
+FA_EXPORT int fa_backward(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          float* workspace, int B, int H, int N, int d, float scale, int causal,
+                          float dropout_p, uint64_t seed, void* stream, int dtype) {
+  fa::AttnArgs a;
+  FA_TRY(fill_bwd(a, q, k, v, dout, lse, workspace, B, H, N, d, scale, causal, dropout_p, seed,
+                  dtype));
+  FA_TRY(check_ptrs({q, k, v, o, dout, lse, dq, dk, dv, workspace}));
+  a.o = o;
+  a.dsum_out = workspace;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == FA_BF16;
+  FA_TRY(hip_status(fa::launch_bwd_preprocess(a, s, bf16)));
+  FA_TRY(hip_status(bf16 ? fa::launch_bwd_dkdv_bf16(a, s) : fa::launch_bwd_dkdv_f32(a, s)));
+  return hip_status(bf16 ? fa::launch_bwd_dq_bf16(a, s) : fa::launch_bwd_dq_f32(a, s));
+}
+
+FA_EXPORT int fa_dropout_mask(uint64_t seed, int b, int h, int H, float dropout_p, int row0,
+                              int col0, int rows, int cols, uint8_t* out, void* stream) {
+  FA_TRY(check_dropout(dropout_p));
+  if (out == nullptr) return FA_ERR_NULL;
+  if (H < 1 || b < 0 || h < 0 || h >= H || row0 < 0 || col0 < 0 || rows < 1 || cols < 1)
+    return FA_ERR_ARG;
+  if ((int64_t)rows * cols >= ((int64_t)1 << 31)) return FA_ERR_ARG;
+  if ((int64_t)row0 + rows > INT32_MAX || (int64_t)col0 + cols > INT32_MAX) return FA_ERR_ARG;
+  const uint32_t thr = (uint32_t)std::floor((double)dropout_p * 4294967296.0);
+  return hip_status(fa::launch_dropout_mask(seed, b, h, H, thr, row0, col0, rows, cols, out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+FA_EXPORT const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape: B, H, N must be >= 1 and sizes must fit";
+    case FA_ERR_HEADDIM: return "unsupported head dimension (supported: 64, 80, 128)";
+    case FA_ERR_DTYPE: return "unsupported dtype (FA_F32 or FA_BF16)";
+    case FA_ERR_DROPOUT: return "dropout_p must lie in [0, 1)";
+    case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case FA_ERR_UNSUPPORTED: return "request not supported by this build";
+    case FA_ERR_HIP: return g_hip_error.c_str();
+    case FA_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+FA_EXPORT const char* fa_version(void) { return "fa-mi355x 0.1.0 gfx950"; }

@@ -1,0 +1,131 @@
+// Device helpers for the gfx950 attention kernels: vector types, the bf16
+// matrix-core instruction, LDS/global 128-bit accesses, bf16 packing, and the
+// contraction-index permutation that lets a score tile held in accumulator
+// registers feed the next matrix product without going through LDS.
+//
+// Matrix-core layout used throughout (v_mfma_f32_32x32x16_bf16, wave64):
+//   A (32 x 16, row m, column k):  lane L holds A[L % 32][8*(L/32) + j], j = 0..7
+//   B (16 x 32, row k, column n):  lane L holds B[8*(L/32) + j][L % 32], j = 0..7
+//   C (32 x 32):                   lane L, register r holds
+//                                  C[8*(r/4) + 4*(L/32) + (r%4)][L % 32], r = 0..15
+// The pairing of A and B elements along k is by (L/32, j) for both operands,
+// so any relabelling of k applied to both operands leaves the product
+// unchanged. A C tile therefore serves directly as the B operand of a product
+// that contracts over its row index, provided the A operand is read with the
+// same relabelling: for the 16 rows 16t..16t+15 of a C tile, lane half s
+// supplies rows {16t + 4s + 0..3, 16t + 8 + 4s + 0..3}; LDS copies that feed
+// the matching A operand store those 8 rows contiguously (perm_pos below).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kWave = 64;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Two floats -> two bf16 (round to nearest even) in one 32-bit word, lo first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Hardware base-2 exponential and logarithm (v_exp_f32 / v_log_f32).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ u32x4 ld_global_128(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st_global_64(void* p, u32x2 v) {
+  *reinterpret_cast<u32x2*>(p) = v;
+}
+__device__ __forceinline__ u32x4 ld_lds_128(const char* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+__device__ __forceinline__ void st_lds_128(char* base, int off, u32x4 v) {
+  *reinterpret_cast<u32x4*>(base + off) = v;
+}
+__device__ __forceinline__ void st_lds_64(char* base, int off, u32x2 v) {
+  *reinterpret_cast<u32x2*>(base + off) = v;
+}
+__device__ __forceinline__ f32x4 ld_lds_f32x4(const char* base, int off) {
+  return *reinterpret_cast<const f32x4*>(base + off);
+}
+__device__ __forceinline__ u32x4 ld_lds_u32x4(const char* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+
+// Row index within a 32-row C tile held by accumulator register r of lane half s.
+__device__ __forceinline__ constexpr int c_row(int r, int s) { return 8 * (r >> 2) + 4 * s + (r & 3); }
+
+// Position in a permuted LDS copy of the first of 4 consecutive contraction
+// indices 4g..4g+3: within each group of 16, the 4-blocks are stored in the
+// order 0, 2, 1, 3 so that lane half s reads its 8 indices as one 16-byte run
+// starting at 16t + 8s.
+__device__ __forceinline__ int perm_pos4(int g) {
+  const int q = g & 3;
+  const int qp = (q == 1) ? 2 : (q == 2) ? 1 : q;
+  return ((g >> 2) << 4) | (qp << 2);
+}
+
+// Transposing store: four 16-byte rows (rows 4g..4g+3 of a tile, 8 columns
+// 8c..8c+7 each, bf16) written as 8 columns of a column-major copy:
+// dst[(8c + e) * stride + pos*2 .. +8] = {row0[e], row1[e], row2[e], row3[e]}.
+__device__ __forceinline__ void st_lds_transpose4x8(char* base, int row_bytes, int col0, int pos,
+                                                    const u32x4& r0, const u32x4& r1,
+                                                    const u32x4& r2, const u32x4& r3) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t a = r0[w], b = r1[w], c = r2[w], d = r3[w];
+    const u32x2 even = {(a & 0xffffu) | (b << 16), (c & 0xffffu) | (d << 16)};
+    const u32x2 odd = {(a >> 16) | (b & 0xffff0000u), (c >> 16) | (d & 0xffff0000u)};
+    st_lds_64(base, (col0 + 2 * w) * row_bytes + pos * 2, even);
+    st_lds_64(base, (col0 + 2 * w + 1) * row_bytes + pos * 2, odd);
+  }
+}
+
+// Maps a linear work-group id to (block, batch*heads index). All blocks of a
+// (b, h) pair land on the same XCD (work-groups are dispatched round-robin
+// over the 8 XCDs), so K/V tiles re-read by neighbouring blocks stay in that
+// XCD's L2. `rank` runs from the first-dispatched to the last-dispatched
+// block of an XCD; callers turn it into a block index (heaviest first).
+struct BlockMap {
+  int rank;
+  int bh;
+};
+__device__ __forceinline__ BlockMap map_block(int id, int nblk, int BH) {
+  BlockMap m;
+  if ((BH & 7) == 0) {
+    const int xcd = id & 7;
+    const int local = id >> 3;
+    const int hpx = BH >> 3;
+    m.rank = local / hpx;
+    m.bh = xcd * hpx + (local - m.rank * hpx);
+  } else {
+    m.rank = id / BH;
+    m.bh = id - m.rank * BH;
+  }
+  (void)nblk;
+  return m;
+}
+
+}  // namespace fa

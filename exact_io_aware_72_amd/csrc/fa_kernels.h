@@ -1,0 +1,46 @@
+// Internal launch interface between the C ABI (fa_api.cpp) and the kernels.
+// Arguments are validated by the caller before any of these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct AttnArgs {
+  // inputs
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const void* o = nullptr;     // forward output, read by the backward
+  const void* dout = nullptr;  // upstream gradient dO
+  const float* lse = nullptr;  // [B][H][N] natural-log logsumexp
+  const float* dsum = nullptr; // [B][H][N] D = rowsum(dO * O)
+  // outputs
+  void* o_out = nullptr;
+  float* lse_out = nullptr;
+  float* dsum_out = nullptr;
+  void* dq = nullptr;
+  void* dk = nullptr;
+  void* dv = nullptr;
+  // problem
+  int B = 0, H = 0, N = 0, d = 0;
+  float scale = 0.f;
+  bool causal = false;
+  bool dropout = false;
+  uint32_t drop_threshold = 0;  // keep iff hash >= threshold
+  float drop_rescale = 1.f;     // 1 / (1 - p) in fp32
+  uint64_t seed = 0;
+};
+
+hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_forward_f32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t s, bool bf16);
+hipError_t launch_bwd_dkdv_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_bwd_dq_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_bwd_dkdv_f32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_bwd_dq_f32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_dropout_mask(uint64_t seed, int b, int h, int H, uint32_t threshold, int row0,
+                               int col0, int rows, int cols, uint8_t* out, hipStream_t s);
+
+}  // namespace fa

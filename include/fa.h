@@ -1,0 +1,153 @@
+/*
+ * fa.h — C ABI of the exact IO-aware attention library for AMD MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention
+ *     O = softmax(Q K^T * scale) V,     scale = 1/sqrt(d) normally,
+ * tile by tile, with an online softmax, never writing the N x N score or
+ * probability matrices to device memory, and saving the per-row logsumexp so
+ * that the backward pass recomputes the probabilities instead of storing them.
+ * ("FlashAttention for Efficient Training", sections 2.1 "Forward Pass with
+ * Recomputation", 3.1 "Workflow Breakdown" and 3.2 "Precision Handling and
+ * Numerical Stability"; "How FlashAttention Optimizes GPU Memory for Fast AI
+ * Training", sections "1. Tiling", "2. Online Softmax", "3. Kernel Fusion" and
+ * "4. Recomputation in the Backward Pass".)
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors q, k, v, o, dout, dq, dk, dv are contiguous [B][N][H][d] arrays
+ *     (the (batch, seq_len, num_heads, head_dim) layout of the PyTorch usage
+ *     example, section 4.2 of the first page) of the element type `dtype`.
+ *     lse and the backward workspace are contiguous [B][H][N] float arrays.
+ *   - Every pointer is a DEVICE pointer owned by the caller, aligned to 16
+ *     bytes. The library never allocates, frees, or synchronises, and keeps no
+ *     mutable global state: all calls are safe from several host threads.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *     is enqueued on it and the call returns without waiting; FA_OK means
+ *     "enqueued". Device faults surface at the caller's next synchronisation.
+ *   - Arguments are validated before any HIP call; on any error nothing is
+ *     launched and nothing is written. No C++ exception crosses this ABI.
+ *   - Supported: d in {64, 80, 128}; any N >= 1 (tails handled by masks);
+ *     dtype FA_BF16 (bf16 storage, fp32 accumulation, bf16 matrix cores) or
+ *     FA_F32 (fp32 throughout). Causal masking keeps key j for query i iff
+ *     j <= i (queries and keys share positions 0..N-1).
+ *   - Dropout: 0 <= dropout_p < 1. Probabilities are dropped after the
+ *     softmax normalisation with the keep mask of a counter hash of
+ *     (seed, b, h, row, col) and kept ones are scaled by 1/(1 - dropout_p);
+ *     the logsumexp is that of the undropped probabilities. `seed` is used
+ *     only when dropout_p > 0. The backward pass must receive the same
+ *     (dropout_p, seed) as the forward pass. The hash is specified in the
+ *     comment of fa_dropout_mask below.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  FA_ERR_SHAPE = -2,       /* B, H or N < 1, or a size overflows                 */
+  FA_ERR_HEADDIM = -3,     /* d not in {64, 80, 128}                             */
+  FA_ERR_DTYPE = -4,       /* dtype not FA_F32 / FA_BF16                         */
+  FA_ERR_DROPOUT = -5,     /* dropout_p outside [0, 1) or NaN                    */
+  FA_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned                   */
+  FA_ERR_UNSUPPORTED = -7, /* valid request this build does not implement       */
+  FA_ERR_HIP = -8,         /* a HIP runtime call failed; see fa_status_string    */
+  FA_ERR_ARG = -9          /* other invalid argument (non-finite scale, window)  */
+} fa_status;
+
+/*
+ * Forward pass (steps: stage Q tile, stream K/V tiles, S = scale*Q K^T,
+ * causal tile skip and mask, online softmax, dropout, O += P V, epilogue).
+ *   q, k, v  [B][N][H][d] inputs (dtype)
+ *   o        [B][N][H][d] output (dtype): O = (P o Z / (1-p)) V
+ *   lse      [B][H][N] float output: natural-log logsumexp of the scaled,
+ *            masked scores of each query row (undropped)
+ *   scale    multiplier of Q K^T (finite); normally 1/sqrt(d)
+ *   causal   0 = full attention, nonzero = causal mask
+ * Definition: "FlashAttention for Efficient Training", section 1.1
+ * (Attention(Q,K,V)), section 3.1 (S_ij = Q_i K_j^T / sqrt(d_k), online
+ * softmax) and section 3.2 (log_softmax = x - logsumexp(x)).
+ */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal,
+               float dropout_p, uint64_t seed, void* stream, int dtype);
+
+/* Bytes of the float workspace fa_backward needs: 4*B*H*N (the row terms
+ * D_i = sum_c dO_ic O_ic). Returns 0 if the sizes are invalid. */
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward pass. Runs fa_backward_preprocess, fa_backward_dkdv and
+ * fa_backward_dq on `stream`, in that order.
+ *   q, k, v, o, dout  [B][N][H][d] (dtype); o and lse from fa_forward with
+ *                     the same arguments
+ *   lse               [B][H][N] float from fa_forward
+ *   dq, dk, dv        [B][N][H][d] outputs (dtype), fully overwritten
+ *   workspace         float array of fa_backward_workspace_bytes(...) bytes;
+ *                     receives D = rowsum(dout o o) as [B][H][N]
+ * Gradients of L = sum(dout o O): dV = P~^T dO ("FlashAttention for Efficient
+ * Training", section 3.2 "Integration with Autograd Engines"), dQ and dK by
+ * the chain rule of the same section: dP = (dO V^T) o Z/(1-p),
+ * dS = P o (dP - D), dQ = scale dS K, dK = scale dS^T Q. No atomics: results
+ * are bitwise reproducible run to run.
+ */
+int fa_backward(const void* q, const void* k, const void* v, const void* o,
+                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                float* workspace, int B, int H, int N, int d, float scale,
+                int causal, float dropout_p, uint64_t seed, void* stream, int dtype);
+
+/* Step B1 alone: workspace[b][h][i] = sum_c dout[b][i][h][c] * o[b][i][h][c]
+ * in fp32. Same argument rules as fa_backward. */
+int fa_backward_preprocess(const void* o, const void* dout, float* workspace,
+                           int B, int H, int N, int d, void* stream, int dtype);
+
+/* Step B2 alone: dk and dv, one work-group per key block, looping over the
+ * query blocks that see it. Needs the workspace written by step B1. */
+int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                     const float* lse, const float* workspace, void* dk, void* dv,
+                     int B, int H, int N, int d, float scale, int causal,
+                     float dropout_p, uint64_t seed, void* stream, int dtype);
+
+/* Step B3 alone: dq, one work-group per query block, looping over the key
+ * blocks it sees. Needs the workspace written by step B1. */
+int fa_backward_dq(const void* q, const void* k, const void* v, const void* dout,
+                   const float* lse, const float* workspace, void* dq,
+                   int B, int H, int N, int d, float scale, int causal,
+                   float dropout_p, uint64_t seed, void* stream, int dtype);
+
+/*
+ * Writes the dropout keep mask of head (b, h) for rows row0..row0+rows-1 and
+ * columns col0..col0+cols-1 to out[rows][cols] (device, 1 = keep), with the
+ * same device function the kernels use. The pages fuse dropout into the
+ * kernel without naming a generator; this library's generator is:
+ *   G = 0x9E3779B97F4A7C15;  mix64 = SplitMix64 output function;
+ *   fmix32 = MurmurHash3 32-bit finalizer;
+ *   K_bh = mix64(seed + G*(1 + b*H + h));
+ *   A_i = lo32(mix64(K_bh + G*(2i+1)));  B_j = lo32(mix64(K_bh + G*(2j+2)));
+ *   keep(i, j) = fmix32(A_i ^ B_j) >= floor(dropout_p * 2^32)   (all mod 2^64 / 2^32).
+ * Requires 0 <= b, 0 <= h < H, row0, col0 >= 0, rows, cols >= 1,
+ * rows * cols < 2^31, out non-NULL (any alignment).
+ */
+int fa_dropout_mask(uint64_t seed, int b, int h, int H, float dropout_p,
+                    int row0, int col0, int rows, int cols, uint8_t* out,
+                    void* stream);
+
+/* Human-readable text for a status code. For FA_ERR_HIP it carries the HIP
+ * error of the last failing call on this host thread. Never NULL. */
+const char* fa_status_string(int status);
+
+/* Library version string, e.g. "fa-mi355x 0.1.0 gfx950". */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

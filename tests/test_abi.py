@@ -1,0 +1,122 @@
+"""The C-ABI library: it loads, exports every symbol include/fa.h declares,
+and rejects invalid arguments with the documented status before any HIP call.
+CPU only: no call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_io_aware_72_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa.lib_path()), reason="libfa.so not built")
+
+OK, NULL, SHAPE, HEADDIM, DTYPE, DROPOUT, ALIGN, UNSUP, HIP, ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+P = 0x10000  # a 16-byte aligned stand-in address; never dereferenced by rejected calls
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert _declared() == sorted(fa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared():
+        assert name in exported, name
+    # nothing but the C ABI is exported from the library's own code
+    assert {n for n in exported if n.startswith("fa")} == set(_declared())
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in fa.version()
+    L = fa.lib()
+    for code in (OK, NULL, SHAPE, HEADDIM, DTYPE, DROPOUT, ALIGN, UNSUP, HIP, ARG, 12345):
+        assert isinstance(L.fa_status_string(code), bytes)
+
+
+def test_workspace_bytes():
+    assert fa.workspace_bytes(2, 16, 8192, 128) == 4 * 2 * 16 * 8192
+    assert fa.workspace_bytes(0, 16, 8192, 128) == 0
+    assert fa.workspace_bytes(1, 1, 1, 63) == 0
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=16, d=64, scale=0.125, causal=0, p=0.0, seed=0,
+             stream=None, dtype=1)
+    a.update(kw)
+    return fa.lib().fa_forward(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                               a["d"], a["scale"], a["causal"], a["p"], a["seed"], a["stream"],
+                               a["dtype"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), NULL), (dict(k=0), NULL), (dict(v=0), NULL), (dict(o=0), NULL), (dict(lse=0), NULL),
+    (dict(q=P + 8), ALIGN), (dict(o=P + 2), ALIGN), (dict(lse=P + 4), ALIGN),
+    (dict(B=0), SHAPE), (dict(H=-1), SHAPE), (dict(N=0), SHAPE), (dict(B=1 << 20, H=1 << 10, N=1 << 20), SHAPE),
+    (dict(d=32), HEADDIM), (dict(d=96), HEADDIM), (dict(d=256), HEADDIM),
+    (dict(dtype=2), DTYPE), (dict(dtype=-1), DTYPE),
+    (dict(p=1.0), DROPOUT), (dict(p=-0.1), DROPOUT), (dict(p=float("nan")), DROPOUT), (dict(p=1.5), DROPOUT),
+    (dict(scale=float("inf")), ARG), (dict(scale=float("nan")), ARG),
+])
+def test_forward_rejects(kw, status):
+    assert _fwd(**kw) == status
+
+
+def test_backward_rejects():
+    L = fa.lib()
+    args = [P] * 10 + [1, 1, 16, 64, 0.125, 1, 0.0, 0, None, 1]
+
+    def call(**ch):
+        a = list(args)
+        for idx, val in ch.items():
+            a[int(idx[1:])] = val
+        return L.fa_backward(*a)
+
+    assert call(a0=0) == NULL
+    assert call(a9=0) == NULL  # workspace
+    assert call(a9=P + 4) == ALIGN
+    assert call(a13=80 + 1) == HEADDIM
+    assert call(a12=0) == SHAPE
+    assert call(a16=1.0) == DROPOUT
+    assert call(a19=7) == DTYPE
+    assert call(a14=float("nan")) == ARG
+    dk = [P] * 8 + [1, 1, 16, 64, 0.125, 1, 0.0, 0, None, 1]
+    dk[6] = 0
+    assert L.fa_backward_dkdv(*dk) == NULL
+    dq = [P] * 7 + [1, 1, 16, 64, 0.125, 1, 0.0, 0, None, 1]
+    dq[10] = 100
+    assert L.fa_backward_dq(*dq) == HEADDIM
+    assert L.fa_backward_preprocess(P, P, 0, 1, 1, 16, 64, None, 1) == NULL
+    assert L.fa_backward_preprocess(P, P + 1, P, 1, 1, 16, 64, None, 1) == ALIGN
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 0, 0, 1, 0.1, 0, 0, 4, 4, 0, None), NULL),
+    ((1, 0, 0, 1, 1.0, 0, 0, 4, 4, P, None), DROPOUT),
+    ((1, 0, 1, 1, 0.1, 0, 0, 4, 4, P, None), ARG),      # h >= H
+    ((1, -1, 0, 1, 0.1, 0, 0, 4, 4, P, None), ARG),     # b < 0
+    ((1, 0, 0, 1, 0.1, -1, 0, 4, 4, P, None), ARG),     # row0 < 0
+    ((1, 0, 0, 1, 0.1, 0, 0, 0, 4, P, None), ARG),      # rows < 1
+    ((1, 0, 0, 1, 0.1, 0, 0, 65536, 65536, P, None), ARG),  # rows*cols >= 2^31
+    ((1, 0, 0, 1, 0.1, 2147483000, 0, 1000, 4, P, None), ARG),  # row0+rows overflows
+])
+def test_dropout_mask_rejects(args, status):
+    assert fa.lib().fa_dropout_mask(*args) == status
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa, "_LIB", None)
+    monkeypatch.setattr(fa, "lib_path", lambda: str(tmp_path / "absent.so"))
+    with pytest.raises(fa.FAError):
+        fa.lib()
