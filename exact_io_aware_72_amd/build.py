@@ -31,6 +31,9 @@ COMMON_FLAGS = [
     # Packed fp32 VALU instructions stay off (the compiler would otherwise
     # form them from scalar or float2 code).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core results go to ordinary VGPRs, so the softmax and the
+    # rescale read them without accumulator-register copies.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-function",
     "-I", INCLUDE,

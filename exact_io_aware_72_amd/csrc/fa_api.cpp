@@ -37,6 +37,9 @@ int check_problem(int B, int H, int N, int d, int dtype) {
   if (rows > (int64_t)1 << 36) return FA_ERR_SHAPE;
   if ((rows + 15) / 16 > (int64_t)INT32_MAX) return FA_ERR_SHAPE;
   if ((int64_t)((N + 31) / 32) * B * H > (int64_t)INT32_MAX) return FA_ERR_SHAPE;
+  // The kernels address one batch item's rows with 32-bit byte offsets.
+  const int64_t esize = dtype == FA_BF16 ? 2 : 4;
+  if ((int64_t)N * H * d * esize >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -45,7 +48,9 @@ int check_dropout(float p) {
   return FA_OK;
 }
 
-int check_scale(float scale) { return std::isfinite(scale) ? FA_OK : FA_ERR_ARG; }
+// The kernels take the row max of raw scores and scale it afterwards, which
+// needs scale > 0 (the pages' scale is 1/sqrt(d)).
+int check_scale(float scale) { return (std::isfinite(scale) && scale > 0.0f) ? FA_OK : FA_ERR_ARG; }
 
 void set_dropout(fa::AttnArgs& a, float p, uint64_t seed) {
   a.dropout = p > 0.0f;

@@ -148,7 +148,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdParams p) {
   __shared__ __align__(16) char smem[2 * C::BUF];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int N = p.N, H = p.H;
   const int nkb = (N + C::BK - 1) / C::BK;
@@ -164,8 +165,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdParams p) {
   const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + base;
   const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + base;
   const uint16_t* dOg = static_cast<const uint16_t*>(p.dout) + base;
-  const float* lseg = p.lse + ((int64_t)b * H + h) * N;
-  const float* dsg = p.dsum + ((int64_t)b * H + h) * N;
+  // Buffer resources over this head: reads of rows >= N return zeros. Zero Q
+  // and dO rows (with zero LSE and D) contribute exactly nothing to dK, dV.
+  const uint32_t rs2 = (uint32_t)(H * D * 2);
+  const uint32_t nbytes = (uint32_t)N * rs2;
+  const BufRes rq = make_bufres(Qg, nbytes), rk = make_bufres(Kg, nbytes);
+  const BufRes rv = make_bufres(Vg, nbytes), rdo = make_bufres(dOg, nbytes);
+  const BufRes rl = make_bufres(p.lse + ((int64_t)b * H + h) * N, (uint32_t)N * 4);
+  const BufRes rd = make_bufres(p.dsum + ((int64_t)b * H + h) * N, (uint32_t)N * 4);
 
   if constexpr (C::DP > D) {
     // transposed rows d >= D feed only discarded accumulator rows
@@ -179,14 +186,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdParams p) {
   }
 
   u32x4 kreg[C::NKC], vreg[C::NKC];
-  {
-    const bool ok = mykey < N;
-    const int64_t r = (int64_t)(ok ? mykey : 0) * rs + 8 * hf;
 #pragma unroll
-    for (int c = 0; c < C::NKC; ++c) {
-      kreg[c] = ok ? ld_global_128(Kg + r + 16 * c) : u32x4{0, 0, 0, 0};
-      vreg[c] = ok ? ld_global_128(Vg + r + 16 * c) : u32x4{0, 0, 0, 0};
-    }
+  for (int c = 0; c < C::NKC; ++c) {
+    const uint32_t off = (uint32_t)mykey * rs2 + (16 * c + 8 * hf) * 2;
+    kreg[c] = buf_load_128(rk, off);
+    vreg[c] = buf_load_128(rv, off);
   }
   uint64_t kbh = 0;
   uint32_t bcol = 0;
@@ -204,18 +208,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdParams p) {
     if (tid < 2 * C::ITEMS1) {
       const int which = tid / C::ITEMS1, it = tid - which * C::ITEMS1;
       const int g = it / C::KCH, c = it - g * C::KCH;
-      const uint16_t* src = which ? dOg : Qg;
+      const BufRes src = which ? rdo : rq;
+      const uint32_t off = (uint32_t)(qt0 + 4 * g) * rs2 + 16 * c;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int q = qt0 + 4 * g + j;
-        st[j] = q < N ? ld_global_128(src + (int64_t)q * rs + 8 * c) : u32x4{0, 0, 0, 0};
-      }
+      for (int j = 0; j < 4; ++j) st[j] = buf_load_128(src, off + j * rs2);
     }
     const int q = qt0 + (tid & 31);
     if (tid < 32) {
-      sx = q < N ? lseg[q] * kLog2e : INFINITY;  // rows past N get P = 0
+      sx = buf_load_f32(rl, (uint32_t)q * 4) * kLog2e;
     } else if (tid < 64) {
-      sx = q < N ? dsg[q] : 0.f;
+      sx = buf_load_f32(rd, (uint32_t)q * 4);
     } else if (DROP && tid < 96) {
       sx = __uint_as_float(row_key(kbh, q));
     }
@@ -366,7 +368,8 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
   __shared__ __align__(16) char smem[2 * C::BUF];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int N = p.N, H = p.H;
   const int nqb = (N + C::BQ - 1) / C::BQ;
@@ -391,19 +394,26 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
     }
   }
 
+  // Buffer resources over this head: reads of rows >= N return zeros.
+  const uint32_t rs2 = (uint32_t)(H * D * 2);
+  const uint32_t nbytes = (uint32_t)N * rs2;
+  const BufRes rq = make_bufres(Qg, nbytes), rk = make_bufres(Kg, nbytes);
+  const BufRes rv = make_bufres(Vg, nbytes), rdo = make_bufres(dOg, nbytes);
+  const int64_t statoff = ((int64_t)b * H + h) * N;
+  const BufRes rl = make_bufres(p.lse + statoff, (uint32_t)N * 4);
+  const BufRes rd = make_bufres(p.dsum + statoff, (uint32_t)N * 4);
+
   u32x4 qreg[C::NKC], doreg[C::NKC];
   const bool qok = myq < N;
-  {
-    const int64_t r = (int64_t)(qok ? myq : 0) * rs + 8 * hf;
 #pragma unroll
-    for (int c = 0; c < C::NKC; ++c) {
-      qreg[c] = qok ? ld_global_128(Qg + r + 16 * c) : u32x4{0, 0, 0, 0};
-      doreg[c] = qok ? ld_global_128(dOg + r + 16 * c) : u32x4{0, 0, 0, 0};
-    }
+  for (int c = 0; c < C::NKC; ++c) {
+    const uint32_t off = (uint32_t)myq * rs2 + (16 * c + 8 * hf) * 2;
+    qreg[c] = buf_load_128(rq, off);
+    doreg[c] = buf_load_128(rdo, off);
   }
-  const int64_t statoff = ((int64_t)b * H + h) * N;
-  const float lse2 = qok ? p.lse[statoff + myq] * kLog2e : INFINITY;
-  const float dq_d = qok ? p.dsum[statoff + myq] : 0.f;
+  // Rows past N: zero Q, dO, LSE and D give dS = 0 (never stored anyway).
+  const float lse2 = buf_load_f32(rl, (uint32_t)myq * 4) * kLog2e;
+  const float dq_d = buf_load_f32(rd, (uint32_t)myq * 4);
   uint64_t kbh = 0;
   uint32_t arow = 0;
   if constexpr (DROP) {
@@ -420,12 +430,10 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
     if (tid < 2 * C::ITEMS1) {
       const int which = tid / C::ITEMS1, it = tid - which * C::ITEMS1;
       const int g = it / C::KCH, c = it - g * C::KCH;
-      const uint16_t* src = which ? Vg : Kg;
+      const BufRes src = which ? rv : rk;
+      const uint32_t off = (uint32_t)(k0 + 4 * g) * rs2 + 16 * c;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + 4 * g + j;
-        st[j] = key < N ? ld_global_128(src + (int64_t)key * rs + 8 * c) : u32x4{0, 0, 0, 0};
-      }
+      for (int j = 0; j < 4; ++j) st[j] = buf_load_128(src, off + j * rs2);
     }
     if constexpr (DROP) {
       if (tid >= 224) bst = col_key(kbh, k0 + (tid - 224));

@@ -52,6 +52,21 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 
+// Buffer resource over one (batch, head) slice: offsets are bytes from the
+// slice start, and any 16-byte read at or past `bytes` returns zeros (the
+// hardware range check), which is how rows past N are padded.
+typedef __amdgpu_buffer_rsrc_t BufRes;
+__device__ __forceinline__ BufRes make_bufres(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load_128(BufRes r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ float buf_load_f32(BufRes r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 __device__ __forceinline__ u32x4 ld_global_128(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

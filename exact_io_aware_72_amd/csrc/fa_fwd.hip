@@ -70,7 +70,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   __shared__ __align__(16) char smem[2 * C::BUF];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile decisions are scalar
   const int l32 = lane & 31, hf = lane >> 5;
   const int N = p.N, H = p.H;
   const int nqb = (N + C::BM - 1) / C::BM;
@@ -96,13 +97,16 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
     }
   }
 
+  // Buffer resources over this head's rows: reads of rows >= N return zeros.
+  const uint32_t rs2 = (uint32_t)(H * D * 2);  // bytes between consecutive rows
+  const BufRes rq = make_bufres(Qg, (uint32_t)N * rs2);
+  const BufRes rk = make_bufres(Kg, (uint32_t)N * rs2);
+  const BufRes rv = make_bufres(Vg, (uint32_t)N * rs2);
+
+  // Q operand (B of S^T = K Q^T): 8 d-values per lane per 16-wide chunk.
   u32x4 qreg[C::NKC];
-  {
-    const bool ok = myq < N;
-    const uint16_t* qrow = Qg + (int64_t)(ok ? myq : 0) * rs + 8 * hf;
 #pragma unroll
-    for (int c = 0; c < C::NKC; ++c) qreg[c] = ok ? ld_global_128(qrow + 16 * c) : u32x4{0, 0, 0, 0};
-  }
+  for (int c = 0; c < C::NKC; ++c) qreg[c] = buf_load_128(rq, (uint32_t)myq * rs2 + (16 * c + 8 * hf) * 2);
 
   uint64_t kbh = 0;
   uint32_t arow = 0;
@@ -114,30 +118,30 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   const int kend = CAUSAL ? min(N, q0 + C::BM) : N;
   const int ntiles = (kend + C::BN - 1) / C::BN;
 
+  // Staging registers. Key rows past N read as zeros: their scores are
+  // masked to -inf and their V rows meet zero probabilities.
   u32x4 kst[C::K_PER_T];
   u32x4 vst[C::V_PER_T][4];
   uint32_t bst = 0;
 
   auto load_tile = [&](int k0) {
+    const uint32_t koff = (uint32_t)k0 * rs2;
 #pragma unroll
     for (int i = 0; i < C::K_PER_T; ++i) {
       const int item = tid + i * C::NT;
-      if (item < C::K_ITEMS) {
+      if (C::K_ITEMS % C::NT == 0 || item < C::K_ITEMS) {
         const int r = item / C::KCH, c = item - r * C::KCH;
-        const int key = k0 + r;
-        kst[i] = key < N ? ld_global_128(Kg + (int64_t)key * rs + 8 * c) : u32x4{0, 0, 0, 0};
+        kst[i] = buf_load_128(rk, koff + (uint32_t)r * rs2 + 16 * c);
       }
     }
 #pragma unroll
     for (int i = 0; i < C::V_PER_T; ++i) {
       const int item = tid + i * C::NT;
-      if (item < C::V_ITEMS) {
+      if (C::V_ITEMS % C::NT == 0 || item < C::V_ITEMS) {
         const int g = item / C::KCH, c = item - g * C::KCH;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = k0 + 4 * g + j;
-          vst[i][j] = key < N ? ld_global_128(Vg + (int64_t)key * rs + 8 * c) : u32x4{0, 0, 0, 0};
-        }
+        for (int j = 0; j < 4; ++j)
+          vst[i][j] = buf_load_128(rv, koff + (uint32_t)(4 * g + j) * rs2 + 16 * c);
       }
     }
     if constexpr (DROP) {
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < C::K_PER_T; ++i) {
       const int item = tid + i * C::NT;
-      if (item < C::K_ITEMS) {
+      if (C::K_ITEMS % C::NT == 0 || item < C::K_ITEMS) {
         const int r = item / C::KCH, c = item - r * C::KCH;
         st_lds_128(buf, r * C::KS + c * 16, kst[i]);
       }
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < C::V_PER_T; ++i) {
       const int item = tid + i * C::NT;
-      if (item < C::V_ITEMS) {
+      if (C::V_ITEMS % C::NT == 0 || item < C::V_ITEMS) {
         const int g = item / C::KCH, c = item - g * C::KCH;
         st_lds_transpose4x8(buf + C::KBYTES, C::VS, 8 * c, perm_pos4(g), vst[i][0], vst[i][1],
                             vst[i][2], vst[i][3]);
@@ -171,6 +175,13 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   store_tile(smem);
   __syncthreads();
 
+  // Running statistics in base-2 units of the scaled scores. The reference
+  // max m only moves when a tile's max exceeds it by more than kLazy (then
+  // O and l are rescaled); otherwise probabilities up to 2^kLazy are summed
+  // against the old reference. O and l always share one reference, so the
+  // final O / l and LSE are exact.
+  constexpr float kLazy = 8.0f;
+  const float c2 = p.c2;
   float m = -INFINITY, l = 0.f;
   f32x16 oacc[C::NDB];
 #pragma unroll
@@ -179,69 +190,66 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   for (int t = 0; t < ntiles; ++t) {
     const char* buf = smem + (t & 1) * C::BUF;
     const int k0 = t * C::BN;
-    if (t + 1 < ntiles) load_tile(k0 + C::BN);
-    const bool active = !CAUSAL || (k0 <= qw0 + 31);
-    if (active) {
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile(k0 + C::BN);
+    if (!CAUSAL || k0 <= qw0 + 31) {
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
       for (int c = 0; c < C::NKC; ++c) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          s[kb] = mfma32x32x16(ld_lds_128(buf, (kb * 32 + l32) * C::KS + (16 * c + 8 * hf) * 2),
-                               qreg[c], s[kb]);
+        const int col = (16 * c + 8 * hf) * 2;
+        s0 = mfma32x32x16(ld_lds_128(buf, l32 * C::KS + col), qreg[c], s0);
+        s1 = mfma32x32x16(ld_lds_128(buf, (32 + l32) * C::KS + col), qreg[c], s1);
       }
-      const bool need_mask = (k0 + C::BN > N) || (CAUSAL && k0 + C::BN - 1 > qw0);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      if ((k0 + C::BN > N) || (CAUSAL && k0 + C::BN - 1 > qw0)) {
+        const int lim = CAUSAL ? min(myq, N - 1) : N - 1;  // last visible key
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = s[kb][r] * p.c2;
-          if (need_mask) {
-            const int key = k0 + kb * 32 + c_row(r, hf);
-            if (key >= N || (CAUSAL && key > myq)) x = -INFINITY;
-          }
-          s[kb][r] = x;
-          mx = fmaxf(mx, x);
+          const int key = k0 + c_row(r, hf);
+          s0[r] = key > lim ? -INFINITY : s0[r];
+          s1[r] = key + 32 > lim ? -INFINITY : s1[r];
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m, mx);
-      const float alpha = exp2_hw(m - mnew);
-      m = mnew;
-      float psum = 0.f;
+      float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+      if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
+        const float mnew = fmaxf(m, mx);
+        const float alpha = exp2_hw(m - mnew);
+        m = mnew;
+        l *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = exp2_hw(s[kb][r] - mnew);
-          psum += pv;
-          s[kb][r] = pv;
-        }
+        for (int db = 0; db < C::NDB; ++db) oacc[db] *= alpha;
       }
+      const float nm = -m;
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] = exp2_hw(fmaf(s0[r], c2, nm));
+        s1[r] = exp2_hw(fmaf(s1[r], c2, nm));
+        ps0 += s0[r];
+        ps1 += s1[r];
+      }
+      l += ps0 + ps1;
       if constexpr (DROP) {
         const char* bk = buf + C::KBYTES + C::VBYTES;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int g = 0; g < 4; ++g) {
+          const u32x4 c0 = ld_lds_u32x4(bk, (8 * g + 4 * hf) * 4);
+          const u32x4 c1 = ld_lds_u32x4(bk, (32 + 8 * g + 4 * hf) * 4);
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const u32x4 cols = ld_lds_u32x4(bk, (kb * 32 + 8 * g + 4 * hf) * 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (!keep(arow, cols[e], p.drop_t)) s[kb][4 * g + e] = 0.f;
+          for (int e = 0; e < 4; ++e) {
+            s0[4 * g + e] = keep(arow, c0[e], p.drop_t) ? s0[4 * g + e] : 0.f;
+            s1[4 * g + e] = keep(arow, c1[e], p.drop_t) ? s1[4 * g + e] : 0.f;
           }
         }
       }
-      l = l * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) oacc[db] *= alpha;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const int kb = kt >> 1, rb = (kt & 1) * 8;
-        const u32x4 bop = {pack_bf16x2(s[kb][rb + 0], s[kb][rb + 1]),
-                           pack_bf16x2(s[kb][rb + 2], s[kb][rb + 3]),
-                           pack_bf16x2(s[kb][rb + 4], s[kb][rb + 5]),
-                           pack_bf16x2(s[kb][rb + 6], s[kb][rb + 7])};
+        const f32x16& sv = (kt < 2) ? s0 : s1;
+        const int rb = (kt & 1) * 8;
+        const u32x4 bop = {pack_bf16x2(sv[rb + 0], sv[rb + 1]), pack_bf16x2(sv[rb + 2], sv[rb + 3]),
+                           pack_bf16x2(sv[rb + 4], sv[rb + 5]), pack_bf16x2(sv[rb + 6], sv[rb + 7])};
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
           oacc[db] = mfma32x32x16(
@@ -249,7 +257,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
               oacc[db]);
       }
     }
-    if (t + 1 < ntiles) store_tile(smem + ((t + 1) & 1) * C::BUF);
+    if (more) store_tile(smem + ((t + 1) & 1) * C::BUF);
     __syncthreads();
   }
 

@@ -25,7 +25,8 @@
  *     "enqueued". Device faults surface at the caller's next synchronisation.
  *   - Arguments are validated before any HIP call; on any error nothing is
  *     launched and nothing is written. No C++ exception crosses this ABI.
- *   - Supported: d in {64, 80, 128}; any N >= 1 (tails handled by masks);
+ *   - Supported: d in {64, 80, 128}; any N >= 1 (tails handled by masks)
+ *     with N*H*d*sizeof(element) < 2^31 (one batch item below 2 GiB);
  *     dtype FA_BF16 (bf16 storage, fp32 accumulation, bf16 matrix cores) or
  *     FA_F32 (fp32 throughout). Causal masking keeps key j for query i iff
  *     j <= i (queries and keys share positions 0..N-1).
@@ -52,14 +53,16 @@ typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,        /* a required pointer is NULL                         */
-  FA_ERR_SHAPE = -2,       /* B, H or N < 1, or a size overflows                 */
+  FA_ERR_SHAPE = -2,       /* B, H or N < 1, a batch item of 2 GiB or more, or
+                              a size that overflows                             */
   FA_ERR_HEADDIM = -3,     /* d not in {64, 80, 128}                             */
   FA_ERR_DTYPE = -4,       /* dtype not FA_F32 / FA_BF16                         */
   FA_ERR_DROPOUT = -5,     /* dropout_p outside [0, 1) or NaN                    */
   FA_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned                   */
   FA_ERR_UNSUPPORTED = -7, /* valid request this build does not implement       */
   FA_ERR_HIP = -8,         /* a HIP runtime call failed; see fa_status_string    */
-  FA_ERR_ARG = -9          /* other invalid argument (non-finite scale, window)  */
+  FA_ERR_ARG = -9          /* other invalid argument (scale not finite and > 0,
+                              bad mask window)                                  */
 } fa_status;
 
 /*
@@ -69,7 +72,7 @@ typedef enum {
  *   o        [B][N][H][d] output (dtype): O = (P o Z / (1-p)) V
  *   lse      [B][H][N] float output: natural-log logsumexp of the scaled,
  *            masked scores of each query row (undropped)
- *   scale    multiplier of Q K^T (finite); normally 1/sqrt(d)
+ *   scale    multiplier of Q K^T, finite and > 0; normally 1/sqrt(d)
  *   causal   0 = full attention, nonzero = causal mask
  * Definition: "FlashAttention for Efficient Training", section 1.1
  * (Attention(Q,K,V)), section 3.1 (S_ij = Q_i K_j^T / sqrt(d_k), online
