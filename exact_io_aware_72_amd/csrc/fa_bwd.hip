@@ -111,17 +111,18 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const void* __restrict__ o
 }
 
 // ---------------------------------------------------------------------------
-// B2 (bf16): one work-group per (block of 128 keys, b, h); each wave owns 32
-// keys, holding K and V rows of those keys in registers and dK^T, dV^T
-// accumulators (lane = key). Query tiles of 32 rows stream through LDS, each
+// B2 (bf16): one work-group of 8 waves per (block of 256 keys, b, h); each
+// wave owns 32 keys, with their K rows in registers, their V rows in LDS
+// (read once per query tile) and dK^T, dV^T accumulators (lane = key).
+// Query tiles of 32 rows stream through LDS, staged once for all 8 waves and
 // stored twice: row-major (A operand of S = Q K^T and dP = dO V^T) and
 // transposed with the contraction relabelling (A operand of dK^T += Q^T dS
 // and dV^T += dO^T P~).
 template <int D, bool DROP>
 struct DkdvCfg {
-  static constexpr int NT = 256;
-  static constexpr int BK = 128;
-  static constexpr int BQ = 32;
+  static constexpr int NT = 512;   // 8 waves
+  static constexpr int BK = 256;   // keys per work-group
+  static constexpr int BQ = 32;    // queries per tile
   static constexpr int NKC = D / 16;
   static constexpr int DP = (D + 31) / 32 * 32;
   static constexpr int NDB = DP / 32;
@@ -130,6 +131,7 @@ struct DkdvCfg {
   static constexpr int TS = (BQ + 8) * 2;  // bytes per transposed row
   static constexpr int NAT = BQ * RS;
   static constexpr int TRN = DP * TS;
+  static constexpr int VBLK = BK * RS;     // this block's V rows
   static constexpr int OFF_Q = 0;
   static constexpr int OFF_QT = NAT;
   static constexpr int OFF_DO = NAT + TRN;
@@ -139,13 +141,18 @@ struct DkdvCfg {
   static constexpr int OFF_AR = OFF_DS + BQ * 4;
   static constexpr int BUF = OFF_AR + (DROP ? BQ * 4 : 0);
   static constexpr int ITEMS1 = (BQ / 4) * KCH;  // 4-row x 16-byte items per tensor
-  static_assert(2 * ITEMS1 <= NT, "one staging item per thread");
+  static constexpr int STAT0 = 256;              // first thread loading row statistics
+  static_assert(2 * ITEMS1 <= STAT0, "staging items fit below the statistics threads");
+  static constexpr int V_ITEMS = BK * KCH;
+  static constexpr int V_PER_T = (V_ITEMS + NT - 1) / NT;
 };
 
 template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdParams p) {
   using C = DkdvCfg<D, DROP>;
-  __shared__ __align__(16) char smem[2 * C::BUF];
+  __shared__ __align__(16) char smem[C::VBLK + 2 * C::BUF];
+  char* const vblk = smem;
+  char* const bufs = smem + C::VBLK;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -181,17 +188,25 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdParams p) {
       const int which = i / PAD16, j = i - which * PAD16;
       const int bsel = which >> 1;
       const int off = (which & 1) ? C::OFF_DOT : C::OFF_QT;
-      st_lds_128(smem + bsel * C::BUF + off + D * C::TS, j * 16, u32x4{0, 0, 0, 0});
+      st_lds_128(bufs + bsel * C::BUF + off + D * C::TS, j * 16, u32x4{0, 0, 0, 0});
     }
   }
 
-  u32x4 kreg[C::NKC], vreg[C::NKC];
+  // This block's V rows, row-major in LDS (B operand of dP = dO V^T).
 #pragma unroll
-  for (int c = 0; c < C::NKC; ++c) {
-    const uint32_t off = (uint32_t)mykey * rs2 + (16 * c + 8 * hf) * 2;
-    kreg[c] = buf_load_128(rk, off);
-    vreg[c] = buf_load_128(rv, off);
+  for (int i = 0; i < C::V_PER_T; ++i) {
+    const int item = tid + i * C::NT;
+    if (C::V_ITEMS % C::NT == 0 || item < C::V_ITEMS) {
+      const int r = item / C::KCH, c = item - r * C::KCH;
+      st_lds_128(vblk, r * C::RS + c * 16, buf_load_128(rv, (uint32_t)(k0 + r) * rs2 + 16 * c));
+    }
   }
+  u32x4 kreg[C::NKC];
+#pragma unroll
+  for (int c = 0; c < C::NKC; ++c)
+    kreg[c] = buf_load_128(rk, (uint32_t)mykey * rs2 + (16 * c + 8 * hf) * 2);
+  const int vrow = (wave * 32 + l32) * C::RS + 16 * hf;  // this lane's V row in LDS
+
   uint64_t kbh = 0;
   uint32_t bcol = 0;
   if constexpr (DROP) {
@@ -212,14 +227,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdParams p) {
       const uint32_t off = (uint32_t)(qt0 + 4 * g) * rs2 + 16 * c;
 #pragma unroll
       for (int j = 0; j < 4; ++j) st[j] = buf_load_128(src, off + j * rs2);
-    }
-    const int q = qt0 + (tid & 31);
-    if (tid < 32) {
-      sx = buf_load_f32(rl, (uint32_t)q * 4) * kLog2e;
-    } else if (tid < 64) {
-      sx = buf_load_f32(rd, (uint32_t)q * 4);
-    } else if (DROP && tid < 96) {
-      sx = __uint_as_float(row_key(kbh, q));
+    } else if (tid >= C::STAT0) {
+      const int which = (tid - C::STAT0) >> 5;
+      const int q = qt0 + (tid & 31);
+      if (which == 0) {
+        sx = buf_load_f32(rl, (uint32_t)q * 4) * kLog2e;
+      } else if (which == 1) {
+        sx = buf_load_f32(rd, (uint32_t)q * 4);
+      } else if (DROP && which == 2) {
+        sx = __uint_as_float(row_key(kbh, q));
+      }
     }
   };
   auto store_tile = [&](char* buf) {
@@ -231,9 +248,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) st_lds_128(nat, (4 * g + j) * C::RS + c * 16, st[j]);
       st_lds_transpose4x8(trn, C::TS, 8 * c, perm_pos4(g), st[0], st[1], st[2], st[3]);
-    }
-    if (tid < (DROP ? 96 : 64)) {
-      const int off = tid < 32 ? C::OFF_LSE : (tid < 64 ? C::OFF_DS : C::OFF_AR);
+    } else if (tid >= C::STAT0 && tid < C::STAT0 + (DROP ? 96 : 64)) {
+      const int which = (tid - C::STAT0) >> 5;
+      const int off = which == 0 ? C::OFF_LSE : (which == 1 ? C::OFF_DS : C::OFF_AR);
       *reinterpret_cast<float*>(buf + off + (tid & 31) * 4) = sx;
     }
   };
@@ -245,29 +262,25 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdParams p) {
     dvacc[db] = f32x16{};
   }
 
-  if (ntiles > 0) {
-    load_tile(qstart);
-    store_tile(smem);
-  }
+  load_tile(qstart);
+  store_tile(bufs);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    const char* buf = smem + (t & 1) * C::BUF;
+    const char* buf = bufs + (t & 1) * C::BUF;
     const int qt0 = qstart + t * C::BQ;
-    if (t + 1 < ntiles) load_tile(qt0 + C::BQ);
-    const bool active = !CAUSAL || (qt0 + C::BQ - 1 >= kw0);
-    if (active) {
-      // S = Q K^T : lane = key, register r -> query qt0 + c_row(r, hf)
-      f32x16 s = f32x16{};
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile(qt0 + C::BQ);
+    if (!CAUSAL || qt0 + C::BQ - 1 >= kw0) {
+      // S = Q K^T and dP = dO V^T : lane = key, register r -> query qt0 + c_row(r, hf)
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int c = 0; c < C::NKC; ++c)
-        s = mfma32x32x16(ld_lds_128(buf + C::OFF_Q, l32 * C::RS + (16 * c + 8 * hf) * 2), kreg[c],
-                         s);
-      f32x16 dp = f32x16{};
-#pragma unroll
-      for (int c = 0; c < C::NKC; ++c)
-        dp = mfma32x32x16(ld_lds_128(buf + C::OFF_DO, l32 * C::RS + (16 * c + 8 * hf) * 2),
-                          vreg[c], dp);
+      for (int c = 0; c < C::NKC; ++c) {
+        const int col = (16 * c + 8 * hf) * 2;
+        s = mfma32x32x16(ld_lds_128(buf + C::OFF_Q, l32 * C::RS + col), kreg[c], s);
+        dp = mfma32x32x16(ld_lds_128(buf + C::OFF_DO, l32 * C::RS + col),
+                          ld_lds_128(vblk, vrow + 32 * c), dp);
+      }
       const bool need_mask = CAUSAL && (qt0 < kw0 + 31);
       float pt[16];
 #pragma unroll
@@ -279,8 +292,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float pv = exp2_hw(s[r] * p.c2 - l2[e]);
-          if (need_mask && mykey > qt0 + c_row(r, hf)) pv = 0.f;
+          float pv = exp2_hw(fmaf(s[r], p.c2, -l2[e]));
+          if (need_mask) pv = mykey > qt0 + c_row(r, hf) ? 0.f : pv;
           float dpv = dp[r];
           if constexpr (DROP) {
             const bool kp = keep(ar[e], bcol, p.drop_t);
@@ -307,7 +320,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdParams p) {
         }
       }
     }
-    if (t + 1 < ntiles) store_tile(smem + ((t + 1) & 1) * C::BUF);
+    if (more) store_tile(bufs + ((t + 1) & 1) * C::BUF);
     __syncthreads();
   }
 
@@ -786,7 +799,7 @@ hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t s, bool bf16) {
 
 hipError_t launch_bwd_dkdv_bf16(const AttnArgs& a, hipStream_t s) {
   const BwdParams prm = make_params(a);
-  const dim3 grid((unsigned)(((a.N + 127) / 128) * a.B * a.H)), block(256);
+  const dim3 grid((unsigned)(((a.N + 255) / 256) * a.B * a.H)), block(512);
   FA_DISPATCH(bwd_dkdv_bf16_kernel, a.d, a.causal, a.dropout, grid, block, s, prm);
   return hipGetLastError();
 }
