@@ -154,6 +154,9 @@ def main():
     ap.add_argument("--also", type=int, nargs="*", default=[4])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB mebibytes (three times), "
+                         "the reference kernel for scaling HBM traffic counters, and exit")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py measures one GPU: the attention kernels run on a single device and this build "
@@ -168,6 +171,16 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     fa.lib()  # fails loudly if the HIP library is missing
+
+    if a.copy_calibration:
+        n = a.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
 
     w = WORKLOADS[a.workload]
     r = run_gpu(w, a.steps, a.warmup, torch, fa)

@@ -222,9 +222,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdParams p) {
   auto load_tile = [&](int qt0) {
     if (tid < 2 * C::ITEMS1) {
       const int which = tid / C::ITEMS1, it = tid - which * C::ITEMS1;
-      const int g = it / C::KCH, c = it - g * C::KCH;
+      const StageItem si = stage_item(it, C::BQ / 4, C::KCH);
       const BufRes src = which ? rdo : rq;
-      const uint32_t off = (uint32_t)(qt0 + 4 * g) * rs2 + 16 * c;
+      const uint32_t off = (uint32_t)(qt0 + 4 * si.g) * rs2 + 16 * si.c;
 #pragma unroll
       for (int j = 0; j < 4; ++j) st[j] = buf_load_128(src, off + j * rs2);
     } else if (tid >= C::STAT0) {
@@ -242,12 +242,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdParams p) {
   auto store_tile = [&](char* buf) {
     if (tid < 2 * C::ITEMS1) {
       const int which = tid / C::ITEMS1, it = tid - which * C::ITEMS1;
-      const int g = it / C::KCH, c = it - g * C::KCH;
+      const StageItem si = stage_item(it, C::BQ / 4, C::KCH);
       char* nat = buf + (which ? C::OFF_DO : C::OFF_Q);
       char* trn = buf + (which ? C::OFF_DOT : C::OFF_QT);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st_lds_128(nat, (4 * g + j) * C::RS + c * 16, st[j]);
-      st_lds_transpose4x8(trn, C::TS, 8 * c, perm_pos4(g), st[0], st[1], st[2], st[3]);
+      for (int j = 0; j < 4; ++j) st_lds_128(nat, (4 * si.g + j) * C::RS + si.c * 16, st[j]);
+      st_lds_transpose4x8(trn, C::TS, 8 * si.c, perm_pos4(si.g), st[0], st[1], st[2], st[3]);
     } else if (tid >= C::STAT0 && tid < C::STAT0 + (DROP ? 96 : 64)) {
       const int which = (tid - C::STAT0) >> 5;
       const int off = which == 0 ? C::OFF_LSE : (which == 1 ? C::OFF_DS : C::OFF_AR);
@@ -442,9 +442,9 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
   auto load_tile = [&](int k0) {
     if (tid < 2 * C::ITEMS1) {
       const int which = tid / C::ITEMS1, it = tid - which * C::ITEMS1;
-      const int g = it / C::KCH, c = it - g * C::KCH;
+      const StageItem si = stage_item(it, C::BK / 4, C::KCH);
       const BufRes src = which ? rv : rk;
-      const uint32_t off = (uint32_t)(k0 + 4 * g) * rs2 + 16 * c;
+      const uint32_t off = (uint32_t)(k0 + 4 * si.g) * rs2 + 16 * si.c;
 #pragma unroll
       for (int j = 0; j < 4; ++j) st[j] = buf_load_128(src, off + j * rs2);
     }
@@ -455,12 +455,12 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
   auto store_tile = [&](char* buf) {
     if (tid < 2 * C::ITEMS1) {
       const int which = tid / C::ITEMS1, it = tid - which * C::ITEMS1;
-      const int g = it / C::KCH, c = it - g * C::KCH;
+      const StageItem si = stage_item(it, C::BK / 4, C::KCH);
       char* nat = buf + (which ? C::OFF_V : C::OFF_K);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st_lds_128(nat, (4 * g + j) * C::RS + c * 16, st[j]);
+      for (int j = 0; j < 4; ++j) st_lds_128(nat, (4 * si.g + j) * C::RS + si.c * 16, st[j]);
       if (which == 0)
-        st_lds_transpose4x8(buf + C::OFF_KT, C::TS, 8 * c, perm_pos4(g), st[0], st[1], st[2],
+        st_lds_transpose4x8(buf + C::OFF_KT, C::TS, 8 * si.c, perm_pos4(si.g), st[0], st[1], st[2],
                             st[3]);
     }
     if constexpr (DROP) {

@@ -89,6 +89,34 @@ __device__ __forceinline__ u32x4 ld_lds_u32x4(const char* base, int off) {
   return *reinterpret_cast<const u32x4*>(base + off);
 }
 
+// Exchange between lane L and lane L ^ 32 without LDS (v_permlane32_swap):
+// swapping x with itself leaves {x_L, x_(L^32)} in the two results, in the
+// same order on both lane halves, so the combined value is bitwise identical
+// on lanes L and L ^ 32.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Staging item for a tile that is stored both row-major and transposed.
+// Item `it` covers rows 4g..4g+3 of the tile and the 16-byte column chunk c.
+// Consecutive items take consecutive g (so the 8-byte transposed writes of
+// one LDS pass land in distinct banks) and a chunk skewed by g (so the
+// row-major 16-byte writes of one pass do too).
+struct StageItem {
+  int g, c;
+};
+__device__ __forceinline__ StageItem stage_item(int it, int ngroups, int nchunks) {
+  StageItem s;
+  s.g = it % ngroups;
+  s.c = (it / ngroups + s.g) % nchunks;
+  return s;
+}
+
 // Row index within a 32-row C tile held by accumulator register r of lane half s.
 __device__ __forceinline__ constexpr int c_row(int r, int s) { return 8 * (r >> 2) + 4 * s + (r & 3); }
 

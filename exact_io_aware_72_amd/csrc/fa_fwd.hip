@@ -138,10 +138,10 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
     for (int i = 0; i < C::V_PER_T; ++i) {
       const int item = tid + i * C::NT;
       if (C::V_ITEMS % C::NT == 0 || item < C::V_ITEMS) {
-        const int g = item / C::KCH, c = item - g * C::KCH;
+        const StageItem si = stage_item(item, C::BN / 4, C::KCH);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          vst[i][j] = buf_load_128(rv, koff + (uint32_t)(4 * g + j) * rs2 + 16 * c);
+          vst[i][j] = buf_load_128(rv, koff + (uint32_t)(4 * si.g + j) * rs2 + 16 * si.c);
       }
     }
     if constexpr (DROP) {
@@ -161,8 +161,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
     for (int i = 0; i < C::V_PER_T; ++i) {
       const int item = tid + i * C::NT;
       if (C::V_ITEMS % C::NT == 0 || item < C::V_ITEMS) {
-        const int g = item / C::KCH, c = item - g * C::KCH;
-        st_lds_transpose4x8(buf + C::KBYTES, C::VS, 8 * c, perm_pos4(g), vst[i][0], vst[i][1],
+        const StageItem si = stage_item(item, C::BN / 4, C::KCH);
+        st_lds_transpose4x8(buf + C::KBYTES, C::VS, 8 * si.c, perm_pos4(si.g), vst[i][0], vst[i][1],
                             vst[i][2], vst[i][3]);
       }
     }
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
       float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+      mx = xor32_max(mx) * c2;
       if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
         const float mnew = fmaxf(m, mx);
         const float alpha = exp2_hw(m - mnew);
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
     __syncthreads();
   }
 
-  const float ltot = l + __shfl_xor(l, 32);
+  const float ltot = xor32_sum(l);
   if (myq < N) {
     const float inv = (DROP ? p.drop_r : 1.f) / ltot;
     uint16_t* orow = p.o + base + (int64_t)myq * rs;
