@@ -34,6 +34,8 @@ COMMON_FLAGS = [
     # Matrix-core results go to ordinary VGPRs, so the softmax and the
     # rescale read them without accumulator-register copies.
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # No NaN quieting before max: lets row maxima use v_max3 on raw scores.
+    "-fno-honor-nans",
     "-Wall",
     "-Wno-unused-function",
     "-I", INCLUDE,

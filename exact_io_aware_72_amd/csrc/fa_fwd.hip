@@ -27,6 +27,7 @@
 #include "fa_device.h"
 #include "fa_hash.h"
 #include "fa_kernels.h"
+#include "fa_tile.h"
 
 namespace fa {
 namespace {
@@ -44,7 +45,7 @@ struct FwdParams {
   uint64_t seed;
 };
 
-template <int D, bool DROP>
+template <int D>
 struct FwdCfg {
   static constexpr int NT = 256;                 // 4 waves
   static constexpr int BM = 128;                 // query rows per work-group
@@ -52,22 +53,24 @@ struct FwdCfg {
   static constexpr int NKC = D / 16;             // k-steps of S^T = K Q^T
   static constexpr int DP = (D + 31) / 32 * 32;  // rows of O^T computed (d padded to 32)
   static constexpr int NDB = DP / 32;
-  static constexpr int KCH = D / 8;              // 16-byte chunks per row
-  static constexpr int KS = (D + 8) * 2;         // LDS bytes per K row (padded)
-  static constexpr int VS = (BN + 8) * 2;        // LDS bytes per V^T row (padded)
-  static constexpr int KBYTES = BN * KS;
-  static constexpr int VBYTES = DP * VS;
-  static constexpr int BUF = KBYTES + VBYTES + (DROP ? BN * 4 : 0);
-  static constexpr int K_ITEMS = BN * KCH;
-  static constexpr int K_PER_T = (K_ITEMS + NT - 1) / NT;
-  static constexpr int V_ITEMS = (BN / 4) * KCH;
-  static constexpr int V_PER_T = (V_ITEMS + NT - 1) / NT;
+  using KT = Tile<BN, D, Swz::kRow>;             // K tile: 16-byte row reads
+  using VT = Tile<BN, D, Swz::kTr>;              // V tile: transposing reads
+  static constexpr int STAGE = KT::BYTES + VT::BYTES;
+  static constexpr int NLOAD = KT::NLOAD + VT::NLOAD;  // load instructions per tile
+  static constexpr int LPW = (NLOAD + 3) / 4;          // per wave
 };
 
 template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
-  using C = FwdCfg<D, DROP>;
-  __shared__ __align__(16) char smem[2 * C::BUF];
+  using C = FwdCfg<D>;
+  using KT = typename C::KT;
+  using VT = typename C::VT;
+  // Two stages of K and V tiles; separate arrays so that reads of one stage
+  // only wait for the loads into that stage.
+  __shared__ __align__(16) char st0[C::STAGE];
+  __shared__ __align__(16) char st1[C::STAGE];
+  __shared__ __align__(16) uint32_t ck0[DROP ? C::BN : 1];
+  __shared__ __align__(16) uint32_t ck1[DROP ? C::BN : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -86,24 +89,11 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   const uint16_t* Qg = p.q + base;
   const uint16_t* Kg = p.k + base;
   const uint16_t* Vg = p.v + base;
-
-  // Rows d >= D of the transposed V tiles only feed discarded output rows;
-  // clear them once so they hold finite values.
-  if constexpr (C::DP > D) {
-    constexpr int PAD16 = (C::DP - D) * C::VS / 16;
-    for (int i = tid; i < 2 * PAD16; i += C::NT) {
-      const int bsel = i / PAD16, j = i - bsel * PAD16;
-      st_lds_128(smem + bsel * C::BUF + C::KBYTES + D * C::VS, j * 16, u32x4{0, 0, 0, 0});
-    }
-  }
-
-  // Buffer resources over this head's rows: reads of rows >= N return zeros.
   const uint32_t rs2 = (uint32_t)(H * D * 2);  // bytes between consecutive rows
-  const BufRes rq = make_bufres(Qg, (uint32_t)N * rs2);
-  const BufRes rk = make_bufres(Kg, (uint32_t)N * rs2);
-  const BufRes rv = make_bufres(Vg, (uint32_t)N * rs2);
 
-  // Q operand (B of S^T = K Q^T): 8 d-values per lane per 16-wide chunk.
+  // Q operand (B of S^T = K Q^T): 8 d-values per lane per 16-wide chunk;
+  // rows >= N read as zeros through the buffer range check.
+  const BufRes rq = make_bufres(Qg, (uint32_t)N * rs2);
   u32x4 qreg[C::NKC];
 #pragma unroll
   for (int c = 0; c < C::NKC; ++c) qreg[c] = buf_load_128(rq, (uint32_t)myq * rs2 + (16 * c + 8 * hf) * 2);
@@ -118,62 +108,56 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   const int kend = CAUSAL ? min(N, q0 + C::BM) : N;
   const int ntiles = (kend + C::BN - 1) / C::BN;
 
-  // Staging registers. Key rows past N read as zeros: their scores are
-  // masked to -inf and their V rows meet zero probabilities.
-  u32x4 kst[C::K_PER_T];
-  u32x4 vst[C::V_PER_T][4];
-  uint32_t bst = 0;
-
-  auto load_tile = [&](int k0) {
-    const uint32_t koff = (uint32_t)k0 * rs2;
+  // This wave's share of the tile loads: K instructions first, then V.
+  uint32_t dsrc[C::LPW];
+  int dlds[C::LPW];
 #pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int item = tid + i * C::NT;
-      if (C::K_ITEMS % C::NT == 0 || item < C::K_ITEMS) {
-        const int r = item / C::KCH, c = item - r * C::KCH;
-        kst[i] = buf_load_128(rk, koff + (uint32_t)r * rs2 + 16 * c);
-      }
+  for (int m = 0; m < C::LPW; ++m) {
+    const int i = (wave & 3) + 4 * m;
+    int off = 0, row = 0, ch = 0;
+    if (i < KT::NLOAD) {
+      KT::load_slot(i, lane, off, row, ch);
+    } else if (i < C::NLOAD) {
+      VT::load_slot(i - KT::NLOAD, lane, off, row, ch);
+      off += KT::BYTES;
     }
+    dsrc[m] = (uint32_t)row * rs2 + 16 * ch;
+    dlds[m] = off;
+  }
+  auto issue = [&](char* stage, uint32_t* ck, int k0) {
+    // Resources start at row k0 and end at row N: rows past N arrive as zeros.
+    const uint32_t left = (uint32_t)(N - k0) * rs2;
+    const BufRes rk = make_bufres(Kg + (int64_t)k0 * rs, left);
+    const BufRes rv = make_bufres(Vg + (int64_t)k0 * rs, left);
 #pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-      const int item = tid + i * C::NT;
-      if (C::V_ITEMS % C::NT == 0 || item < C::V_ITEMS) {
-        const StageItem si = stage_item(item, C::BN / 4, C::KCH);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          vst[i][j] = buf_load_128(rv, koff + (uint32_t)(4 * si.g + j) * rs2 + 16 * si.c);
-      }
-    }
-    if constexpr (DROP) {
-      if (tid < C::BN) bst = col_key(kbh, k0 + tid);
-    }
-  };
-  auto store_tile = [&](char* buf) {
-#pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int item = tid + i * C::NT;
-      if (C::K_ITEMS % C::NT == 0 || item < C::K_ITEMS) {
-        const int r = item / C::KCH, c = item - r * C::KCH;
-        st_lds_128(buf, r * C::KS + c * 16, kst[i]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-      const int item = tid + i * C::NT;
-      if (C::V_ITEMS % C::NT == 0 || item < C::V_ITEMS) {
-        const StageItem si = stage_item(item, C::BN / 4, C::KCH);
-        st_lds_transpose4x8(buf + C::KBYTES, C::VS, 8 * si.c, perm_pos4(si.g), vst[i][0], vst[i][1],
-                            vst[i][2], vst[i][3]);
-      }
+    for (int m = 0; m < C::LPW; ++m) {
+      const int i = (wave & 3) + 4 * m;
+      if (i < C::NLOAD) lds_dma_16(i < KT::NLOAD ? rk : rv, stage + dlds[m], dsrc[m]);
     }
     if constexpr (DROP) {
-      if (tid < C::BN) *reinterpret_cast<uint32_t*>(buf + C::KBYTES + C::VBYTES + tid * 4) = bst;
+      if (tid < C::BN) ck[tid] = col_key(kbh, k0 + tid);
     }
   };
 
-  load_tile(0);
-  store_tile(smem);
-  __syncthreads();
+  // Per-lane LDS offsets of the matrix-core operands (loop invariant).
+  // K rows l32 (scores s0) and l32 + 32 (s1), chunk 2c + hf: the swizzle of
+  // row l32 + 32 is that of row l32 with bit 2 flipped.
+  const int xk = hf ^ KT::sw(l32);
+  int ka[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) ka[u] = l32 * 128 + (((2 * u) ^ xk) << 4);
+  const int ktl = KT::TAIL + l32 * 32 + ((hf ^ KT::swt(l32)) << 4);
+  // V: 16-lane group g reads rows 4(g/2) + j (+ 8h + 16kt), columns
+  // 16(g%2) + 4a (+ 32db) for lane 4j + a of the group; the uniform part of
+  // the swizzle selects one of four precomputed offsets.
+  const int vg = lane >> 4, vj = (lane >> 2) & 3, va = lane & 3;
+  const int vs = vg >> 1, vgh = vg & 1;
+  const int vlp = (2 * vgh) ^ (va >> 1) ^ (2 * vj) ^ vs;
+  int vaoff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    vaoff[u] = KT::BYTES + (4 * vs + vj) * 128 + ((vlp ^ (2 * u)) << 4) + 8 * (va & 1);
+  const int vtl = KT::BYTES + VT::TAIL + (4 * vs + vj) * 32 + 8 * va;
 
   // Running statistics in base-2 units of the scaled scores. The reference
   // max m only moves when a tile's max exceeds it by more than kLazy (then
@@ -187,78 +171,124 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16{};
 
-  for (int t = 0; t < ntiles; ++t) {
-    const char* buf = smem + (t & 1) * C::BUF;
+  auto step = [&](const char* cur, const uint32_t* ckc, char* nxt, uint32_t* ckn, int t) {
+    // Tile t has landed in `cur` once every wave's loads are done; after the
+    // barrier nobody reads `nxt` any more, so the next tile can go there.
+    wait_vmem();
+    __syncthreads();
     const int k0 = t * C::BN;
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile(k0 + C::BN);
-    if (!CAUSAL || k0 <= qw0 + 31) {
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
+    if (t + 1 < ntiles) issue(nxt, ckn, k0 + C::BN);
+    if (CAUSAL && k0 > qw0 + 31) return;  // every key of the tile is after this wave's queries
+
+    // S^T = K Q^T: lane = query, registers = keys (c_row layout).
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-      for (int c = 0; c < C::NKC; ++c) {
-        const int col = (16 * c + 8 * hf) * 2;
-        s0 = mfma32x32x16(ld_lds_128(buf, l32 * C::KS + col), qreg[c], s0);
-        s1 = mfma32x32x16(ld_lds_128(buf, (32 + l32) * C::KS + col), qreg[c], s1);
+    for (int c = 0; c < C::NKC; ++c) {
+      int o0, o1;
+      if (2 * c < 8 * KT::NG) {
+        o0 = (c >> 2) * KT::GBYTES + ka[c & 3];
+        o1 = (c >> 2) * KT::GBYTES + 4096 + ka[(c & 3) ^ 2];
+      } else {
+        o0 = ktl;
+        o1 = ktl + 1024;
       }
-      if ((k0 + C::BN > N) || (CAUSAL && k0 + C::BN - 1 > qw0)) {
-        const int lim = CAUSAL ? min(myq, N - 1) : N - 1;  // last visible key
+      s0 = mfma32x32x16(ld_lds_128(cur, o0), qreg[c], s0);
+      s1 = mfma32x32x16(ld_lds_128(cur, o1), qreg[c], s1);
+    }
+    if ((k0 + C::BN > N) || (CAUSAL && k0 + C::BN - 1 > qw0)) {
+      const int lim = CAUSAL ? min(myq, N - 1) : N - 1;  // last visible key
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + c_row(r, hf);
-          s0[r] = key > lim ? -INFINITY : s0[r];
-          s1[r] = key + 32 > lim ? -INFINITY : s1[r];
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + c_row(r, hf);
+        s0[r] = key > lim ? -INFINITY : s0[r];
+        s1[r] = key + 32 > lim ? -INFINITY : s1[r];
       }
-      float mx = fmaxf(s0[0], s1[0]);
+    }
+    float ma = fmaxf(s0[0], s0[1]), mb = fmaxf(s1[0], s1[1]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-      mx = xor32_max(mx) * c2;
-      if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
-        const float mnew = fmaxf(m, mx);
-        const float alpha = exp2_hw(m - mnew);
-        m = mnew;
-        l *= alpha;
+    for (int r = 2; r < 16; r += 2) {
+      ma = fmaxf(fmaxf(ma, s0[r]), s0[r + 1]);
+      mb = fmaxf(fmaxf(mb, s1[r]), s1[r + 1]);
+    }
+    const float mx = xor32_max(fmaxf(ma, mb)) * c2;
+    if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = exp2_hw(m - mnew);
+      m = mnew;
+      l *= alpha;
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) oacc[db] *= alpha;
-      }
-      const float nm = -m;
+      for (int db = 0; db < C::NDB; ++db) oacc[db] *= alpha;
+    }
+    const float nm = -m;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = exp2_hw(fmaf(s0[r], c2, nm));
+      s1[r] = exp2_hw(fmaf(s1[r], c2, nm));
+    }
+    if constexpr (DROP) {
+      // l sums the probabilities before dropout.
       float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s0[r] = exp2_hw(fmaf(s0[r], c2, nm));
-        s1[r] = exp2_hw(fmaf(s1[r], c2, nm));
         ps0 += s0[r];
         ps1 += s1[r];
       }
       l += ps0 + ps1;
-      if constexpr (DROP) {
-        const char* bk = buf + C::KBYTES + C::VBYTES;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x4 c0 = ld_lds_u32x4(bk, (8 * g + 4 * hf) * 4);
-          const u32x4 c1 = ld_lds_u32x4(bk, (32 + 8 * g + 4 * hf) * 4);
+      for (int g = 0; g < 4; ++g) {
+        const u32x4 c0 = *reinterpret_cast<const u32x4*>(ckc + 8 * g + 4 * hf);
+        const u32x4 c1 = *reinterpret_cast<const u32x4*>(ckc + 32 + 8 * g + 4 * hf);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            s0[4 * g + e] = keep(arow, c0[e], p.drop_t) ? s0[4 * g + e] : 0.f;
-            s1[4 * g + e] = keep(arow, c1[e], p.drop_t) ? s1[4 * g + e] : 0.f;
-          }
+        for (int e = 0; e < 4; ++e) {
+          s0[4 * g + e] = keep(arow, c0[e], p.drop_t) ? s0[4 * g + e] : 0.f;
+          s1[4 * g + e] = keep(arow, c1[e], p.drop_t) ? s1[4 * g + e] : 0.f;
         }
       }
+    }
+    // P^T as the B operand, bf16, in 16-key steps; without dropout the row
+    // sum is taken on these rounded values (v_dot2 with ones).
+    u32x4 pop[4];
+    float la = 0.f, lb = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const f32x16& sv = (kt < 2) ? s0 : s1;
-        const int rb = (kt & 1) * 8;
-        const u32x4 bop = {pack_bf16x2(sv[rb + 0], sv[rb + 1]), pack_bf16x2(sv[rb + 2], sv[rb + 3]),
-                           pack_bf16x2(sv[rb + 4], sv[rb + 5]), pack_bf16x2(sv[rb + 6], sv[rb + 7])};
+    for (int kt = 0; kt < 4; ++kt) {
+      const f32x16& sv = (kt < 2) ? s0 : s1;
+      const int rb = (kt & 1) * 8;
+      pop[kt] = u32x4{pack_bf16x2(sv[rb + 0], sv[rb + 1]), pack_bf16x2(sv[rb + 2], sv[rb + 3]),
+                      pack_bf16x2(sv[rb + 4], sv[rb + 5]), pack_bf16x2(sv[rb + 6], sv[rb + 7])};
+      if constexpr (!DROP) {
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-          oacc[db] = mfma32x32x16(
-              ld_lds_128(buf, C::KBYTES + (db * 32 + l32) * C::VS + (16 * kt + 8 * hf) * 2), bop,
-              oacc[db]);
+        for (int w = 0; w < 4; ++w) {
+          float& acc = (w & 1) ? lb : la;
+          acc = add_bf16_pair(pop[kt][w], acc);
+        }
       }
     }
-    if (more) store_tile(smem + ((t + 1) & 1) * C::BUF);
-    __syncthreads();
+    if constexpr (!DROP) l += la + lb;
+    // O^T += V^T P^T: V fragments by transposing reads (two per operand).
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        u32x2 v0, v1;
+        if (4 * db < 8 * VT::NG) {
+          const int gb = (db >> 1) * VT::GBYTES + 2048 * kt;
+          const int u = 2 * ((db ^ kt) & 1);
+          v0 = ld_lds_tr16(cur, gb + vaoff[u]);
+          v1 = ld_lds_tr16(cur, gb + 1024 + vaoff[u + 1]);
+        } else {
+          v0 = ld_lds_tr16(cur, vtl + 512 * kt);
+          v1 = ld_lds_tr16(cur, vtl + 512 * kt + 256);
+        }
+        const u32x4 aop = {v0[0], v0[1], v1[0], v1[1]};
+        oacc[db] = mfma32x32x16(aop, pop[kt], oacc[db]);
+      }
+    }
+  };
+
+  issue(st0, ck0, 0);
+  for (int t = 0; t < ntiles; t += 2) {
+    step(st0, ck0, st1, ck1, t);
+    if (t + 1 < ntiles) step(st1, ck1, st0, ck0, t + 1);
   }
 
   const float ltot = xor32_sum(l);
