@@ -22,6 +22,7 @@
 #include "fa_device.h"
 #include "fa_hash.h"
 #include "fa_kernels.h"
+#include "fa_tile.h"
 
 namespace fa {
 namespace {
@@ -111,14 +112,64 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const void* __restrict__ o
 }
 
 // ---------------------------------------------------------------------------
+// Offsets shared by the two bf16 backward kernels, for a 32-row tile in the
+// kBoth layout (rows = queries or keys, columns = d).
+//   Row reads (16 bytes, lane = row l32, chunk 2c + hf): four per-lane
+//   offsets, one per value of c & 3; the group of chunk 2c adds a constant.
+//   Transposing reads for the A operand of a product contracting over the
+//   rows: 16-lane group g covers rows 4(g/2) + j (+ 8h + 16kt) and columns
+//   16(g%2) + 4a (+ 32db) for lane 4j + a; the uniform part of the swizzle,
+//   (db & 1, h), selects one of four per-lane offsets.
+template <int D>
+struct Both32 {
+  using T = Tile<32, D, Swz::kBoth>;
+  int row[4];     // row reads, full groups
+  int row_tail;   // row reads, tail group (D = 80)
+  int tr[4];      // transposing reads, full groups
+  int tr_tail[2]; // transposing reads, tail group, by h
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int x = hf ^ T::sw(l32);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) row[u] = l32 * 128 + (((2 * u) ^ x) << 4);
+    row_tail = T::TAIL + l32 * 32 + ((hf ^ T::swt(l32)) << 4);
+    const int g = lane >> 4, j = (lane >> 2) & 3, a = lane & 3;
+    const int s = g >> 1, gh = g & 1;
+    const int lp = (2 * gh) ^ (a >> 1) ^ (2 * j) ^ s;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) tr[u] = (4 * s + j) * 128 + ((lp ^ (2 * u)) << 4) + 8 * (a & 1);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      tr_tail[hh] = T::TAIL + (4 * s + j) * 32 + (((a >> 1) ^ s ^ hh) << 4) + 8 * (a & 1);
+  }
+  // Row read of k-step c (d = 16c .. 16c + 15).
+  __device__ __forceinline__ int row_off(int c) const {
+    return (2 * c < 8 * T::NG) ? (c >> 2) * T::GBYTES + row[c & 3] : row_tail;
+  }
+  // The two transposing reads (h = 0, 1) of d-block db and row step kt.
+  __device__ __forceinline__ u32x4 tr_frag(const char* tile, int db, int kt) const {
+    u32x2 v0, v1;
+    if (4 * db < 8 * T::NG) {
+      const int gb = (db >> 1) * T::GBYTES + 2048 * kt;
+      const int u = 2 * (db & 1);
+      v0 = ld_lds_tr16(tile, gb + tr[u]);
+      v1 = ld_lds_tr16(tile, gb + 1024 + tr[u + 1]);
+    } else {
+      v0 = ld_lds_tr16(tile, tr_tail[0] + 512 * kt);
+      v1 = ld_lds_tr16(tile, tr_tail[1] + 512 * kt + 256);
+    }
+    return u32x4{v0[0], v0[1], v1[0], v1[1]};
+  }
+};
+
+// ---------------------------------------------------------------------------
 // B2 (bf16): one work-group of 8 waves per (block of 256 keys, b, h); each
-// wave owns 32 keys, with their K rows in registers, their V rows in LDS
-// (read once per query tile) and dK^T, dV^T accumulators (lane = key).
-// Query tiles of 32 rows stream through LDS, staged once for all 8 waves and
-// stored twice: row-major (A operand of S = Q K^T and dP = dO V^T) and
-// transposed with the contraction relabelling (A operand of dK^T += Q^T dS
-// and dV^T += dO^T P~).
-template <int D, bool DROP>
+// wave owns 32 keys (lane = key) with their K rows in registers, the block's
+// V rows in LDS, and dK^T, dV^T accumulators. Query tiles of 32 rows of Q and
+// dO stream through two LDS stages by direct-to-LDS loads; one copy of each
+// serves the row reads (A operand of S = Q K^T and dP = dO V^T) and the
+// transposing reads (A operand of dK^T += Q^T dS and dV^T += dO^T P~).
+template <int D>
 struct DkdvCfg {
   static constexpr int NT = 512;   // 8 waves
   static constexpr int BK = 256;   // keys per work-group
@@ -126,33 +177,29 @@ struct DkdvCfg {
   static constexpr int NKC = D / 16;
   static constexpr int DP = (D + 31) / 32 * 32;
   static constexpr int NDB = DP / 32;
-  static constexpr int KCH = D / 8;
-  static constexpr int RS = (D + 8) * 2;   // bytes per row-major row
-  static constexpr int TS = (BQ + 8) * 2;  // bytes per transposed row
-  static constexpr int NAT = BQ * RS;
-  static constexpr int TRN = DP * TS;
-  static constexpr int VBLK = BK * RS;     // this block's V rows
-  static constexpr int OFF_Q = 0;
-  static constexpr int OFF_QT = NAT;
-  static constexpr int OFF_DO = NAT + TRN;
-  static constexpr int OFF_DOT = 2 * NAT + TRN;
-  static constexpr int OFF_LSE = 2 * (NAT + TRN);
-  static constexpr int OFF_DS = OFF_LSE + BQ * 4;
-  static constexpr int OFF_AR = OFF_DS + BQ * 4;
-  static constexpr int BUF = OFF_AR + (DROP ? BQ * 4 : 0);
-  static constexpr int ITEMS1 = (BQ / 4) * KCH;  // 4-row x 16-byte items per tensor
-  static constexpr int STAT0 = 256;              // first thread loading row statistics
-  static_assert(2 * ITEMS1 <= STAT0, "staging items fit below the statistics threads");
-  static constexpr int V_ITEMS = BK * KCH;
-  static constexpr int V_PER_T = (V_ITEMS + NT - 1) / NT;
+  using QT = Tile<BQ, D, Swz::kBoth>;  // Q and dO tiles
+  using VB = Tile<BK, D, Swz::kRow>;   // the block's V rows
+  static constexpr int STAGE = 2 * QT::BYTES;
+  static constexpr int NLOAD = 2 * QT::NLOAD;
+  static constexpr int LPW = (NLOAD + 7) / 8;
+  static constexpr int VLPW = (VB::NLOAD + 7) / 8;
 };
 
 template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdParams p) {
-  using C = DkdvCfg<D, DROP>;
-  __shared__ __align__(16) char smem[C::VBLK + 2 * C::BUF];
-  char* const vblk = smem;
-  char* const bufs = smem + C::VBLK;
+  using C = DkdvCfg<D>;
+  using QT = typename C::QT;
+  using VB = typename C::VB;
+  __shared__ __align__(16) char vblk[VB::BYTES];
+  __shared__ __align__(16) char st0[C::STAGE];
+  __shared__ __align__(16) char st1[C::STAGE];
+  // Per-stage statistics of the tile's queries: lse * log2(e), D, row keys.
+  __shared__ __align__(16) float ls0[C::BQ];
+  __shared__ __align__(16) float ls1[C::BQ];
+  __shared__ __align__(16) float dd0[C::BQ];
+  __shared__ __align__(16) float dd1[C::BQ];
+  __shared__ __align__(16) uint32_t ar0[DROP ? C::BQ : 1];
+  __shared__ __align__(16) uint32_t ar1[DROP ? C::BQ : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -172,40 +219,37 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdParams p) {
   const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + base;
   const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + base;
   const uint16_t* dOg = static_cast<const uint16_t*>(p.dout) + base;
-  // Buffer resources over this head: reads of rows >= N return zeros. Zero Q
-  // and dO rows (with zero LSE and D) contribute exactly nothing to dK, dV.
   const uint32_t rs2 = (uint32_t)(H * D * 2);
-  const uint32_t nbytes = (uint32_t)N * rs2;
-  const BufRes rq = make_bufres(Qg, nbytes), rk = make_bufres(Kg, nbytes);
-  const BufRes rv = make_bufres(Vg, nbytes), rdo = make_bufres(dOg, nbytes);
-  const BufRes rl = make_bufres(p.lse + ((int64_t)b * H + h) * N, (uint32_t)N * 4);
-  const BufRes rd = make_bufres(p.dsum + ((int64_t)b * H + h) * N, (uint32_t)N * 4);
+  const int64_t statoff = ((int64_t)b * H + h) * N;
+  const BufRes rl = make_bufres(p.lse + statoff, (uint32_t)N * 4);
+  const BufRes rd = make_bufres(p.dsum + statoff, (uint32_t)N * 4);
 
-  if constexpr (C::DP > D) {
-    // transposed rows d >= D feed only discarded accumulator rows
-    constexpr int PAD16 = (C::DP - D) * C::TS / 16;
-    for (int i = tid; i < 2 * 2 * PAD16; i += C::NT) {
-      const int which = i / PAD16, j = i - which * PAD16;
-      const int bsel = which >> 1;
-      const int off = (which & 1) ? C::OFF_DOT : C::OFF_QT;
-      st_lds_128(bufs + bsel * C::BUF + off + D * C::TS, j * 16, u32x4{0, 0, 0, 0});
-    }
-  }
-
-  // This block's V rows, row-major in LDS (B operand of dP = dO V^T).
+  // The block's V rows into LDS (rows >= N arrive as zeros).
+  {
+    const BufRes rvb = make_bufres(Vg + (int64_t)k0 * rs, (uint32_t)(N - k0) * rs2);
 #pragma unroll
-  for (int i = 0; i < C::V_PER_T; ++i) {
-    const int item = tid + i * C::NT;
-    if (C::V_ITEMS % C::NT == 0 || item < C::V_ITEMS) {
-      const int r = item / C::KCH, c = item - r * C::KCH;
-      st_lds_128(vblk, r * C::RS + c * 16, buf_load_128(rv, (uint32_t)(k0 + r) * rs2 + 16 * c));
+    for (int m = 0; m < C::VLPW; ++m) {
+      const int i = (wave & 7) + 8 * m;
+      if (i < VB::NLOAD) {
+        int off, row, ch;
+        VB::load_slot(i, lane, off, row, ch);
+        lds_dma_16(rvb, vblk + off, (uint32_t)row * rs2 + 16 * ch);
+      }
     }
   }
+  // This lane's K row (B operand of S = Q K^T); zeros past N.
+  const BufRes rk = make_bufres(Kg, (uint32_t)N * rs2);
   u32x4 kreg[C::NKC];
 #pragma unroll
   for (int c = 0; c < C::NKC; ++c)
     kreg[c] = buf_load_128(rk, (uint32_t)mykey * rs2 + (16 * c + 8 * hf) * 2);
-  const int vrow = (wave * 32 + l32) * C::RS + 16 * hf;  // this lane's V row in LDS
+  // This lane's V row in LDS (B operand of dP = dO V^T).
+  const int vr = wave * 32 + l32;
+  const int vx = hf ^ VB::sw(vr);
+  int vrow[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) vrow[u] = vr * 128 + (((2 * u) ^ vx) << 4);
+  const int vrow_tail = VB::TAIL + vr * 32 + ((hf ^ VB::swt(vr)) << 4);
 
   uint64_t kbh = 0;
   uint32_t bcol = 0;
@@ -217,43 +261,57 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdParams p) {
   const int qstart = CAUSAL ? k0 : 0;
   const int ntiles = (N - qstart + C::BQ - 1) / C::BQ;
 
-  u32x4 st[4];
+  // This wave's share of the tile loads: Q instructions, then dO.
+  uint32_t dsrc[C::LPW];
+  int dlds[C::LPW];
+#pragma unroll
+  for (int m = 0; m < C::LPW; ++m) {
+    const int i = (wave & 7) + 8 * m;
+    int off = 0, row = 0, ch = 0;
+    if (i < QT::NLOAD) {
+      QT::load_slot(i, lane, off, row, ch);
+    } else if (i < C::NLOAD) {
+      QT::load_slot(i - QT::NLOAD, lane, off, row, ch);
+      off += QT::BYTES;
+    }
+    dsrc[m] = (uint32_t)row * rs2 + 16 * ch;
+    dlds[m] = off;
+  }
+  // Statistics of a query tile: threads 0-31 load lse, 32-63 load D,
+  // 64-95 hash the row keys; stored after the tile's compute. Rows past N
+  // read zeros (their Q and dO rows are zero too, so they add nothing).
   float sx = 0.f;
-  auto load_tile = [&](int qt0) {
-    if (tid < 2 * C::ITEMS1) {
-      const int which = tid / C::ITEMS1, it = tid - which * C::ITEMS1;
-      const StageItem si = stage_item(it, C::BQ / 4, C::KCH);
-      const BufRes src = which ? rdo : rq;
-      const uint32_t off = (uint32_t)(qt0 + 4 * si.g) * rs2 + 16 * si.c;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) st[j] = buf_load_128(src, off + j * rs2);
-    } else if (tid >= C::STAT0) {
-      const int which = (tid - C::STAT0) >> 5;
-      const int q = qt0 + (tid & 31);
-      if (which == 0) {
-        sx = buf_load_f32(rl, (uint32_t)q * 4) * kLog2e;
-      } else if (which == 1) {
-        sx = buf_load_f32(rd, (uint32_t)q * 4);
-      } else if (DROP && which == 2) {
-        sx = __uint_as_float(row_key(kbh, q));
-      }
+  auto stat_load = [&](int qt0) {
+    if (tid < 32) {
+      sx = buf_load_f32(rl, (uint32_t)(qt0 + tid) * 4);
+    } else if (tid < 64) {
+      sx = buf_load_f32(rd, (uint32_t)(qt0 + tid - 32) * 4);
+    } else if (DROP && tid < 96) {
+      sx = __uint_as_float(row_key(kbh, qt0 + tid - 64));
     }
   };
-  auto store_tile = [&](char* buf) {
-    if (tid < 2 * C::ITEMS1) {
-      const int which = tid / C::ITEMS1, it = tid - which * C::ITEMS1;
-      const StageItem si = stage_item(it, C::BQ / 4, C::KCH);
-      char* nat = buf + (which ? C::OFF_DO : C::OFF_Q);
-      char* trn = buf + (which ? C::OFF_DOT : C::OFF_QT);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) st_lds_128(nat, (4 * si.g + j) * C::RS + si.c * 16, st[j]);
-      st_lds_transpose4x8(trn, C::TS, 8 * si.c, perm_pos4(si.g), st[0], st[1], st[2], st[3]);
-    } else if (tid >= C::STAT0 && tid < C::STAT0 + (DROP ? 96 : 64)) {
-      const int which = (tid - C::STAT0) >> 5;
-      const int off = which == 0 ? C::OFF_LSE : (which == 1 ? C::OFF_DS : C::OFF_AR);
-      *reinterpret_cast<float*>(buf + off + (tid & 31) * 4) = sx;
+  auto stat_store = [&](float* ls, float* dd, uint32_t* ar) {
+    if (tid < 32) {
+      ls[tid] = sx * kLog2e;
+    } else if (tid < 64) {
+      dd[tid - 32] = sx;
+    } else if (DROP && tid < 96) {
+      ar[tid - 64] = __float_as_uint(sx);
     }
   };
+  auto issue = [&](char* stage, int qt0) {
+    const uint32_t left = (uint32_t)(N - qt0) * rs2;
+    const BufRes rq = make_bufres(Qg + (int64_t)qt0 * rs, left);
+    const BufRes ro = make_bufres(dOg + (int64_t)qt0 * rs, left);
+#pragma unroll
+    for (int m = 0; m < C::LPW; ++m) {
+      const int i = (wave & 7) + 8 * m;
+      if (i < C::NLOAD) lds_dma_16(i < QT::NLOAD ? rq : ro, stage + dlds[m], dsrc[m]);
+    }
+  };
+
+  Both32<D> ofs;
+  ofs.init(lane);
 
   f32x16 dkacc[C::NDB], dvacc[C::NDB];
 #pragma unroll
@@ -262,66 +320,74 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdParams p) {
     dvacc[db] = f32x16{};
   }
 
-  load_tile(qstart);
-  store_tile(bufs);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const char* buf = bufs + (t & 1) * C::BUF;
+  auto step = [&](const char* cur, const float* lsc, const float* ddc, const uint32_t* arc,
+                  char* nxt, float* lsn, float* ddn, uint32_t* arn, int t) {
+    wait_vmem();
+    __syncthreads();
     const int qt0 = qstart + t * C::BQ;
     const bool more = t + 1 < ntiles;
-    if (more) load_tile(qt0 + C::BQ);
+    if (more) {
+      stat_load(qt0 + C::BQ);
+      issue(nxt, qt0 + C::BQ);
+    }
     if (!CAUSAL || qt0 + C::BQ - 1 >= kw0) {
       // S = Q K^T and dP = dO V^T : lane = key, register r -> query qt0 + c_row(r, hf)
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < C::NKC; ++c) {
-        const int col = (16 * c + 8 * hf) * 2;
-        s = mfma32x32x16(ld_lds_128(buf + C::OFF_Q, l32 * C::RS + col), kreg[c], s);
-        dp = mfma32x32x16(ld_lds_128(buf + C::OFF_DO, l32 * C::RS + col),
-                          ld_lds_128(vblk, vrow + 32 * c), dp);
+        const int o = ofs.row_off(c);
+        const int vo = (2 * c < 8 * VB::NG) ? (c >> 2) * VB::GBYTES + vrow[c & 3] : vrow_tail;
+        s = mfma32x32x16(ld_lds_128(cur, o), kreg[c], s);
+        dp = mfma32x32x16(ld_lds_128(cur, QT::BYTES + o), ld_lds_128(vblk, vo), dp);
       }
       const bool need_mask = CAUSAL && (qt0 < kw0 + 31);
-      float pt[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l2 = ld_lds_f32x4(buf + C::OFF_LSE, (8 * g + 4 * hf) * 4);
-        const f32x4 dd = ld_lds_f32x4(buf + C::OFF_DS, (8 * g + 4 * hf) * 4);
-        u32x4 ar = {0, 0, 0, 0};
-        if constexpr (DROP) ar = ld_lds_u32x4(buf + C::OFF_AR, (8 * g + 4 * hf) * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float pv = exp2_hw(fmaf(s[r], p.c2, -l2[e]));
-          if (need_mask) pv = mykey > qt0 + c_row(r, hf) ? 0.f : pv;
-          float dpv = dp[r];
-          if constexpr (DROP) {
-            const bool kp = keep(ar[e], bcol, p.drop_t);
-            pt[r] = kp ? pv * p.drop_r : 0.f;
-            dpv = kp ? dpv * p.drop_r : 0.f;
-          } else {
-            pt[r] = pv;
-          }
-          s[r] = pv * (dpv - dd[e]);  // dS
-        }
-      }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const int rb = kt * 8;
-        const u32x4 pop = {pack_bf16x2(pt[rb + 0], pt[rb + 1]), pack_bf16x2(pt[rb + 2], pt[rb + 3]),
-                           pack_bf16x2(pt[rb + 4], pt[rb + 5]), pack_bf16x2(pt[rb + 6], pt[rb + 7])};
-        const u32x4 sop = {pack_bf16x2(s[rb + 0], s[rb + 1]), pack_bf16x2(s[rb + 2], s[rb + 3]),
-                           pack_bf16x2(s[rb + 4], s[rb + 5]), pack_bf16x2(s[rb + 6], s[rb + 7])};
+        float pt[8], dsv[8];
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const int g = 2 * kt + gg;
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(lsc + 8 * g + 4 * hf);
+          const f32x4 dd = *reinterpret_cast<const f32x4*>(ddc + 8 * g + 4 * hf);
+          u32x4 ar = {0, 0, 0, 0};
+          if constexpr (DROP) ar = *reinterpret_cast<const u32x4*>(arc + 8 * g + 4 * hf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float pv = exp2_hw(fmaf(s[r], p.c2, -l2[e]));
+            if (need_mask) pv = mykey > qt0 + c_row(r, hf) ? 0.f : pv;
+            float dpv = dp[r];
+            float ptv = pv;
+            if constexpr (DROP) {
+              const bool kp = keep(ar[e], bcol, p.drop_t);
+              ptv = kp ? pv * p.drop_r : 0.f;
+              dpv = kp ? dpv * p.drop_r : 0.f;
+            }
+            pt[4 * gg + e] = ptv;
+            dsv[4 * gg + e] = pv * (dpv - dd[e]);
+          }
+        }
+        const u32x4 pop = {pack_bf16x2(pt[0], pt[1]), pack_bf16x2(pt[2], pt[3]),
+                           pack_bf16x2(pt[4], pt[5]), pack_bf16x2(pt[6], pt[7])};
+        const u32x4 sop = {pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3]),
+                           pack_bf16x2(dsv[4], dsv[5]), pack_bf16x2(dsv[6], dsv[7])};
+        // dV^T += dO^T P~ and dK^T += Q^T dS over the 16 queries of step kt.
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          const int off = (db * 32 + l32) * C::TS + (16 * kt + 8 * hf) * 2;
-          dvacc[db] = mfma32x32x16(ld_lds_128(buf + C::OFF_DOT, off), pop, dvacc[db]);
-          dkacc[db] = mfma32x32x16(ld_lds_128(buf + C::OFF_QT, off), sop, dkacc[db]);
+          dvacc[db] = mfma32x32x16(ofs.tr_frag(cur + QT::BYTES, db, kt), pop, dvacc[db]);
+          dkacc[db] = mfma32x32x16(ofs.tr_frag(cur, db, kt), sop, dkacc[db]);
         }
       }
     }
-    if (more) store_tile(bufs + ((t + 1) & 1) * C::BUF);
-    __syncthreads();
+    if (more) stat_store(lsn, ddn, arn);
+  };
+
+  stat_load(qstart);
+  issue(st0, qstart);
+  stat_store(ls0, dd0, ar0);
+  for (int t = 0; t < ntiles; t += 2) {
+    step(st0, ls0, dd0, ar0, st1, ls1, dd1, ar1, t);
+    if (t + 1 < ntiles) step(st1, ls1, dd1, ar1, st0, ls0, dd0, ar0, t + 1);
   }
 
   if (mykey < N) {
@@ -349,11 +415,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // B3 (bf16): one work-group per (block of 128 queries, b, h); each wave owns
 // 32 queries with Q and dO rows in registers and a dQ^T accumulator
-// (lane = query). Key tiles of 32 rows stream through LDS: K row-major
-// (A operand of S^T = K Q^T), K transposed with the contraction relabelling
-// (A operand of dQ^T += K^T dS^T) and V row-major (A operand of
-// dP^T = V dO^T).
-template <int D, bool DROP>
+// (lane = query). Key tiles of 32 rows of K and V stream through two LDS
+// stages by direct-to-LDS loads: K row reads (A operand of S^T = K Q^T) and
+// K transposing reads (A operand of dQ^T += K^T dS^T) from one copy, V row
+// reads (A operand of dP^T = V dO^T).
+template <int D>
 struct DqCfg {
   static constexpr int NT = 256;
   static constexpr int BQ = 128;
@@ -361,24 +427,22 @@ struct DqCfg {
   static constexpr int NKC = D / 16;
   static constexpr int DP = (D + 31) / 32 * 32;
   static constexpr int NDB = DP / 32;
-  static constexpr int KCH = D / 8;
-  static constexpr int RS = (D + 8) * 2;
-  static constexpr int TS = (BK + 8) * 2;
-  static constexpr int NAT = BK * RS;
-  static constexpr int TRN = DP * TS;
-  static constexpr int OFF_K = 0;
-  static constexpr int OFF_KT = NAT;
-  static constexpr int OFF_V = NAT + TRN;
-  static constexpr int OFF_BC = 2 * NAT + TRN;
-  static constexpr int BUF = OFF_BC + (DROP ? BK * 4 : 0);
-  static constexpr int ITEMS1 = (BK / 4) * KCH;
-  static_assert(2 * ITEMS1 <= NT, "one staging item per thread");
+  using KT = Tile<BK, D, Swz::kBoth>;
+  using VT = Tile<BK, D, Swz::kRow>;
+  static constexpr int STAGE = KT::BYTES + VT::BYTES;
+  static constexpr int NLOAD = KT::NLOAD + VT::NLOAD;
+  static constexpr int LPW = (NLOAD + 3) / 4;
 };
 
 template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
-  using C = DqCfg<D, DROP>;
-  __shared__ __align__(16) char smem[2 * C::BUF];
+  using C = DqCfg<D>;
+  using KT = typename C::KT;
+  using VT = typename C::VT;
+  __shared__ __align__(16) char st0[C::STAGE];
+  __shared__ __align__(16) char st1[C::STAGE];
+  __shared__ __align__(16) uint32_t bc0[DROP ? C::BK : 1];
+  __shared__ __align__(16) uint32_t bc1[DROP ? C::BK : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -398,33 +462,21 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
   const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + base;
   const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + base;
   const uint16_t* dOg = static_cast<const uint16_t*>(p.dout) + base;
-
-  if constexpr (C::DP > D) {
-    constexpr int PAD16 = (C::DP - D) * C::TS / 16;
-    for (int i = tid; i < 2 * PAD16; i += C::NT) {
-      const int bsel = i / PAD16, j = i - bsel * PAD16;
-      st_lds_128(smem + bsel * C::BUF + C::OFF_KT + D * C::TS, j * 16, u32x4{0, 0, 0, 0});
-    }
-  }
-
-  // Buffer resources over this head: reads of rows >= N return zeros.
   const uint32_t rs2 = (uint32_t)(H * D * 2);
   const uint32_t nbytes = (uint32_t)N * rs2;
-  const BufRes rq = make_bufres(Qg, nbytes), rk = make_bufres(Kg, nbytes);
-  const BufRes rv = make_bufres(Vg, nbytes), rdo = make_bufres(dOg, nbytes);
+  const BufRes rq = make_bufres(Qg, nbytes), rdo = make_bufres(dOg, nbytes);
   const int64_t statoff = ((int64_t)b * H + h) * N;
   const BufRes rl = make_bufres(p.lse + statoff, (uint32_t)N * 4);
   const BufRes rd = make_bufres(p.dsum + statoff, (uint32_t)N * 4);
 
+  // Rows past N: zero Q, dO, LSE and D give dS = 0 (never stored anyway).
   u32x4 qreg[C::NKC], doreg[C::NKC];
-  const bool qok = myq < N;
 #pragma unroll
   for (int c = 0; c < C::NKC; ++c) {
     const uint32_t off = (uint32_t)myq * rs2 + (16 * c + 8 * hf) * 2;
     qreg[c] = buf_load_128(rq, off);
     doreg[c] = buf_load_128(rdo, off);
   }
-  // Rows past N: zero Q, dO, LSE and D give dS = 0 (never stored anyway).
   const float lse2 = buf_load_f32(rl, (uint32_t)myq * 4) * kLog2e;
   const float dq_d = buf_load_f32(rd, (uint32_t)myq * 4);
   uint64_t kbh = 0;
@@ -437,97 +489,100 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
   const int kend = CAUSAL ? min(N, q0 + C::BQ) : N;
   const int ntiles = (kend + C::BK - 1) / C::BK;
 
-  u32x4 st[4];
-  uint32_t bst = 0;
-  auto load_tile = [&](int k0) {
-    if (tid < 2 * C::ITEMS1) {
-      const int which = tid / C::ITEMS1, it = tid - which * C::ITEMS1;
-      const StageItem si = stage_item(it, C::BK / 4, C::KCH);
-      const BufRes src = which ? rv : rk;
-      const uint32_t off = (uint32_t)(k0 + 4 * si.g) * rs2 + 16 * si.c;
+  // This wave's share of the tile loads: K instructions, then V.
+  uint32_t dsrc[C::LPW];
+  int dlds[C::LPW];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st[j] = buf_load_128(src, off + j * rs2);
+  for (int m = 0; m < C::LPW; ++m) {
+    const int i = (wave & 3) + 4 * m;
+    int off = 0, row = 0, ch = 0;
+    if (i < KT::NLOAD) {
+      KT::load_slot(i, lane, off, row, ch);
+    } else if (i < C::NLOAD) {
+      VT::load_slot(i - KT::NLOAD, lane, off, row, ch);
+      off += KT::BYTES;
+    }
+    dsrc[m] = (uint32_t)row * rs2 + 16 * ch;
+    dlds[m] = off;
+  }
+  auto issue = [&](char* stage, uint32_t* bc, int k0) {
+    const uint32_t left = (uint32_t)(N - k0) * rs2;
+    const BufRes rk = make_bufres(Kg + (int64_t)k0 * rs, left);
+    const BufRes rv = make_bufres(Vg + (int64_t)k0 * rs, left);
+#pragma unroll
+    for (int m = 0; m < C::LPW; ++m) {
+      const int i = (wave & 3) + 4 * m;
+      if (i < C::NLOAD) lds_dma_16(i < KT::NLOAD ? rk : rv, stage + dlds[m], dsrc[m]);
     }
     if constexpr (DROP) {
-      if (tid >= 224) bst = col_key(kbh, k0 + (tid - 224));
+      if (tid < C::BK) bc[tid] = col_key(kbh, k0 + tid);
     }
   };
-  auto store_tile = [&](char* buf) {
-    if (tid < 2 * C::ITEMS1) {
-      const int which = tid / C::ITEMS1, it = tid - which * C::ITEMS1;
-      const StageItem si = stage_item(it, C::BK / 4, C::KCH);
-      char* nat = buf + (which ? C::OFF_V : C::OFF_K);
+
+  Both32<D> ofs;
+  ofs.init(lane);
+  const int vx = hf ^ VT::sw(l32);
+  int vrow[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st_lds_128(nat, (4 * si.g + j) * C::RS + si.c * 16, st[j]);
-      if (which == 0)
-        st_lds_transpose4x8(buf + C::OFF_KT, C::TS, 8 * si.c, perm_pos4(si.g), st[0], st[1], st[2],
-                            st[3]);
-    }
-    if constexpr (DROP) {
-      if (tid >= 224) *reinterpret_cast<uint32_t*>(buf + C::OFF_BC + (tid - 224) * 4) = bst;
-    }
-  };
+  for (int u = 0; u < 4; ++u) vrow[u] = KT::BYTES + l32 * 128 + (((2 * u) ^ vx) << 4);
+  const int vrow_tail = KT::BYTES + VT::TAIL + l32 * 32 + ((hf ^ VT::swt(l32)) << 4);
 
   f32x16 dqacc[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) dqacc[db] = f32x16{};
 
-  load_tile(0);
-  store_tile(smem);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const char* buf = smem + (t & 1) * C::BUF;
+  auto step = [&](const char* cur, const uint32_t* bcc, char* nxt, uint32_t* bcn, int t) {
+    wait_vmem();
+    __syncthreads();
     const int k0 = t * C::BK;
-    if (t + 1 < ntiles) load_tile(k0 + C::BK);
-    const bool active = !CAUSAL || (k0 <= qw0 + 31);
-    if (active) {
-      // S^T = K Q^T : lane = query, register r -> key k0 + c_row(r, hf)
-      f32x16 s = f32x16{};
+    if (t + 1 < ntiles) issue(nxt, bcn, k0 + C::BK);
+    if (CAUSAL && k0 > qw0 + 31) return;
+    // S^T = K Q^T and dP^T = V dO^T : lane = query, register r -> key k0 + c_row(r, hf)
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int c = 0; c < C::NKC; ++c)
-        s = mfma32x32x16(ld_lds_128(buf + C::OFF_K, l32 * C::RS + (16 * c + 8 * hf) * 2), qreg[c],
-                         s);
-      f32x16 dp = f32x16{};
+    for (int c = 0; c < C::NKC; ++c) {
+      const int vo = (2 * c < 8 * VT::NG) ? (c >> 2) * VT::GBYTES + vrow[c & 3] : vrow_tail;
+      s = mfma32x32x16(ld_lds_128(cur, ofs.row_off(c)), qreg[c], s);
+      dp = mfma32x32x16(ld_lds_128(cur, vo), doreg[c], dp);
+    }
+    const bool need_mask = (k0 + C::BK > N) || (CAUSAL && k0 + C::BK - 1 > qw0);
 #pragma unroll
-      for (int c = 0; c < C::NKC; ++c)
-        dp = mfma32x32x16(ld_lds_128(buf + C::OFF_V, l32 * C::RS + (16 * c + 8 * hf) * 2),
-                          doreg[c], dp);
-      const bool need_mask = (k0 + C::BK > N) || (CAUSAL && k0 + C::BK - 1 > qw0);
+    for (int kt = 0; kt < 2; ++kt) {
+      float dsv[8];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int gg = 0; gg < 2; ++gg) {
+        const int g = 2 * kt + gg;
         u32x4 bc = {0, 0, 0, 0};
-        if constexpr (DROP) bc = ld_lds_u32x4(buf + C::OFF_BC, (8 * g + 4 * hf) * 4);
+        if constexpr (DROP) bc = *reinterpret_cast<const u32x4*>(bcc + 8 * g + 4 * hf);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float pv = exp2_hw(s[r] * p.c2 - lse2);
+          float pv = exp2_hw(fmaf(s[r], p.c2, -lse2));
           if (need_mask) {
             const int key = k0 + c_row(r, hf);
             if (key >= N || (CAUSAL && key > myq)) pv = 0.f;
           }
           float dpv = dp[r];
           if constexpr (DROP) dpv = keep(arow, bc[e], p.drop_t) ? dpv * p.drop_r : 0.f;
-          s[r] = pv * (dpv - dq_d);
+          dsv[4 * gg + e] = pv * (dpv - dq_d);
         }
       }
+      const u32x4 sop = {pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3]),
+                         pack_bf16x2(dsv[4], dsv[5]), pack_bf16x2(dsv[6], dsv[7])};
+      // dQ^T += K^T dS^T over the 16 keys of step kt.
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int rb = kt * 8;
-        const u32x4 sop = {pack_bf16x2(s[rb + 0], s[rb + 1]), pack_bf16x2(s[rb + 2], s[rb + 3]),
-                           pack_bf16x2(s[rb + 4], s[rb + 5]), pack_bf16x2(s[rb + 6], s[rb + 7])};
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-          dqacc[db] = mfma32x32x16(
-              ld_lds_128(buf + C::OFF_KT, (db * 32 + l32) * C::TS + (16 * kt + 8 * hf) * 2), sop,
-              dqacc[db]);
-      }
+      for (int db = 0; db < C::NDB; ++db)
+        dqacc[db] = mfma32x32x16(ofs.tr_frag(cur, db, kt), sop, dqacc[db]);
     }
-    if (t + 1 < ntiles) store_tile(smem + ((t + 1) & 1) * C::BUF);
-    __syncthreads();
+  };
+
+  issue(st0, bc0, 0);
+  for (int t = 0; t < ntiles; t += 2) {
+    step(st0, bc0, st1, bc1, t);
+    if (t + 1 < ntiles) step(st1, bc1, st0, bc0, t + 1);
   }
 
-  if (qok) {
+  if (myq < N) {
     uint16_t* dqrow = static_cast<uint16_t*>(p.dq) + base + (int64_t)myq * rs;
     const float sc = p.scale;
 #pragma unroll

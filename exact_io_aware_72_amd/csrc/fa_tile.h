@@ -7,7 +7,8 @@
 // operand reads of one LDS pass land in distinct banks:
 //   kRow: 16-byte reads, lane = row, one chunk column (operands along D);
 //   kTr:  8-byte transposing reads (ds_read_b64_tr_b16), four rows and two
-//         chunks per 16 lanes (operands along the rows).
+//         chunks per 16 lanes (operands along the rows);
+//   kBoth: both of the above from one copy of the tile.
 // A direct-to-LDS buffer load writes 64 consecutive 16-byte slots (one per
 // lane, in lane order), so each load instruction fills 8 rows of one group
 // (or 32 rows of the tail) and the swizzle is applied by choosing which chunk
@@ -19,7 +20,7 @@
 
 namespace fa {
 
-enum class Swz { kRow, kTr };
+enum class Swz { kRow, kTr, kBoth };
 
 template <int R, int D, Swz S>
 struct Tile {
@@ -34,11 +35,17 @@ struct Tile {
   static constexpr int NTAIL = TC ? R / 32 : 0;
   static constexpr int NLOAD = NFULL + NTAIL;
 
+  // Chunk swizzle of row r. kRow: distinct over any 8 (and, by row parity,
+  // 16) consecutive rows. kTr: rows 4k..4k+3 get values differing in bits 1-2,
+  // so two adjacent chunks of four rows land in 8 distinct positions. kBoth
+  // satisfies both conditions.
   __device__ __forceinline__ static int sw(int r) {
-    return S == Swz::kRow ? ((r ^ (r >> 3)) & 7) : ((((r & 3) << 1) ^ (r >> 2)) & 7);
+    if constexpr (S == Swz::kRow) return (r ^ (r >> 3)) & 7;
+    if constexpr (S == Swz::kTr) return (((r & 3) << 1) ^ (r >> 2)) & 7;
+    return ((((r & 3) << 1) | ((r >> 2) & 1)) ^ (((r >> 3) & 1) << 1)) & 7;
   }
   __device__ __forceinline__ static int swt(int r) {
-    return S == Swz::kRow ? (((r >> 2) ^ (r >> 3)) & 1) : 0;
+    return S == Swz::kTr ? 0 : (((r >> 2) ^ (r >> 3)) & 1);
   }
   // Load instruction i (0 <= i < NLOAD): the LDS byte offset it writes
   // (uniform over the wave) and the row and 16-byte chunk this lane fetches.
