@@ -163,7 +163,7 @@ struct Both32 {
 };
 
 // ---------------------------------------------------------------------------
-// B2 (bf16): one work-group of 8 waves per (block of 256 keys, b, h); each
+// B2 (bf16): one work-group of NW waves per (block of 32 NW keys, b, h); each
 // wave owns 32 keys (lane = key) with their K rows in registers, the block's
 // V rows in LDS, and dK^T, dV^T accumulators. Query tiles of 32 rows of Q and
 // dO stream through two LDS stages by direct-to-LDS loads; one copy of each
@@ -171,8 +171,9 @@ struct Both32 {
 // transposing reads (A operand of dK^T += Q^T dS and dV^T += dO^T P~).
 template <int D>
 struct DkdvCfg {
-  static constexpr int NT = 512;   // 8 waves
-  static constexpr int BK = 256;   // keys per work-group
+  static constexpr int NW = 4;     // waves per work-group (32 keys each)
+  static constexpr int NT = 64 * NW;
+  static constexpr int BK = 32 * NW;  // keys per work-group
   static constexpr int BQ = 32;    // queries per tile
   static constexpr int NKC = D / 16;
   static constexpr int DP = (D + 31) / 32 * 32;
@@ -181,12 +182,12 @@ struct DkdvCfg {
   using VB = Tile<BK, D, Swz::kRow>;   // the block's V rows
   static constexpr int STAGE = 2 * QT::BYTES;
   static constexpr int NLOAD = 2 * QT::NLOAD;
-  static constexpr int LPW = (NLOAD + 7) / 8;
-  static constexpr int VLPW = (VB::NLOAD + 7) / 8;
+  static constexpr int LPW = (NLOAD + NW - 1) / NW;
+  static constexpr int VLPW = (VB::NLOAD + NW - 1) / NW;
 };
 
 template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdParams p) {
+__global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams p) {
   using C = DkdvCfg<D>;
   using QT = typename C::QT;
   using VB = typename C::VB;
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdParams p) {
     const BufRes rvb = make_bufres(Vg + (int64_t)k0 * rs, (uint32_t)(N - k0) * rs2);
 #pragma unroll
     for (int m = 0; m < C::VLPW; ++m) {
-      const int i = (wave & 7) + 8 * m;
+      const int i = (wave % C::NW) + C::NW * m;
       if (i < VB::NLOAD) {
         int off, row, ch;
         VB::load_slot(i, lane, off, row, ch);
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdParams p) {
   int dlds[C::LPW];
 #pragma unroll
   for (int m = 0; m < C::LPW; ++m) {
-    const int i = (wave & 7) + 8 * m;
+    const int i = (wave % C::NW) + C::NW * m;
     int off = 0, row = 0, ch = 0;
     if (i < QT::NLOAD) {
       QT::load_slot(i, lane, off, row, ch);
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdParams p) {
     const BufRes ro = make_bufres(dOg + (int64_t)qt0 * rs, left);
 #pragma unroll
     for (int m = 0; m < C::LPW; ++m) {
-      const int i = (wave & 7) + 8 * m;
+      const int i = (wave % C::NW) + C::NW * m;
       if (i < C::NLOAD) lds_dma_16(i < QT::NLOAD ? rq : ro, stage + dlds[m], dsrc[m]);
     }
   };
@@ -340,7 +341,14 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdParams p) {
         s = mfma32x32x16(ld_lds_128(cur, o), kreg[c], s);
         dp = mfma32x32x16(ld_lds_128(cur, QT::BYTES + o), ld_lds_128(vblk, vo), dp);
       }
-      const bool need_mask = CAUSAL && (qt0 < kw0 + 31);
+      // Issue order: the three LDS reads of step c + 2 go out before the two
+      // products of step c, so read latency overlaps the matrix cores.
+      sched_lds_ahead<C::NKC, 3, 2>();
+      if (CAUSAL && qt0 < kw0 + 31) {
+        // diagonal tile: keys after the query get probability exp2(-inf) = 0
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = mykey > qt0 + c_row(r, hf) ? -INFINITY : s[r];
+      }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         float pt[8], dsv[8];
@@ -354,8 +362,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            float pv = exp2_hw(fmaf(s[r], p.c2, -l2[e]));
-            if (need_mask) pv = mykey > qt0 + c_row(r, hf) ? 0.f : pv;
+            const float pv = exp2_hw(fmaf(s[r], p.c2, -l2[e]));
             float dpv = dp[r];
             float ptv = pv;
             if constexpr (DROP) {
@@ -378,6 +385,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdParams p) {
           dkacc[db] = mfma32x32x16(ofs.tr_frag(cur, db, kt), sop, dkacc[db]);
         }
       }
+      // Statistics reads first, then the four transposing reads of step i + 1
+      // ahead of the two products of step i.
+      sched_lds_ahead<2 * C::NDB, 4, 2, DROP ? 12 : 8, 1>();
     }
     if (more) stat_store(lsn, ddn, arn);
   };
@@ -545,6 +555,7 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
       s = mfma32x32x16(ld_lds_128(cur, ofs.row_off(c)), qreg[c], s);
       dp = mfma32x32x16(ld_lds_128(cur, vo), doreg[c], dp);
     }
+    sched_lds_ahead<C::NKC, 2, 2>();
     const bool need_mask = (k0 + C::BK > N) || (CAUSAL && k0 + C::BK - 1 > qw0);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -574,6 +585,7 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
       for (int db = 0; db < C::NDB; ++db)
         dqacc[db] = mfma32x32x16(ofs.tr_frag(cur, db, kt), sop, dqacc[db]);
     }
+    sched_lds_ahead<2 * C::NDB, 2, 1, DROP ? 4 : 0>();
   };
 
   issue(st0, bc0, 0);
@@ -854,7 +866,8 @@ hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t s, bool bf16) {
 
 hipError_t launch_bwd_dkdv_bf16(const AttnArgs& a, hipStream_t s) {
   const BwdParams prm = make_params(a);
-  const dim3 grid((unsigned)(((a.N + 255) / 256) * a.B * a.H)), block(512);
+  constexpr int BK = DkdvCfg<64>::BK, NT = DkdvCfg<64>::NT;
+  const dim3 grid((unsigned)(((a.N + BK - 1) / BK) * a.B * a.H)), block(NT);
   FA_DISPATCH(bwd_dkdv_bf16_kernel, a.d, a.causal, a.dropout, grid, block, s, prm);
   return hipGetLastError();
 }

@@ -125,6 +125,24 @@ __device__ __forceinline__ StageItem stage_item(int it, int ngroups, int nchunks
   return s;
 }
 
+// Scheduling hint for a fully unrolled loop of `steps` steps, each issuing
+// `reads` LDS reads and `mfmas` matrix products that consume them: the reads
+// of the first `ahead` steps go first, then every step's products are
+// followed by the reads of the step `ahead` steps later. Placed after the loop, in the same
+// basic block; it only constrains instruction order.
+// `first` extra reads (operands of other work in the block) join the first
+// group; `ahead` is the lookahead in steps.
+template <int steps, int reads, int mfmas, int first = 0, int ahead = 2>
+__device__ __forceinline__ void sched_lds_ahead() {
+  constexpr int kMfma = 0x008, kDsRead = 0x100;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, first + ahead * reads, 0);
+#pragma unroll
+  for (int c = 0; c < steps; ++c) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, mfmas, 0);
+    if (c + ahead < steps) __builtin_amdgcn_sched_group_barrier(kDsRead, reads, 0);
+  }
+}
+
 // Row index within a 32-row C tile held by accumulator register r of lane half s.
 __device__ __forceinline__ constexpr int c_row(int r, int s) { return 8 * (r >> 2) + 4 * s + (r & 3); }
 
