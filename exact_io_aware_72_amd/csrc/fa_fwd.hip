@@ -195,6 +195,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
       s0 = mfma32x32x16(ld_lds_128(cur, o0), qreg[c], s0);
       s1 = mfma32x32x16(ld_lds_128(cur, o1), qreg[c], s1);
     }
+    sched_lds_ahead<C::NKC, 2, 2>();
     if ((k0 + C::BN > N) || (CAUSAL && k0 + C::BN - 1 > qw0)) {
       const int lim = CAUSAL ? min(myq, N - 1) : N - 1;  // last visible key
 #pragma unroll
