@@ -102,6 +102,39 @@ def run_gpu(w, steps, warmup, torch, fa):
     }
 
 
+def kernel_source_digest():
+    """SHA-256 over the kernel sources and the build flags: HBM traffic
+    figures recorded under profiles/ are valid only for this digest."""
+    import hashlib
+    from exact_io_aware_72_amd import build as fa_build
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(fa_build.CSRC)):
+        with open(os.path.join(fa_build.CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    h.update(" ".join(f for f in fa_build.COMMON_FLAGS if not f.startswith("/")).encode())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload_name, kernel):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) that
+    profiles/hbm_traffic_*.txt records for this kernel and workload, or None
+    when none is recorded or the kernels changed since it was measured."""
+    import glob
+    digest = kernel_source_digest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "hbm_traffic_*.txt"))):
+        with open(path) as f:
+            for line in f:
+                if not line.startswith("kernel="):
+                    continue
+                kv = dict(tok.split("=", 1) for tok in line.split())
+                if kv.get("kernel") == kernel and kv.get("workload") == workload_name:
+                    if kv.get("digest") != digest:
+                        return None
+                    return {"fetch_bytes": float(kv["fetch_bytes"]), "write_bytes": float(kv["write_bytes"]),
+                            "source": os.path.relpath(path, ROOT)}
+    return None
+
+
 def roofline(w, kernel_ms):
     units = kernel_units(w)
     name = max(kernel_ms, key=kernel_ms.get)
@@ -111,9 +144,11 @@ def roofline(w, kernel_ms):
         achieved, peak, unit = work / sec / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = work / sec / 1e9, PEAK_HBM_GBS, "GB/s"
+    rec = recorded_traffic(w.name, name)
     return {"kernel": name, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
             "frac": achieved / peak, "avg_ms": kernel_ms[name], "work_per_launch": work,
-            "traffic": None}
+            "traffic": None if rec is None else rec["fetch_bytes"] + rec["write_bytes"],
+            "traffic_detail": rec}
 
 
 def cpu_baseline(w, seconds):
