@@ -131,10 +131,12 @@ __device__ __forceinline__ StageItem stage_item(int it, int ngroups, int nchunks
 // followed by the reads of the step `ahead` steps later. Placed after the loop, in the same
 // basic block; it only constrains instruction order.
 // `first` extra reads (operands of other work in the block) join the first
-// group; `ahead` is the lookahead in steps.
-template <int steps, int reads, int mfmas, int first = 0, int ahead = 2>
+// group; `ahead` is the lookahead in steps. `ds_mask` selects the LDS
+// instruction class (0x100: reads; 0x080: any LDS access, which also covers
+// the transposing reads).
+template <int steps, int reads, int mfmas, int first = 0, int ahead = 2, int ds_mask = 0x100>
 __device__ __forceinline__ void sched_lds_ahead() {
-  constexpr int kMfma = 0x008, kDsRead = 0x100;
+  constexpr int kMfma = 0x008, kDsRead = ds_mask;
   __builtin_amdgcn_sched_group_barrier(kDsRead, first + ahead * reads, 0);
 #pragma unroll
   for (int c = 0; c < steps; ++c) {
