@@ -6,7 +6,9 @@ HIP events between them time each kernel. Inputs are resident in HBM before
 the timed region. Prints one JSON line.
 
 Workload: B=2, H=16, N=8192, d=128, causal, bf16 (the N=8K headline shape);
-the N=32K, d=80 shape is reported alongside under "also".
+the N=32K, d=80 shape and a packed batch of sixteen causal sequences of
+512..8192 tokens (with the time the same sequences take padded to the
+longest) are reported alongside under "also".
 FLOP convention: forward 4*B*H*N^2*d, halved for causal; backward 2.5x.
 """
 from __future__ import annotations
@@ -22,7 +24,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import WORKLOADS, counted_flops, make_inputs  # noqa: E402
+from workloads import (VARLEN_WORKLOADS, WORKLOADS, counted_flops, counted_flops_varlen,  # noqa: E402
+                       make_inputs, make_varlen_inputs)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
@@ -99,6 +102,60 @@ def run_gpu(w, steps, warmup, torch, fa):
         "fwd_tflops": fwd_f / (fwd_ms * 1e-3) / 1e12,
         "bwd_tflops": bwd_f / (bwd_ms * 1e-3) / 1e12,
         "kernel_ms": per,
+    }
+
+
+def run_gpu_varlen(wv, steps, warmup, torch, fa):
+    """Packed variable-length batch: forward_varlen + backward_varlen per step,
+    FLOPs counted per sequence. Also times the same sequences padded to the
+    longest one as a fixed-length batch (what padding would cost)."""
+    cu, inp = make_varlen_inputs(wv)
+    dev = {k: torch.from_numpy(v[0].view(np.int16)).view(torch.bfloat16).cuda() for k, v in inp.items()}
+    cu_d = torch.from_numpy(cu).cuda()
+    lengths = np.diff(cu)
+    maxlen = int(lengths.max())
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    total = q.shape[0]
+    o = torch.empty_like(q)
+    lse = torch.empty((wv.H, total), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty((wv.H, total), dtype=torch.float32, device="cuda")
+    args = (wv.causal, wv.dropout_p, wv.dropout_seed, wv.scale)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        fa.forward_varlen(q, k, v, cu_d, maxlen, *args, out=o, lse=lse)
+        if ev:
+            ev[1].record()
+        fa.backward_varlen(q, k, v, o, do, lse, cu_d, maxlen, *args, dq=dq, dk=dk, dv=dv,
+                           workspace=ws)
+        if ev:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_step = evs[0][0].elapsed_time(evs[-1][2]) / steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    fwd_f, bwd_f = counted_flops_varlen(lengths, wv.H, wv.d, wv.causal, True)
+    del dev, q, k, v, do, o, dq, dk, dv
+    torch.cuda.empty_cache()
+    padded = WORKLOADS[3].with_(B=len(lengths), H=wv.H, N=maxlen, d=wv.d, causal=wv.causal,
+                                dropout_p=wv.dropout_p)
+    rp = run_gpu(padded, max(2, steps // 2), 1, torch, fa)
+    return {
+        "workload": wv.name, "num_seqs": len(lengths), "total_tokens": int(total),
+        "max_seqlen": maxlen, "tflops": (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12,
+        "ms_per_step": ms_step, "pct_of_peak": 100.0 * (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
+        / PEAK_BF16_TFLOPS,
+        "fwd_tflops": fwd_f / (fwd_ms * 1e-3) / 1e12, "bwd_tflops": bwd_f / (bwd_ms * 1e-3) / 1e12,
+        "padded_fixed_length_ms_per_step": rp["ms_per_step"],
     }
 
 
@@ -187,6 +244,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--also", type=int, nargs="*", default=[4])
+    ap.add_argument("--also-varlen", nargs="*", default=["varlen16"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -249,6 +307,9 @@ def main():
                      "pct_of_peak": 100.0 * ra["tflops"] / PEAK_BF16_TFLOPS,
                      "fwd_tflops": ra["fwd_tflops"], "bwd_tflops": ra["bwd_tflops"],
                      "kernel_ms": ra["kernel_ms"], "roofline": roofline(wa, ra["kernel_ms"])})
+        torch.cuda.empty_cache()
+    for name in a.also_varlen:
+        also.append(run_gpu_varlen(VARLEN_WORKLOADS[name], max(3, a.steps // 4), 2, torch, fa))
         torch.cuda.empty_cache()
     line["also"] = also
     line["cpu_baseline"] = None if a.no_cpu_baseline else cpu_baseline(w, a.cpu_seconds)

@@ -19,7 +19,8 @@ import os
 __all__ = [
     "FAError", "lib", "lib_path", "version", "forward", "backward", "backward_preprocess",
     "backward_dkdv", "backward_dq", "workspace_bytes", "dropout_mask", "FlashAttnFunction",
-    "flash_attention", "EXPORTED_SYMBOLS", "STATUS",
+    "flash_attention", "forward_varlen", "backward_varlen", "varlen_workspace_bytes",
+    "EXPORTED_SYMBOLS", "STATUS",
 ]
 
 FA_F32, FA_BF16 = 0, 1
@@ -31,6 +32,7 @@ STATUS = {
 EXPORTED_SYMBOLS = (
     "fa_forward", "fa_backward", "fa_backward_workspace_bytes", "fa_backward_preprocess",
     "fa_backward_dkdv", "fa_backward_dq", "fa_dropout_mask", "fa_status_string", "fa_version",
+    "fa_forward_varlen", "fa_backward_varlen", "fa_backward_varlen_workspace_bytes",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,6 +59,9 @@ _SIGS = {
     "fa_backward_dkdv": (_i, [_vp] * 8 + [_i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
     "fa_backward_dq": (_i, [_vp] * 7 + [_i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
     "fa_dropout_mask": (_i, [_u64, _i, _i, _i, _f, _i, _i, _i, _i, _vp, _vp]),
+    "fa_forward_varlen": (_i, [_vp] * 6 + [_i, _i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
+    "fa_backward_varlen_workspace_bytes": (_sz, [_i, _i, _i]),
+    "fa_backward_varlen": (_i, [_vp] * 11 + [_i, _i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
     "fa_version": (ctypes.c_char_p, []),
 }
@@ -202,6 +207,73 @@ def backward_dq(q, k, v, dout, lse, workspace, causal=False, dropout_p=0.0, seed
                               _stream(q), _code(q))
     _check(st, "fa_backward_dq")
     return dq
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length batches: tensors (total, num_heads, head_dim), sequence
+# s in rows cu_seqlens[s] .. cu_seqlens[s+1]-1 (cu_seqlens: int32 on the GPU).
+def _shape_varlen(q, *others):
+    if q.dim() != 3:
+        raise ValueError("expected packed tensors of shape (total_tokens, num_heads, head_dim)")
+    for t in (q,) + others:
+        if t.shape != q.shape:
+            raise ValueError(f"shape mismatch: {tuple(t.shape)} vs {tuple(q.shape)}")
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v (and o, dout) must share one dtype")
+        if t.device != q.device or t.device.type != "cuda":
+            raise ValueError("tensors must live on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return q.shape
+
+
+def _cu(cu_seqlens, q):
+    torch = _torch()
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of num_seqs + 1 offsets")
+    if cu_seqlens.device != q.device or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous tensor on the tensors' GPU")
+    return cu_seqlens.numel() - 1
+
+
+def varlen_workspace_bytes(total: int, H: int, d: int) -> int:
+    return int(lib().fa_backward_varlen_workspace_bytes(total, H, d))
+
+
+def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, dropout_p=0.0, seed=0,
+                   scale=None, out=None, lse=None):
+    """Returns (o, lse): o like q; lse float32 (H, total), natural log."""
+    torch = _torch()
+    total, H, d = _shape_varlen(q, k, v)
+    nseq = _cu(cu_seqlens, q)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((H, total), dtype=torch.float32, device=q.device) if lse is None else lse
+    _shape_varlen(q, o)
+    st = lib().fa_forward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                 lse_t.data_ptr(), cu_seqlens.data_ptr(), nseq, total,
+                                 int(max_seqlen), H, d, _scale(scale, d), int(bool(causal)),
+                                 float(dropout_p), int(seed), _stream(q), _code(q))
+    _check(st, "fa_forward_varlen")
+    return o, lse_t
+
+
+def backward_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen, causal=False, dropout_p=0.0,
+                    seed=0, scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """Returns (dq, dk, dv) for L = sum(dout * o) over a packed batch."""
+    torch = _torch()
+    total, H, d = _shape_varlen(q, k, v, o, dout)
+    nseq = _cu(cu_seqlens, q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    ws = torch.empty((H, total), dtype=torch.float32, device=q.device) if workspace is None else workspace
+    st = lib().fa_backward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                  dv.data_ptr(), ws.data_ptr(), cu_seqlens.data_ptr(), nseq, total,
+                                  int(max_seqlen), H, d, _scale(scale, d), int(bool(causal)),
+                                  float(dropout_p), int(seed), _stream(q), _code(q))
+    _check(st, "fa_backward_varlen")
+    return dq, dk, dv
 
 
 def dropout_mask(seed, b, h, H, dropout_p, row0, col0, rows, cols, device="cuda"):

@@ -194,6 +194,95 @@ FA_EXPORT int fa_backward(const void* q, const void* k, const void* v, const voi
   return hip_status(bf16 ? fa::launch_bwd_dq_bf16(a, s) : fa::launch_bwd_dq_f32(a, s));
 }
 
+// ---------------------------------------------------------------------------
+// Packed variable-length batches.
+namespace {
+int check_varlen(const int* cu, int num_seqs, int total, int max_seqlen, int H, int d,
+                 int dtype) {
+  // Per-sequence rules are those of a fixed-length batch of num_seqs items of
+  // max_seqlen rows (grid sizes, 32-bit offsets within one sequence).
+  FA_TRY(check_problem(num_seqs, H, max_seqlen, d, dtype));
+  if (cu == nullptr) return FA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(cu) & 3u) != 0) return FA_ERR_ALIGN;
+  if (total < 0) return FA_ERR_SHAPE;
+  if ((int64_t)total * H > (int64_t)1 << 36) return FA_ERR_SHAPE;
+  if (((int64_t)total * H + 15) / 16 > (int64_t)INT32_MAX) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+void set_varlen(fa::AttnArgs& a, const int* cu, int num_seqs, int total, int max_seqlen, int H,
+                int d) {
+  a.cu_seqlens = cu;
+  a.total = total;
+  a.B = num_seqs;
+  a.N = max_seqlen;
+  a.H = H;
+  a.d = d;
+}
+}  // namespace
+
+FA_EXPORT int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int* cu_seqlens, int num_seqs, int total, int max_seqlen,
+                                int H, int d, float scale, int causal, float dropout_p,
+                                uint64_t seed, void* stream, int dtype) {
+  FA_TRY(check_varlen(cu_seqlens, num_seqs, total, max_seqlen, H, d, dtype));
+  FA_TRY(check_dropout(dropout_p));
+  FA_TRY(check_scale(scale));
+  if (total == 0) return FA_OK;  // nothing to compute
+  FA_TRY(check_ptrs({q, k, v, o, lse}));
+  fa::AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o_out = o;
+  a.lse_out = lse;
+  set_varlen(a, cu_seqlens, num_seqs, total, max_seqlen, H, d);
+  a.scale = scale;
+  a.causal = causal != 0;
+  set_dropout(a, dropout_p, seed);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(dtype == FA_BF16 ? fa::launch_forward_bf16(a, s)
+                                     : fa::launch_forward_f32(a, s));
+}
+
+FA_EXPORT size_t fa_backward_varlen_workspace_bytes(int total, int H, int d) {
+  if (total < 0 || H < 1 || (d != 64 && d != 80 && d != 128)) return 0;
+  if ((int64_t)total * H > (int64_t)1 << 36) return 0;
+  return (size_t)4 * (size_t)H * (size_t)total;
+}
+
+FA_EXPORT int fa_backward_varlen(const void* q, const void* k, const void* v, const void* o,
+                                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                 float* workspace, const int* cu_seqlens, int num_seqs, int total,
+                                 int max_seqlen, int H, int d, float scale, int causal,
+                                 float dropout_p, uint64_t seed, void* stream, int dtype) {
+  FA_TRY(check_varlen(cu_seqlens, num_seqs, total, max_seqlen, H, d, dtype));
+  FA_TRY(check_dropout(dropout_p));
+  FA_TRY(check_scale(scale));
+  if (total == 0) return FA_OK;  // nothing to compute
+  FA_TRY(check_ptrs({q, k, v, o, dout, lse, dq, dk, dv, workspace}));
+  fa::AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dsum = workspace;
+  a.dsum_out = workspace;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  set_varlen(a, cu_seqlens, num_seqs, total, max_seqlen, H, d);
+  a.scale = scale;
+  a.causal = causal != 0;
+  set_dropout(a, dropout_p, seed);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == FA_BF16;
+  FA_TRY(hip_status(fa::launch_bwd_preprocess(a, s, bf16)));
+  FA_TRY(hip_status(bf16 ? fa::launch_bwd_dkdv_bf16(a, s) : fa::launch_bwd_dkdv_f32(a, s)));
+  return hip_status(bf16 ? fa::launch_bwd_dq_bf16(a, s) : fa::launch_bwd_dq_f32(a, s));
+}
+
 FA_EXPORT int fa_dropout_mask(uint64_t seed, int b, int h, int H, float dropout_p, int row0,
                               int col0, int rows, int cols, uint8_t* out, void* stream) {
   FA_TRY(check_dropout(dropout_p));

@@ -37,7 +37,9 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  int B, H, N;
+  int B, H, N;  // N: rows per sequence (the longest one for packed batches)
+  const int* cu;  // packed variable-length batch offsets, or nullptr
+  int total;
   float scale;
   float c2;  // scale * log2(e)
   uint32_t drop_t;
@@ -59,6 +61,8 @@ BwdParams make_params(const AttnArgs& a) {
   p.B = a.B;
   p.H = a.H;
   p.N = a.N;
+  p.cu = a.cu_seqlens;
+  p.total = a.total;
   p.scale = a.scale;
   p.c2 = a.scale * kLog2e;
   p.drop_t = a.drop_threshold;
@@ -70,14 +74,17 @@ BwdParams make_params(const AttnArgs& a) {
 // ---------------------------------------------------------------------------
 // B1: D[b][h][i] = sum_c dO[b][i][h][c] * O[b][i][h][c], fp32. Sixteen lanes
 // per row, 16-byte loads; bound by HBM bandwidth.
+// Rows are (token, head) pairs in storage order; the statistics index is
+// [b][h][n] for fixed-length batches (total == 0) and [h][token] for packed
+// variable-length batches of `total` tokens.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const void* __restrict__ o,
                                                       const void* __restrict__ dout,
                                                       float* __restrict__ dsum, int B, int H,
-                                                      int N) {
+                                                      int N, int total) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int NCH = D * ESZ / 16;
-  const int64_t rows = (int64_t)B * N * H;
+  const int64_t rows = total ? (int64_t)total * H : (int64_t)B * N * H;
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   float acc = 0.f;
@@ -105,9 +112,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const void* __restrict__ o
   if (row < rows && sub == 0) {
     const int h = (int)(row % H);
     const int64_t bn = row / H;
-    const int n = (int)(bn % N);
-    const int b = (int)(bn / N);
-    dsum[((int64_t)b * H + h) * N + n] = acc;
+    if (total) {
+      dsum[(int64_t)h * total + bn] = acc;
+    } else {
+      const int n = (int)(bn % N);
+      const int b = (int)(bn / N);
+      dsum[((int64_t)b * H + h) * N + n] = acc;
+    }
   }
 }
 
@@ -206,22 +217,25 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
-  const int N = p.N, H = p.H;
-  const int nkb = (N + C::BK - 1) / C::BK;
+  const int H = p.H;
+  const int nkb = (p.N + C::BK - 1) / C::BK;
   const BlockMap bm = map_block(blockIdx.x, nkb, p.B * H);
   const int kblk = bm.rank;  // causal: key block 0 sees the most queries
   const int b = bm.bh / H, h = bm.bh - b * H;
+  const SeqRows sr = seq_rows(p.cu, p.total, b, h, H, D, p.N);
+  const int N = sr.n;
   const int k0 = kblk * C::BK;
+  if (k0 >= N) return;  // block past the end of a shorter sequence
   const int kw0 = k0 + wave * 32;
   const int mykey = kw0 + l32;
   const int64_t rs = (int64_t)H * D;
-  const int64_t base = ((int64_t)b * N * H + h) * D;
+  const int64_t base = sr.base;
   const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + base;
   const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + base;
   const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + base;
   const uint16_t* dOg = static_cast<const uint16_t*>(p.dout) + base;
   const uint32_t rs2 = (uint32_t)(H * D * 2);
-  const int64_t statoff = ((int64_t)b * H + h) * N;
+  const int64_t statoff = sr.stat;
   const BufRes rl = make_bufres(p.lse + statoff, (uint32_t)N * 4);
   const BufRes rd = make_bufres(p.dsum + statoff, (uint32_t)N * 4);
 
@@ -458,16 +472,19 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
-  const int N = p.N, H = p.H;
-  const int nqb = (N + C::BQ - 1) / C::BQ;
+  const int H = p.H;
+  const int nqb = (p.N + C::BQ - 1) / C::BQ;
   const BlockMap bm = map_block(blockIdx.x, nqb, p.B * H);
   const int qb = CAUSAL ? (nqb - 1 - bm.rank) : bm.rank;
   const int b = bm.bh / H, h = bm.bh - b * H;
+  const SeqRows sr = seq_rows(p.cu, p.total, b, h, H, D, p.N);
+  const int N = sr.n;
   const int q0 = qb * C::BQ;
+  if (q0 >= N) return;  // block past the end of a shorter sequence
   const int qw0 = q0 + wave * 32;
   const int myq = qw0 + l32;
   const int64_t rs = (int64_t)H * D;
-  const int64_t base = ((int64_t)b * N * H + h) * D;
+  const int64_t base = sr.base;
   const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + base;
   const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + base;
   const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + base;
@@ -475,7 +492,7 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
   const uint32_t rs2 = (uint32_t)(H * D * 2);
   const uint32_t nbytes = (uint32_t)N * rs2;
   const BufRes rq = make_bufres(Qg, nbytes), rdo = make_bufres(dOg, nbytes);
-  const int64_t statoff = ((int64_t)b * H + h) * N;
+  const int64_t statoff = sr.stat;
   const BufRes rl = make_bufres(p.lse + statoff, (uint32_t)N * 4);
   const BufRes rd = make_bufres(p.dsum + statoff, (uint32_t)N * 4);
 
@@ -625,19 +642,22 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdParams p) {
 
   const int tid = threadIdx.x;
   const int ki = tid >> 2, part = tid & 3;
-  const int N = p.N, H = p.H;
-  const int nkb = (N + BKW - 1) / BKW;
+  const int H = p.H;
+  const int nkb = (p.N + BKW - 1) / BKW;
   const BlockMap bm = map_block(blockIdx.x, nkb, p.B * H);
   const int b = bm.bh / H, h = bm.bh - b * H;
+  const SeqRows sr = seq_rows(p.cu, p.total, b, h, H, D, p.N);
+  const int N = sr.n;
   const int k0 = bm.rank * BKW;
+  if (k0 >= N) return;  // block past the end of a shorter sequence
   const int mykey = k0 + ki;
   const int64_t rs = (int64_t)H * D;
-  const int64_t base = ((int64_t)b * N * H + h) * D;
+  const int64_t base = sr.base;
   const float* Qg = static_cast<const float*>(p.q) + base;
   const float* Kg = static_cast<const float*>(p.k) + base;
   const float* Vg = static_cast<const float*>(p.v) + base;
   const float* dOg = static_cast<const float*>(p.dout) + base;
-  const int64_t statoff = ((int64_t)b * H + h) * N;
+  const int64_t statoff = sr.stat;
 
   float kv[DQ], vv[DQ], dk[DQ], dv[DQ];
   const bool kok = mykey < N;
@@ -724,20 +744,23 @@ __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdParams p) {
 
   const int tid = threadIdx.x;
   const int qi = tid >> 2, part = tid & 3;
-  const int N = p.N, H = p.H;
-  const int nqb = (N + BQW - 1) / BQW;
+  const int H = p.H;
+  const int nqb = (p.N + BQW - 1) / BQW;
   const BlockMap bm = map_block(blockIdx.x, nqb, p.B * H);
   const int qb = CAUSAL ? (nqb - 1 - bm.rank) : bm.rank;
   const int b = bm.bh / H, h = bm.bh - b * H;
+  const SeqRows sr = seq_rows(p.cu, p.total, b, h, H, D, p.N);
+  const int N = sr.n;
   const int q0 = qb * BQW;
+  if (q0 >= N) return;  // block past the end of a shorter sequence
   const int myq = q0 + qi;
   const int64_t rs = (int64_t)H * D;
-  const int64_t base = ((int64_t)b * N * H + h) * D;
+  const int64_t base = sr.base;
   const float* Qg = static_cast<const float*>(p.q) + base;
   const float* Kg = static_cast<const float*>(p.k) + base;
   const float* Vg = static_cast<const float*>(p.v) + base;
   const float* dOg = static_cast<const float*>(p.dout) + base;
-  const int64_t statoff = ((int64_t)b * H + h) * N;
+  const int64_t statoff = sr.stat;
 
   const bool qok = myq < N;
   float qv[DQ], gv[DQ], dq[DQ];
@@ -843,16 +866,18 @@ __global__ __launch_bounds__(256) void dropout_mask_kernel(uint64_t seed, int b,
 }  // namespace
 
 hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t s, bool bf16) {
-  const int64_t rows = (int64_t)a.B * a.N * a.H;
+  const int64_t rows = a.cu_seqlens ? (int64_t)a.total * a.H : (int64_t)a.B * a.N * a.H;
+  const int total = a.cu_seqlens ? a.total : 0;
+  if (rows == 0) return hipSuccess;
   const dim3 grid((unsigned)((rows + 15) / 16)), block(256);
 #define FA_PRE(D)                                                                             \
   case D:                                                                                     \
     if (bf16)                                                                                 \
       hipLaunchKernelGGL((bwd_pre_kernel<D, true>), grid, block, 0, s, a.o, a.dout, a.dsum_out, \
-                         a.B, a.H, a.N);                                                      \
+                         a.B, a.H, a.N, total);                                               \
     else                                                                                      \
       hipLaunchKernelGGL((bwd_pre_kernel<D, false>), grid, block, 0, s, a.o, a.dout,          \
-                         a.dsum_out, a.B, a.H, a.N);                                          \
+                         a.dsum_out, a.B, a.H, a.N, total);                                   \
     break;
   switch (a.d) {
     FA_PRE(64)

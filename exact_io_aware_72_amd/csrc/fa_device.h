@@ -174,11 +174,44 @@ __device__ __forceinline__ void st_lds_transpose4x8(char* base, int row_bytes, i
   }
 }
 
+// Rows of one (sequence, head) pair: the sequence length, the element offset
+// of its first row in the [.., H, d] tensors, and the offset of its first
+// entry in the per-row statistics (lse, D). Fixed-length batches (cu ==
+// nullptr): sequence s is batch item s of N rows, statistics [B][H][N].
+// Packed variable-length batches: sequence s holds rows cu[s]..cu[s+1]-1 of
+// [total, H, d] tensors, statistics [H][total]; offsets are clamped to
+// [0, total] and lengths to max_n so that malformed offsets cannot address
+// memory outside the tensors.
+struct SeqRows {
+  int n;
+  int64_t base;
+  int64_t stat;
+};
+__device__ __forceinline__ SeqRows seq_rows(const int* cu, int total, int s, int h, int H, int D,
+                                            int max_n) {
+  SeqRows r;
+  if (cu == nullptr) {
+    r.n = max_n;
+    r.base = ((int64_t)s * max_n * H + h) * D;
+    r.stat = ((int64_t)s * H + h) * max_n;
+  } else {
+    const int a = min(max(cu[s], 0), total);
+    const int e = min(max(cu[s + 1], a), total);
+    r.n = min(e - a, max_n);
+    r.base = ((int64_t)a * H + h) * D;
+    r.stat = (int64_t)h * total + a;
+  }
+  return r;
+}
+
 // Maps a linear work-group id to (block, batch*heads index). All blocks of a
 // (b, h) pair land on the same XCD (work-groups are dispatched round-robin
 // over the 8 XCDs), so K/V tiles re-read by neighbouring blocks stay in that
-// XCD's L2. `rank` runs from the first-dispatched to the last-dispatched
-// block of an XCD; callers turn it into a block index (heaviest first).
+// XCD's L2. Pairs are dealt to XCDs by index modulo 8, which spreads the
+// heads of each sequence over the XCDs: sequences of different lengths then
+// load the XCDs evenly (when the head count is a multiple of 8). Consecutive ids sweep all pairs of one XCD before the next
+// block rank, so the rank order (heaviest first for causal masks) holds on
+// every XCD.
 struct BlockMap {
   int rank;
   int bh;
@@ -190,7 +223,7 @@ __device__ __forceinline__ BlockMap map_block(int id, int nblk, int BH) {
     const int local = id >> 3;
     const int hpx = BH >> 3;
     m.rank = local / hpx;
-    m.bh = xcd * hpx + (local - m.rank * hpx);
+    m.bh = (local - m.rank * hpx) * 8 + xcd;
   } else {
     m.rank = id / BH;
     m.bh = id - m.rank * BH;

@@ -38,7 +38,9 @@ struct FwdParams {
   const uint16_t* v;
   uint16_t* o;
   float* lse;
-  int B, H, N;
+  int B, H, N;  // N: rows per sequence (the longest one for packed batches)
+  const int* cu;  // packed variable-length batch offsets, or nullptr
+  int total;
   float c2;  // scale * log2(e)
   uint32_t drop_t;
   float drop_r;
@@ -76,16 +78,19 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile decisions are scalar
   const int l32 = lane & 31, hf = lane >> 5;
-  const int N = p.N, H = p.H;
-  const int nqb = (N + C::BM - 1) / C::BM;
+  const int H = p.H;
+  const int nqb = (p.N + C::BM - 1) / C::BM;
   const BlockMap bm = map_block(blockIdx.x, nqb, p.B * H);
   const int qb = CAUSAL ? (nqb - 1 - bm.rank) : bm.rank;
   const int b = bm.bh / H, h = bm.bh - b * H;
+  const SeqRows sr = seq_rows(p.cu, p.total, b, h, H, D, p.N);
+  const int N = sr.n;
   const int q0 = qb * C::BM;
+  if (q0 >= N) return;  // block past the end of a shorter sequence
   const int qw0 = q0 + wave * 32;
   const int myq = qw0 + l32;
   const int64_t rs = (int64_t)H * D;
-  const int64_t base = ((int64_t)b * N * H + h) * D;
+  const int64_t base = sr.base;
   const uint16_t* Qg = p.q + base;
   const uint16_t* Kg = p.k + base;
   const uint16_t* Vg = p.v + base;
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
         }
       }
     }
-    if (hf == 0) p.lse[((int64_t)b * H + h) * N + myq] = (m + log2_hw(ltot)) * kLn2;
+    if (hf == 0) p.lse[sr.stat + myq] = (m + log2_hw(ltot)) * kLn2;
   }
 }
 
@@ -323,6 +328,8 @@ struct FwdParamsF {
   float* o;
   float* lse;
   int B, H, N;
+  const int* cu;
+  int total;
   float c2;
   uint32_t drop_t;
   float drop_r;
@@ -338,15 +345,18 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
 
   const int tid = threadIdx.x;
   const int qi = tid >> 1, part = tid & 1;
-  const int N = p.N, H = p.H;
-  const int nqb = (N + BM - 1) / BM;
+  const int H = p.H;
+  const int nqb = (p.N + BM - 1) / BM;
   const BlockMap bm = map_block(blockIdx.x, nqb, p.B * H);
   const int qb = CAUSAL ? (nqb - 1 - bm.rank) : bm.rank;
   const int b = bm.bh / H, h = bm.bh - b * H;
+  const SeqRows sr = seq_rows(p.cu, p.total, b, h, H, D, p.N);
+  const int N = sr.n;
   const int q0 = qb * BM;
+  if (q0 >= N) return;  // block past the end of a shorter sequence
   const int myq = q0 + qi;
   const int64_t rs = (int64_t)H * D;
-  const int64_t base = ((int64_t)b * N * H + h) * D;
+  const int64_t base = sr.base;
 
   float qv[DH], ov[DH];
   {
@@ -425,7 +435,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
     float* orow = p.o + base + (int64_t)myq * rs + part * DH;
 #pragma unroll
     for (int c = 0; c < DH; ++c) orow[c] = ov[c] * inv;
-    if (part == 0) p.lse[((int64_t)b * H + h) * N + myq] = (m + log2_hw(l)) * kLn2;
+    if (part == 0) p.lse[sr.stat + myq] = (m + log2_hw(l)) * kLn2;
   }
 }
 
@@ -473,6 +483,8 @@ hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s) {
   prm.B = a.B;
   prm.H = a.H;
   prm.N = a.N;
+  prm.cu = a.cu_seqlens;
+  prm.total = a.total;
   prm.c2 = a.scale * kLog2e;
   prm.drop_t = a.drop_threshold;
   prm.drop_r = a.drop_rescale;
@@ -497,6 +509,8 @@ hipError_t launch_forward_f32(const AttnArgs& a, hipStream_t s) {
   prm.B = a.B;
   prm.H = a.H;
   prm.N = a.N;
+  prm.cu = a.cu_seqlens;
+  prm.total = a.total;
   prm.c2 = a.scale * kLog2e;
   prm.drop_t = a.drop_threshold;
   prm.drop_r = a.drop_rescale;

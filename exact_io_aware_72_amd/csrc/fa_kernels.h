@@ -23,8 +23,13 @@ struct AttnArgs {
   void* dq = nullptr;
   void* dk = nullptr;
   void* dv = nullptr;
-  // problem
+  // problem. Fixed-length batches: B items of N rows each, statistics
+  // [B][H][N]. Packed variable-length batches (cu_seqlens != nullptr): B
+  // sequences, sequence s holding rows cu_seqlens[s]..cu_seqlens[s+1]-1 of
+  // [total][H][d] tensors, N = the longest sequence, statistics [H][total].
   int B = 0, H = 0, N = 0, d = 0;
+  const int* cu_seqlens = nullptr;
+  int total = 0;
   float scale = 0.f;
   bool causal = false;
   bool dropout = false;

@@ -126,6 +126,43 @@ int fa_backward_dq(const void* q, const void* k, const void* v, const void* dout
                    float dropout_p, uint64_t seed, void* stream, int dtype);
 
 /*
+ * Packed variable-length batches ("FlashAttention for Efficient Training",
+ * section 5.2 "Handling Variable Sequence Lengths": a query attends only to
+ * the keys of its own sequence, scores of other positions being -inf, and
+ * no work is spent on padding). Sequence s holds rows
+ * cu_seqlens[s] .. cu_seqlens[s+1]-1 of the packed tensors; positions,
+ * causal masking and the dropout hash (with b = s) count from the sequence
+ * start.
+ *   q, k, v, o, dout, dq, dk, dv  [total][H][d] (dtype)
+ *   lse, workspace                [H][total] float
+ *   cu_seqlens  DEVICE int32 array of num_seqs + 1 non-decreasing offsets
+ *               in [0, total] (normally cu_seqlens[0] = 0); every sequence
+ *               at most max_seqlen rows. Offsets are clamped to
+ *               [0, total] and lengths to max_seqlen on the device, so a
+ *               malformed array cannot address memory outside the tensors
+ *               (the results are then unspecified); rows outside every
+ *               sequence are not written.
+ *   num_seqs >= 1, max_seqlen >= 1, total >= 0 (total == 0: returns FA_OK
+ *   after the argument checks above, touching nothing); other arguments and errors
+ *   as for fa_forward / fa_backward (the shape rules apply to a batch of
+ *   num_seqs items of max_seqlen rows). cu_seqlens needs 4-byte alignment.
+ */
+int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int* cu_seqlens, int num_seqs, int total, int max_seqlen,
+                      int H, int d, float scale, int causal, float dropout_p, uint64_t seed,
+                      void* stream, int dtype);
+
+/* Bytes of the workspace fa_backward_varlen needs: 4*H*total (D as [H][total]).
+ * Returns 0 if the sizes are invalid. */
+size_t fa_backward_varlen_workspace_bytes(int total, int H, int d);
+
+int fa_backward_varlen(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       float* workspace, const int* cu_seqlens, int num_seqs, int total,
+                       int max_seqlen, int H, int d, float scale, int causal, float dropout_p,
+                       uint64_t seed, void* stream, int dtype);
+
+/*
  * Writes the dropout keep mask of head (b, h) for rows row0..row0+rows-1 and
  * columns col0..col0+cols-1 to out[rows][cols] (device, 1 = keep), with the
  * same device function the kernels use. The pages fuse dropout into the

@@ -91,6 +91,64 @@ def _dropped(p_mat, seed, b, h, H, dropout_p, rows, cols):
     return p_mat * z * r
 
 
+def head_forward(qh, kh, vh, scale, causal, dropout_p, seed, b, h, H, panel=_PANEL):
+    """One head of one sequence: qh, kh, vh are [n, d] float64 arrays, (b, h, H)
+    key the dropout hash. Returns (O [n, d], LSE [n])."""
+    n = qh.shape[0]
+    o = np.zeros((n, vh.shape[1]), np.float64)
+    lse = np.zeros(n, np.float64)
+    for r0 in range(0, n, panel):
+        r1 = min(r0 + panel, n)
+        nc = _panel_cols(causal, r1, kh.shape[0])
+        s = attention_scores(qh[r0:r1], kh[:nc], scale, causal, r0)
+        _, _, l_ = softmax_stats(s)
+        p = attention_probs(s, l_)
+        pt = _dropped(p, seed, b, h, H, dropout_p, np.arange(r0, r1), np.arange(nc))
+        o[r0:r1] = pt @ vh[:nc]
+        lse[r0:r1] = l_
+    return o, lse
+
+
+def head_backward(qh, kh, vh, doh, scale, causal, dropout_p, seed, b, h, H, panel=_PANEL,
+                  check_d=True):
+    """One head of one sequence ([n, d] float64 arrays). Returns
+    (dQ, dK, dV, D) with D = rowsum(P * dP) of length n."""
+    n = qh.shape[0]
+    dq = np.zeros_like(qh)
+    dk = np.zeros_like(kh)
+    dv = np.zeros_like(vh)
+    dd = np.zeros(n, np.float64)
+    keep_r = 1.0 / (1.0 - float(np.float32(dropout_p)))
+    for r0 in range(0, n, panel):
+        r1 = min(r0 + panel, n)
+        rows = np.arange(r0, r1)
+        nc = _panel_cols(causal, r1, kh.shape[0])
+        cols = np.arange(nc)
+        s = attention_scores(qh[r0:r1], kh[:nc], scale, causal, r0)
+        _, _, l_ = softmax_stats(s)
+        p = attention_probs(s, l_)
+        if dropout_p != 0.0:
+            z = keep_mask(seed, b, h, H, dropout_p, rows, cols)
+            pt = p * z * keep_r
+        else:
+            z = None
+            pt = p
+        dv[:nc] += pt.T @ doh[r0:r1]
+        dpt = doh[r0:r1] @ vh[:nc].T
+        dp = dpt * z * keep_r if z is not None else dpt
+        d_row = np.sum(p * dp, axis=1)
+        if check_d:
+            o_rows = pt @ vh[:nc]
+            d_alt = np.sum(doh[r0:r1] * o_rows, axis=1)
+            if not np.allclose(d_row, d_alt, rtol=1e-9, atol=1e-9):
+                raise AssertionError("rowsum(P*dP) != rowsum(dO*O)")
+        ds = p * (dp - d_row[:, None])
+        dq[r0:r1] = float(scale) * (ds @ kh[:nc])
+        dk[:nc] += float(scale) * (ds.T @ qh[r0:r1])
+        dd[r0:r1] = d_row
+    return dq, dk, dv, dd
+
+
 def forward(q, k, v, scale, causal, dropout_p=0.0, seed=0, heads=None, panel=_PANEL):
     """Returns (O [B,N,H,d] float64, LSE [B,H,N] float64).
     Only the (b, h) pairs in `heads` are computed (others are left zero)."""
@@ -101,16 +159,9 @@ def forward(q, k, v, scale, causal, dropout_p=0.0, seed=0, heads=None, panel=_PA
     o = np.zeros((B, N, H, v.shape[3]), np.float64)
     lse = np.zeros((B, H, N), np.float64)
     for b, h in _heads(B, H, heads):
-        qh, kh, vh = q[b, :, h, :], k[b, :, h, :], v[b, :, h, :]
-        for r0 in range(0, N, panel):
-            r1 = min(r0 + panel, N)
-            nc = _panel_cols(causal, r1, kh.shape[0])
-            s = attention_scores(qh[r0:r1], kh[:nc], scale, causal, r0)
-            _, _, l_ = softmax_stats(s)
-            p = attention_probs(s, l_)
-            pt = _dropped(p, seed, b, h, H, dropout_p, np.arange(r0, r1), np.arange(nc))
-            o[b, r0:r1, h, :] = pt @ vh[:nc]
-            lse[b, h, r0:r1] = l_
+        o[b, :, h, :], lse[b, h, :] = head_forward(
+            q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], scale, causal, dropout_p, seed, b, h, H,
+            panel)
     return o, lse
 
 
@@ -128,36 +179,10 @@ def backward(q, k, v, do, scale, causal, dropout_p=0.0, seed=0, heads=None, pane
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     dd = np.zeros((B, H, N), np.float64)
-    keep_r = 1.0 / (1.0 - float(np.float32(dropout_p)))
     for b, h in _heads(B, H, heads):
-        qh, kh, vh, doh = q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], do[b, :, h, :]
-        for r0 in range(0, N, panel):
-            r1 = min(r0 + panel, N)
-            rows = np.arange(r0, r1)
-            nc = _panel_cols(causal, r1, kh.shape[0])
-            cols = np.arange(nc)
-            s = attention_scores(qh[r0:r1], kh[:nc], scale, causal, r0)
-            _, _, l_ = softmax_stats(s)
-            p = attention_probs(s, l_)
-            if dropout_p != 0.0:
-                z = keep_mask(seed, b, h, H, dropout_p, rows, cols)
-                pt = p * z * keep_r
-            else:
-                z = None
-                pt = p
-            dv[b, :nc, h, :] += pt.T @ doh[r0:r1]
-            dpt = doh[r0:r1] @ vh[:nc].T
-            dp = dpt * z * keep_r if z is not None else dpt
-            d_row = np.sum(p * dp, axis=1)
-            if check_d:
-                o_rows = pt @ vh[:nc]
-                d_alt = np.sum(doh[r0:r1] * o_rows, axis=1)
-                if not np.allclose(d_row, d_alt, rtol=1e-9, atol=1e-9):
-                    raise AssertionError("rowsum(P*dP) != rowsum(dO*O)")
-            ds = p * (dp - d_row[:, None])
-            dq[b, r0:r1, h, :] = float(scale) * (ds @ kh[:nc])
-            dk[b, :nc, h, :] += float(scale) * (ds.T @ qh[r0:r1])
-            dd[b, h, r0:r1] = d_row
+        dq[b, :, h, :], dk[b, :, h, :], dv[b, :, h, :], dd[b, h, :] = head_backward(
+            q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], do[b, :, h, :], scale, causal,
+            dropout_p, seed, b, h, H, panel, check_d)
     return dq, dk, dv, dd
 
 

@@ -122,3 +122,48 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "lib_path", lambda: str(tmp_path / "absent.so"))
     with pytest.raises(fa.FAError):
         fa.lib()
+
+
+def _fwd_varlen(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, cu=P, S=2, total=100, maxlen=64, H=2, d=128, scale=0.1,
+             causal=1, p=0.0, seed=0, stream=None, dtype=1)
+    a.update(kw)
+    return fa.lib().fa_forward_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["S"],
+                                      a["total"], a["maxlen"], a["H"], a["d"], a["scale"],
+                                      a["causal"], a["p"], a["seed"], a["stream"], a["dtype"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=0), NULL), (dict(cu=P + 2), ALIGN), (dict(q=0), NULL), (dict(lse=0), NULL),
+    (dict(o=P + 8), ALIGN), (dict(S=0), SHAPE), (dict(maxlen=0), SHAPE), (dict(total=-1), SHAPE),
+    (dict(total=1 << 30, H=128), SHAPE), (dict(H=0), SHAPE), (dict(d=96), HEADDIM), (dict(dtype=3), DTYPE),
+    (dict(p=1.0), DROPOUT), (dict(scale=float("nan")), ARG),
+    # an empty batch passes the argument checks and then touches nothing
+    (dict(total=0, q=0, k=0, v=0, o=0, lse=0), OK),
+])
+def test_forward_varlen_rejects(kw, status):
+    assert _fwd_varlen(**kw) == status
+
+
+def test_backward_varlen_rejects():
+    L = fa.lib()
+    args = [P] * 11 + [2, 100, 64, 2, 128, 0.1, 1, 0.0, 0, None, 1]
+
+    def call(**ch):
+        a = list(args)
+        for idx, val in ch.items():
+            a[int(idx[1:])] = val
+        return L.fa_backward_varlen(*a)
+
+    assert call(a10=0) == NULL        # cu_seqlens
+    assert call(a9=0) == NULL         # workspace
+    assert call(a9=P + 4) == ALIGN
+    assert call(a10=P + 1) == ALIGN
+    assert call(a11=0) == SHAPE       # num_seqs
+    assert call(a12=-5) == SHAPE      # total
+    assert call(a15=80 + 16) == HEADDIM
+    assert call(a18=-0.5) == DROPOUT
+    assert call(a21=9) == DTYPE
+    assert call(a12=0, a0=0) == OK
+    assert fa.varlen_workspace_bytes(100, 3, 80) == 4 * 3 * 100
+    assert fa.varlen_workspace_bytes(-1, 3, 80) == 0

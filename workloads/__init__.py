@@ -35,6 +35,11 @@ __all__ = [
     "make_inputs",
     "make_tensor",
     "counted_flops",
+    "VarlenWorkload",
+    "VARLEN_WORKLOADS",
+    "varlen_lengths",
+    "make_varlen_inputs",
+    "counted_flops_varlen",
 ]
 
 
@@ -148,4 +153,75 @@ def counted_flops(B: int, H: int, N: int, d: int, causal: bool, backward: bool) 
     fwd = 4.0 * B * H * N * N * d
     if causal:
         fwd /= 2.0
+    return fwd, (2.5 * fwd if backward else 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Packed batches of sequences of different lengths ("FlashAttention for
+# Efficient Training", section 5.2 "Handling Variable Sequence Lengths").
+#
+# Recipe (fixed): rng = numpy.random.default_rng(seed);
+#   lengths = rng.integers(min_len, max_len + 1, size=num_seqs) unless the
+#   workload lists them explicitly; cu_seqlens = [0, cumsum(lengths)] (int32);
+#   then q, k, v, do drawn as for fixed-length batches with shape
+#   [total, H, d] from the same rng, after the lengths.
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    name: str
+    num_seqs: int
+    H: int
+    d: int
+    dtype: str
+    causal: bool
+    dropout_p: float
+    min_len: int = 1
+    max_len: int = 1
+    lengths: tuple = ()
+    seed: int = 3000
+    amp: float = 1.0
+    dropout_seed: int = 2027
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    def with_(self, **kw) -> "VarlenWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+VARLEN_WORKLOADS = {
+    # Sixteen causal sequences of 512..8192 tokens (mean about 4.3k), the
+    # length spread the pages' padding-versus-packing comparison is about.
+    "varlen16": VarlenWorkload("bf16_varlen16_H16_len512-8192_d128_causal_fwdbwd", 16, 16, 128,
+                               "bf16", True, 0.0, min_len=512, max_len=8192, seed=3006),
+}
+
+
+def varlen_lengths(w: VarlenWorkload) -> np.ndarray:
+    """Sequence lengths of `w` (int64), drawn first from the workload's rng."""
+    if w.lengths:
+        return np.asarray(w.lengths, np.int64)
+    rng = np.random.default_rng(w.seed)
+    return rng.integers(w.min_len, w.max_len + 1, size=w.num_seqs).astype(np.int64)
+
+
+def make_varlen_inputs(w: VarlenWorkload, with_grad: bool = True):
+    """Returns (cu_seqlens int32 [num_seqs + 1], dict name -> (stored, values))
+    with tensors of shape [total, H, d]."""
+    rng = np.random.default_rng(w.seed)
+    if w.lengths:
+        lengths = np.asarray(w.lengths, np.int64)
+    else:
+        lengths = rng.integers(w.min_len, w.max_len + 1, size=w.num_seqs).astype(np.int64)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    shape = (int(cu[-1]), w.H, w.d)
+    out = {}
+    for name in ("q", "k", "v") + (("do",) if with_grad else ()):
+        out[name] = make_tensor(rng, shape, w.amp, w.dtype)
+    return cu, out
+
+
+def counted_flops_varlen(lengths, H: int, d: int, causal: bool, backward: bool) -> tuple:
+    """counted_flops summed over the sequences of a packed batch."""
+    fwd = sum(counted_flops(1, H, int(n), d, causal, False)[0] for n in lengths)
     return fwd, (2.5 * fwd if backward else 0.0)
