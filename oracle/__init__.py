@@ -10,6 +10,8 @@ Contents:
   attention.py     plain fp64 forward / backward that materialise S and P
   dropout_hash.py  the dropout keep-mask counter hash, from the published
                    SplitMix64 and MurmurHash3 finalizers
+  varlen.py        the same attention over packed batches of sequences of
+                   different lengths
 
 Parity status: every function here is pinned by tests under tests/ against
 closed forms, invariants, brute force and finite differences, except the
