@@ -8,7 +8,9 @@ the timed region. Prints one JSON line.
 Workload: B=2, H=16, N=8192, d=128, causal, bf16 (the N=8K headline shape);
 the N=32K, d=80 shape and a packed batch of sixteen causal sequences of
 512..8192 tokens (with the time the same sequences take padded to the
-longest) are reported alongside under "also".
+longest), and a block-sparse N=32K sequence (local window plus global key
+blocks, with the dense time on the same shape) are reported alongside under
+"also".
 FLOP convention: forward 4*B*H*N^2*d, halved for causal; backward 2.5x.
 """
 from __future__ import annotations
@@ -24,8 +26,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import (VARLEN_WORKLOADS, WORKLOADS, counted_flops, counted_flops_varlen,  # noqa: E402
-                       make_inputs, make_varlen_inputs)
+from workloads import (SPARSE_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS, block_mask_local_global,  # noqa: E402
+                       counted_flops, counted_flops_varlen, make_inputs, make_varlen_inputs)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
@@ -159,6 +161,70 @@ def run_gpu_varlen(wv, steps, warmup, torch, fa):
     }
 
 
+def kept_score_elements(mask, N, causal):
+    """Score elements a block mask (and the causal mask) leave in, per head."""
+    blk = 128
+    nb = mask.shape[-1]
+    size = np.minimum(blk, N - blk * np.arange(nb))  # rows (= columns) per block
+    full = np.outer(size, size).astype(np.float64)
+    if causal:
+        # below the diagonal every element counts, above none, on it a triangle
+        tri = size * (size + 1) / 2.0
+        full = np.tril(full, -1) + np.diag(tri)
+    return float(np.sum(full * (mask != 0)))
+
+
+def run_gpu_sparse(name, steps, warmup, torch, fa):
+    """Block-sparse fwd + bwd on a long sequence; FLOPs counted on the kept
+    score elements (4*d per element forward, 2.5x backward). Also times the
+    dense kernels on the same shape."""
+    w, kw = SPARSE_WORKLOADS[name]
+    mask_np = block_mask_local_global(w.N, **kw)
+    dev = _device_inputs(w, torch)
+    m = torch.from_numpy(mask_np).cuda()
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    args = (w.causal, w.dropout_p, w.dropout_seed, w.scale)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        fa.forward_blocksparse(q, k, v, m, *args, out=o, lse=lse)
+        if ev:
+            ev[1].record()
+        fa.backward_blocksparse(q, k, v, o, do, lse, m, *args, dq=dq, dk=dk, dv=dv, workspace=ws)
+        if ev:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_step = evs[0][0].elapsed_time(evs[-1][2]) / steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    elems = kept_score_elements(mask_np, w.N, w.causal) * w.B * w.H
+    fwd_f = 4.0 * w.d * elems
+    bwd_f = 2.5 * fwd_f
+    del dev, q, k, v, do, o, dq, dk, dv
+    torch.cuda.empty_cache()
+    rd = run_gpu(w, max(2, steps // 2), 1, torch, fa)
+    return {
+        "workload": w.name, "mask": f"local window +-{kw['window']} blocks + {kw['n_global']} global key blocks",
+        "density": float(np.mean(mask_np != 0)), "tflops": (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12,
+        "ms_per_step": ms_step, "pct_of_peak": 100.0 * (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
+        / PEAK_BF16_TFLOPS,
+        "fwd_tflops": fwd_f / (fwd_ms * 1e-3) / 1e12, "bwd_tflops": bwd_f / (bwd_ms * 1e-3) / 1e12,
+        "dense_ms_per_step": rd["ms_per_step"],
+    }
+
+
 def kernel_source_digest():
     """SHA-256 over the kernel sources and the build flags: HBM traffic
     figures recorded under profiles/ are valid only for this digest."""
@@ -245,6 +311,7 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--also", type=int, nargs="*", default=[4])
     ap.add_argument("--also-varlen", nargs="*", default=["varlen16"])
+    ap.add_argument("--also-sparse", nargs="*", default=["local_global"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -310,6 +377,9 @@ def main():
         torch.cuda.empty_cache()
     for name in a.also_varlen:
         also.append(run_gpu_varlen(VARLEN_WORKLOADS[name], max(3, a.steps // 4), 2, torch, fa))
+        torch.cuda.empty_cache()
+    for name in a.also_sparse:
+        also.append(run_gpu_sparse(name, max(3, a.steps // 4), 2, torch, fa))
         torch.cuda.empty_cache()
     line["also"] = also
     line["cpu_baseline"] = None if a.no_cpu_baseline else cpu_baseline(w, a.cpu_seconds)

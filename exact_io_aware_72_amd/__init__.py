@@ -20,6 +20,7 @@ __all__ = [
     "FAError", "lib", "lib_path", "version", "forward", "backward", "backward_preprocess",
     "backward_dkdv", "backward_dq", "workspace_bytes", "dropout_mask", "FlashAttnFunction",
     "flash_attention", "forward_varlen", "backward_varlen", "varlen_workspace_bytes",
+    "forward_blocksparse", "backward_blocksparse", "BLOCK",
     "EXPORTED_SYMBOLS", "STATUS",
 ]
 
@@ -33,6 +34,7 @@ EXPORTED_SYMBOLS = (
     "fa_forward", "fa_backward", "fa_backward_workspace_bytes", "fa_backward_preprocess",
     "fa_backward_dkdv", "fa_backward_dq", "fa_dropout_mask", "fa_status_string", "fa_version",
     "fa_forward_varlen", "fa_backward_varlen", "fa_backward_varlen_workspace_bytes",
+    "fa_forward_blocksparse", "fa_backward_blocksparse",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -51,6 +53,7 @@ class FAError(RuntimeError):
 
 
 _vp, _i, _f, _u64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, ctypes.c_size_t
+_i64 = ctypes.c_int64
 _SIGS = {
     "fa_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
     "fa_backward_workspace_bytes": (_sz, [_i, _i, _i, _i]),
@@ -62,6 +65,8 @@ _SIGS = {
     "fa_forward_varlen": (_i, [_vp] * 6 + [_i, _i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
     "fa_backward_varlen_workspace_bytes": (_sz, [_i, _i, _i]),
     "fa_backward_varlen": (_i, [_vp] * 11 + [_i, _i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
+    "fa_forward_blocksparse": (_i, [_vp] * 6 + [_i64, _i64, _i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
+    "fa_backward_blocksparse": (_i, [_vp] * 11 + [_i64, _i64, _i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
     "fa_version": (ctypes.c_char_p, []),
 }
@@ -273,6 +278,66 @@ def backward_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen, causal=False,
                                   int(max_seqlen), H, d, _scale(scale, d), int(bool(causal)),
                                   float(dropout_p), int(seed), _stream(q), _code(q))
     _check(st, "fa_backward_varlen")
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Block-sparse masks over 128 x 128 blocks of the score matrix.
+BLOCK = 128
+
+
+def _mask_args(mask, q, B, H, N):
+    """(pointer, batch stride, head stride) of a uint8 GPU mask shaped
+    (nb, nb), (H, nb, nb) or (B, H, nb, nb), nb = ceil(N / 128); the last two
+    dimensions must be contiguous, the others may be broadcast (stride 0)."""
+    torch = _torch()
+    nb = -(-N // BLOCK)
+    if mask.dtype != torch.uint8 or mask.device != q.device:
+        raise ValueError("block mask must be a uint8 tensor on the tensors' GPU")
+    if tuple(mask.shape[-2:]) != (nb, nb) or mask.stride(-1) != 1 or mask.stride(-2) != nb:
+        raise ValueError(f"block mask must end in a contiguous ({nb}, {nb}) grid")
+    if mask.dim() == 2:
+        return mask.data_ptr(), 0, 0
+    if mask.dim() == 3 and mask.shape[0] == H:
+        return mask.data_ptr(), 0, mask.stride(0)
+    if mask.dim() == 4 and tuple(mask.shape[:2]) == (B, H):
+        return mask.data_ptr(), mask.stride(0), mask.stride(1)
+    raise ValueError("block mask must be (nb, nb), (H, nb, nb) or (B, H, nb, nb)")
+
+
+def forward_blocksparse(q, k, v, block_mask, causal=False, dropout_p=0.0, seed=0, scale=None,
+                        out=None, lse=None):
+    """Returns (o, lse) computing only the blocks where block_mask != 0."""
+    torch = _torch()
+    B, N, H, d = _shape(q, k, v)
+    mp, sb, sh = _mask_args(block_mask, q, B, H, N)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _shape(q, o)
+    st = lib().fa_forward_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      lse_t.data_ptr(), mp, sb, sh, B, H, N, d, _scale(scale, d),
+                                      int(bool(causal)), float(dropout_p), int(seed), _stream(q),
+                                      _code(q))
+    _check(st, "fa_forward_blocksparse")
+    return o, lse_t
+
+
+def backward_blocksparse(q, k, v, o, dout, lse, block_mask, causal=False, dropout_p=0.0, seed=0,
+                         scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """Returns (dq, dk, dv) for L = sum(dout * o) under the same block mask."""
+    torch = _torch()
+    B, N, H, d = _shape(q, k, v, o, dout)
+    mp, sb, sh = _mask_args(block_mask, q, B, H, N)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    ws = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if workspace is None else workspace
+    st = lib().fa_backward_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                       dv.data_ptr(), ws.data_ptr(), mp, sb, sh, B, H, N, d,
+                                       _scale(scale, d), int(bool(causal)), float(dropout_p),
+                                       int(seed), _stream(q), _code(q))
+    _check(st, "fa_backward_blocksparse")
     return dq, dk, dv
 
 

@@ -283,6 +283,74 @@ FA_EXPORT int fa_backward_varlen(const void* q, const void* k, const void* v, co
   return hip_status(bf16 ? fa::launch_bwd_dq_bf16(a, s) : fa::launch_bwd_dq_f32(a, s));
 }
 
+// ---------------------------------------------------------------------------
+// Block-sparse masks.
+namespace {
+int check_block_mask(const uint8_t* m, int64_t sb, int64_t sh, int N) {
+  if (m == nullptr) return FA_ERR_NULL;
+  if (sb < 0 || sh < 0) return FA_ERR_ARG;
+  if (N > fa::kSparseBlock * fa::kSparseMaxBlocks) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+}  // namespace
+
+FA_EXPORT int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, const uint8_t* block_mask, int64_t mask_stride_b,
+                                     int64_t mask_stride_h, int B, int H, int N, int d,
+                                     float scale, int causal, float dropout_p, uint64_t seed,
+                                     void* stream, int dtype) {
+  FA_TRY(check_problem(B, H, N, d, dtype));
+  FA_TRY(check_dropout(dropout_p));
+  FA_TRY(check_scale(scale));
+  FA_TRY(check_block_mask(block_mask, mask_stride_b, mask_stride_h, N));
+  FA_TRY(check_ptrs({q, k, v, o, lse}));
+  fa::AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o_out = o;
+  a.lse_out = lse;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.block_mask = block_mask;
+  a.mask_stride_b = mask_stride_b;
+  a.mask_stride_h = mask_stride_h;
+  a.scale = scale;
+  a.causal = causal != 0;
+  set_dropout(a, dropout_p, seed);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(dtype == FA_BF16 ? fa::launch_forward_bf16(a, s)
+                                     : fa::launch_forward_f32(a, s));
+}
+
+FA_EXPORT int fa_backward_blocksparse(const void* q, const void* k, const void* v, const void* o,
+                                      const void* dout, const float* lse, void* dq, void* dk,
+                                      void* dv, float* workspace, const uint8_t* block_mask,
+                                      int64_t mask_stride_b, int64_t mask_stride_h, int B, int H,
+                                      int N, int d, float scale, int causal, float dropout_p,
+                                      uint64_t seed, void* stream, int dtype) {
+  fa::AttnArgs a;
+  FA_TRY(fill_bwd(a, q, k, v, dout, lse, workspace, B, H, N, d, scale, causal, dropout_p, seed,
+                  dtype));
+  FA_TRY(check_block_mask(block_mask, mask_stride_b, mask_stride_h, N));
+  FA_TRY(check_ptrs({q, k, v, o, dout, lse, dq, dk, dv, workspace}));
+  a.o = o;
+  a.dsum_out = workspace;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.block_mask = block_mask;
+  a.mask_stride_b = mask_stride_b;
+  a.mask_stride_h = mask_stride_h;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == FA_BF16;
+  FA_TRY(hip_status(fa::launch_bwd_preprocess(a, s, bf16)));
+  FA_TRY(hip_status(bf16 ? fa::launch_bwd_dkdv_bf16(a, s) : fa::launch_bwd_dkdv_f32(a, s)));
+  return hip_status(bf16 ? fa::launch_bwd_dq_bf16(a, s) : fa::launch_bwd_dq_f32(a, s));
+}
+
 FA_EXPORT int fa_dropout_mask(uint64_t seed, int b, int h, int H, float dropout_p, int row0,
                               int col0, int rows, int cols, uint8_t* out, void* stream) {
   FA_TRY(check_dropout(dropout_p));

@@ -40,6 +40,8 @@ struct BwdParams {
   int B, H, N;  // N: rows per sequence (the longest one for packed batches)
   const int* cu;  // packed variable-length batch offsets, or nullptr
   int total;
+  const uint8_t* bmask;  // block-sparse mask, or nullptr
+  int64_t msb, msh;
   float scale;
   float c2;  // scale * log2(e)
   uint32_t drop_t;
@@ -63,6 +65,9 @@ BwdParams make_params(const AttnArgs& a) {
   p.N = a.N;
   p.cu = a.cu_seqlens;
   p.total = a.total;
+  p.bmask = a.block_mask;
+  p.msb = a.mask_stride_b;
+  p.msh = a.mask_stride_h;
   p.scale = a.scale;
   p.c2 = a.scale * kLog2e;
   p.drop_t = a.drop_threshold;
@@ -197,7 +202,7 @@ struct DkdvCfg {
   static constexpr int VLPW = (VB::NLOAD + NW - 1) / NW;
 };
 
-template <int D, bool CAUSAL, bool DROP>
+template <int D, bool CAUSAL, bool DROP, bool SPARSE>
 __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams p) {
   using C = DkdvCfg<D>;
   using QT = typename C::QT;
@@ -212,6 +217,8 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
   __shared__ __align__(16) float dd1[C::BQ];
   __shared__ __align__(16) uint32_t ar0[DROP ? C::BQ : 1];
   __shared__ __align__(16) uint32_t ar1[DROP ? C::BQ : 1];
+  __shared__ uint16_t kept[SPARSE ? kSparseMaxBlocks : 1];  // kept query blocks
+  static_assert(!SPARSE || C::BK == kSparseBlock, "a work-group covers one mask column");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -274,7 +281,21 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
   }
 
   const int qstart = CAUSAL ? k0 : 0;
-  const int ntiles = (N - qstart + C::BQ - 1) / C::BQ;
+  int ntiles;
+  if constexpr (SPARSE) {
+    // Kept query blocks of this key block (a mask column), ascending; under
+    // the causal mask only blocks from the diagonal on.
+    const int nb = (N + kSparseBlock - 1) / kSparseBlock;
+    const uint8_t* mcol = p.bmask + b * p.msb + h * p.msh + kblk;
+    const KeptBlocks kb = collect_blocks(mcol, nb, CAUSAL ? kblk : 0, nb, kept, lane, wave == 0);
+    ntiles = kept_tiles<C::BQ>(kb, N);
+    __syncthreads();
+  } else {
+    ntiles = (N - qstart + C::BQ - 1) / C::BQ;
+  }
+  auto tile_start = [&](int t) {
+    return SPARSE ? kept_tile_start<C::BQ>(kept, t) : qstart + t * C::BQ;
+  };
 
   // This wave's share of the tile loads: Q instructions, then dO.
   uint32_t dsrc[C::LPW];
@@ -339,11 +360,12 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
                   char* nxt, float* lsn, float* ddn, uint32_t* arn, int t) {
     wait_vmem();
     __syncthreads();
-    const int qt0 = qstart + t * C::BQ;
+    const int qt0 = tile_start(t);
     const bool more = t + 1 < ntiles;
     if (more) {
-      stat_load(qt0 + C::BQ);
-      issue(nxt, qt0 + C::BQ);
+      const int qn = tile_start(t + 1);
+      stat_load(qn);
+      issue(nxt, qn);
     }
     if (!CAUSAL || qt0 + C::BQ - 1 >= kw0) {
       // S = Q K^T and dP = dO V^T : lane = key, register r -> query qt0 + c_row(r, hf)
@@ -406,9 +428,11 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
     if (more) stat_store(lsn, ddn, arn);
   };
 
-  stat_load(qstart);
-  issue(st0, qstart);
-  stat_store(ls0, dd0, ar0);
+  if (ntiles > 0) {
+    stat_load(tile_start(0));
+    issue(st0, tile_start(0));
+    stat_store(ls0, dd0, ar0);
+  }
   for (int t = 0; t < ntiles; t += 2) {
     step(st0, ls0, dd0, ar0, st1, ls1, dd1, ar1, t);
     if (t + 1 < ntiles) step(st1, ls1, dd1, ar1, st0, ls0, dd0, ar0, t + 1);
@@ -458,7 +482,7 @@ struct DqCfg {
   static constexpr int LPW = (NLOAD + 3) / 4;
 };
 
-template <int D, bool CAUSAL, bool DROP>
+template <int D, bool CAUSAL, bool DROP, bool SPARSE>
 __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
   using C = DqCfg<D>;
   using KT = typename C::KT;
@@ -467,6 +491,8 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
   __shared__ __align__(16) char st1[C::STAGE];
   __shared__ __align__(16) uint32_t bc0[DROP ? C::BK : 1];
   __shared__ __align__(16) uint32_t bc1[DROP ? C::BK : 1];
+  __shared__ uint16_t kept[SPARSE ? kSparseMaxBlocks : 1];  // kept key blocks
+  static_assert(!SPARSE || C::BQ == kSparseBlock, "a work-group covers one mask row");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -514,7 +540,18 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
   }
 
   const int kend = CAUSAL ? min(N, q0 + C::BQ) : N;
-  const int ntiles = (kend + C::BK - 1) / C::BK;
+  int ntiles;
+  if constexpr (SPARSE) {
+    const int nb = (N + kSparseBlock - 1) / kSparseBlock;
+    const uint8_t* mrow = p.bmask + b * p.msb + h * p.msh + (int64_t)qb * nb;
+    const KeptBlocks kb =
+        collect_blocks(mrow, 1, 0, (kend + kSparseBlock - 1) / kSparseBlock, kept, lane, wave == 0);
+    ntiles = kept_tiles<C::BK>(kb, kend);
+    __syncthreads();
+  } else {
+    ntiles = (kend + C::BK - 1) / C::BK;
+  }
+  auto tile_start = [&](int t) { return SPARSE ? kept_tile_start<C::BK>(kept, t) : t * C::BK; };
 
   // This wave's share of the tile loads: K instructions, then V.
   uint32_t dsrc[C::LPW];
@@ -561,8 +598,8 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
   auto step = [&](const char* cur, const uint32_t* bcc, char* nxt, uint32_t* bcn, int t) {
     wait_vmem();
     __syncthreads();
-    const int k0 = t * C::BK;
-    if (t + 1 < ntiles) issue(nxt, bcn, k0 + C::BK);
+    const int k0 = tile_start(t);
+    if (t + 1 < ntiles) issue(nxt, bcn, tile_start(t + 1));
     if (CAUSAL && k0 > qw0 + 31) return;
     // S^T = K Q^T and dP^T = V dO^T : lane = query, register r -> key k0 + c_row(r, hf)
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -605,7 +642,7 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
     sched_lds_ahead<2 * C::NDB, 2, 1, DROP ? 4 : 0>();
   };
 
-  issue(st0, bc0, 0);
+  if (ntiles > 0) issue(st0, bc0, tile_start(0));
   for (int t = 0; t < ntiles; t += 2) {
     step(st0, bc0, st1, bc1, t);
     if (t + 1 < ntiles) step(st1, bc1, st0, bc0, t + 1);
@@ -675,7 +712,11 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdParams p) {
     bcol = col_key(kbh, mykey);
   }
   const int qstart = CAUSAL ? k0 : 0;
+  const int nb = (N + kSparseBlock - 1) / kSparseBlock;
+  const uint8_t* mcol =  // this key block's column of the block mask
+      p.bmask ? p.bmask + b * p.msb + h * p.msh + k0 / kSparseBlock : nullptr;
   for (int qt0 = qstart; qt0 < N; qt0 += BQ) {
+    if (mcol != nullptr && mcol[(int64_t)(qt0 / kSparseBlock) * nb] == 0) continue;  // uniform
     __syncthreads();
     for (int i = tid; i < BQ * D / 4; i += 128) {
       const int r = i / (D / 4), c = (i - r * (D / 4)) * 4;
@@ -779,7 +820,12 @@ __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdParams p) {
     arow = row_key(kbh, myq);
   }
   const int kend = CAUSAL ? min(N, q0 + BQW) : N;
+  const uint8_t* mrow =  // this query block's row of the block mask
+      p.bmask ? p.bmask + b * p.msb + h * p.msh +
+                    (int64_t)(q0 / kSparseBlock) * ((N + kSparseBlock - 1) / kSparseBlock)
+              : nullptr;
   for (int k0 = 0; k0 < kend; k0 += BK) {
+    if (mrow != nullptr && mrow[k0 / kSparseBlock] == 0) continue;  // uniform over the block
     __syncthreads();
     for (int i = tid; i < BK * D / 4; i += 128) {
       const int r = i / (D / 4), c = (i - r * (D / 4)) * 4;
@@ -863,6 +909,55 @@ __global__ __launch_bounds__(256) void dropout_mask_kernel(uint64_t seed, int b,
     }                                                                              \
   } while (0)
 
+// bf16 matrix-core kernels: (d, causal, dropout, block-sparse) instances.
+template <int D, bool SPARSE>
+hipError_t launch_dkdv_ds(const BwdParams& prm, bool causal, bool drop, dim3 grid, dim3 block,
+                          hipStream_t s) {
+  if (causal) {
+    if (drop)
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, true, true, SPARSE>), grid, block, 0, s, prm);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, true, false, SPARSE>), grid, block, 0, s, prm);
+  } else {
+    if (drop)
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, false, true, SPARSE>), grid, block, 0, s, prm);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, false, false, SPARSE>), grid, block, 0, s, prm);
+  }
+  return hipGetLastError();
+}
+
+template <int D, bool SPARSE>
+hipError_t launch_dq_ds(const BwdParams& prm, bool causal, bool drop, dim3 grid, dim3 block,
+                        hipStream_t s) {
+  if (causal) {
+    if (drop)
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, true, true, SPARSE>), grid, block, 0, s, prm);
+    else
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, true, false, SPARSE>), grid, block, 0, s, prm);
+  } else {
+    if (drop)
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, false, true, SPARSE>), grid, block, 0, s, prm);
+    else
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, false, false, SPARSE>), grid, block, 0, s, prm);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dkdv_d(const BwdParams& prm, bool causal, bool drop, dim3 grid, dim3 block,
+                         hipStream_t s) {
+  return prm.bmask ? launch_dkdv_ds<D, true>(prm, causal, drop, grid, block, s)
+                   : launch_dkdv_ds<D, false>(prm, causal, drop, grid, block, s);
+}
+
+template <int D>
+hipError_t launch_dq_d(const BwdParams& prm, bool causal, bool drop, dim3 grid, dim3 block,
+                       hipStream_t s) {
+  return prm.bmask ? launch_dq_ds<D, true>(prm, causal, drop, grid, block, s)
+                   : launch_dq_ds<D, false>(prm, causal, drop, grid, block, s);
+}
+
 }  // namespace
 
 hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t s, bool bf16) {
@@ -893,15 +988,23 @@ hipError_t launch_bwd_dkdv_bf16(const AttnArgs& a, hipStream_t s) {
   const BwdParams prm = make_params(a);
   constexpr int BK = DkdvCfg<64>::BK, NT = DkdvCfg<64>::NT;
   const dim3 grid((unsigned)(((a.N + BK - 1) / BK) * a.B * a.H)), block(NT);
-  FA_DISPATCH(bwd_dkdv_bf16_kernel, a.d, a.causal, a.dropout, grid, block, s, prm);
-  return hipGetLastError();
+  switch (a.d) {
+    case 64: return launch_dkdv_d<64>(prm, a.causal, a.dropout, grid, block, s);
+    case 80: return launch_dkdv_d<80>(prm, a.causal, a.dropout, grid, block, s);
+    case 128: return launch_dkdv_d<128>(prm, a.causal, a.dropout, grid, block, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_bwd_dq_bf16(const AttnArgs& a, hipStream_t s) {
   const BwdParams prm = make_params(a);
   const dim3 grid((unsigned)(((a.N + 127) / 128) * a.B * a.H)), block(256);
-  FA_DISPATCH(bwd_dq_bf16_kernel, a.d, a.causal, a.dropout, grid, block, s, prm);
-  return hipGetLastError();
+  switch (a.d) {
+    case 64: return launch_dq_d<64>(prm, a.causal, a.dropout, grid, block, s);
+    case 80: return launch_dq_d<80>(prm, a.causal, a.dropout, grid, block, s);
+    case 128: return launch_dq_d<128>(prm, a.causal, a.dropout, grid, block, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_bwd_dkdv_f32(const AttnArgs& a, hipStream_t s) {

@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_kernels.h"
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -202,6 +204,50 @@ __device__ __forceinline__ SeqRows seq_rows(const int* cu, int total, int s, int
     r.stat = (int64_t)h * total + a;
   }
   return r;
+}
+
+// Block-sparse masks (layout in fa_kernels.h): the kernels visit only kept
+// blocks, so their tiles (64 or 32 rows) never straddle a block edge. One
+// wave collects a work-group's kept blocks into an LDS list.
+struct KeptBlocks {
+  int count;  // kept blocks
+  int last;   // index of the last kept block, -1 if none
+};
+// Scans m[j * stride] for j in [first, n) with one wave and returns the kept
+// count and last index (uniform over the wave). With `write`, also stores the
+// kept indices in ascending order to list[0 .. count-1] (LDS).
+__device__ __forceinline__ KeptBlocks collect_blocks(const uint8_t* m, int64_t stride, int first,
+                                                     int n, uint16_t* list, int lane, bool write) {
+  KeptBlocks r{0, -1};
+  for (int j0 = first; j0 < n; j0 += 64) {
+    const int j = j0 + lane;
+    const bool kept = j < n && m[(int64_t)j * stride] != 0;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(kept);
+    if (write && kept) {
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      list[r.count + below] = (uint16_t)j;
+    }
+    if (bal != 0) r.last = j0 + 63 - __builtin_clzll(bal);
+    r.count += __builtin_popcountll(bal);
+  }
+  return r;
+}
+// Tiles of TILE rows over the kept blocks: T = 128 / TILE per block, except
+// that tiles of the last kept block starting at or past `limit` are dropped.
+template <int TILE>
+__device__ __forceinline__ int kept_tiles(KeptBlocks kb, int limit) {
+  constexpr int T = kSparseBlock / TILE;
+  if (kb.count == 0) return 0;
+  const int in_last = min(T, (limit - kb.last * kSparseBlock + TILE - 1) / TILE);
+  return (kb.count - 1) * T + in_last;
+}
+// First row of tile t of the kept-block list (uniform).
+template <int TILE>
+__device__ __forceinline__ int kept_tile_start(const uint16_t* list, int t) {
+  constexpr int T = kSparseBlock / TILE;
+  const int blk = __builtin_amdgcn_readfirstlane((int)list[t / T]);
+  return blk * kSparseBlock + (t % T) * TILE;
 }
 
 // Maps a linear work-group id to (block, batch*heads index). All blocks of a

@@ -41,6 +41,8 @@ struct FwdParams {
   int B, H, N;  // N: rows per sequence (the longest one for packed batches)
   const int* cu;  // packed variable-length batch offsets, or nullptr
   int total;
+  const uint8_t* bmask;  // block-sparse mask, or nullptr
+  int64_t msb, msh;
   float c2;  // scale * log2(e)
   uint32_t drop_t;
   float drop_r;
@@ -62,7 +64,7 @@ struct FwdCfg {
   static constexpr int LPW = (NLOAD + 3) / 4;          // per wave
 };
 
-template <int D, bool CAUSAL, bool DROP>
+template <int D, bool CAUSAL, bool DROP, bool SPARSE>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   using C = FwdCfg<D>;
   using KT = typename C::KT;
@@ -73,6 +75,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   __shared__ __align__(16) char st1[C::STAGE];
   __shared__ __align__(16) uint32_t ck0[DROP ? C::BN : 1];
   __shared__ __align__(16) uint32_t ck1[DROP ? C::BN : 1];
+  __shared__ uint16_t kept[SPARSE ? kSparseMaxBlocks : 1];  // kept key blocks
+  static_assert(!SPARSE || C::BM == kSparseBlock, "a work-group covers one mask row");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -111,7 +115,19 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   }
 
   const int kend = CAUSAL ? min(N, q0 + C::BM) : N;
-  const int ntiles = (kend + C::BN - 1) / C::BN;
+  int ntiles;
+  if constexpr (SPARSE) {
+    // Kept key blocks of this query block, in ascending order.
+    const int nb = (N + kSparseBlock - 1) / kSparseBlock;
+    const uint8_t* mrow = p.bmask + b * p.msb + h * p.msh + (int64_t)qb * nb;
+    const KeptBlocks kb =
+        collect_blocks(mrow, 1, 0, (kend + kSparseBlock - 1) / kSparseBlock, kept, lane, wave == 0);
+    ntiles = kept_tiles<C::BN>(kb, kend);
+    __syncthreads();
+  } else {
+    ntiles = (kend + C::BN - 1) / C::BN;
+  }
+  auto tile_start = [&](int t) { return SPARSE ? kept_tile_start<C::BN>(kept, t) : t * C::BN; };
 
   // This wave's share of the tile loads: K instructions first, then V.
   uint32_t dsrc[C::LPW];
@@ -181,8 +197,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
     // barrier nobody reads `nxt` any more, so the next tile can go there.
     wait_vmem();
     __syncthreads();
-    const int k0 = t * C::BN;
-    if (t + 1 < ntiles) issue(nxt, ckn, k0 + C::BN);
+    const int k0 = tile_start(t);
+    if (t + 1 < ntiles) issue(nxt, ckn, tile_start(t + 1));
     if (CAUSAL && k0 > qw0 + 31) return;  // every key of the tile is after this wave's queries
 
     // S^T = K Q^T: lane = query, registers = keys (c_row layout).
@@ -291,7 +307,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
     }
   };
 
-  issue(st0, ck0, 0);
+  if (ntiles > 0) issue(st0, ck0, tile_start(0));
   for (int t = 0; t < ntiles; t += 2) {
     step(st0, ck0, st1, ck1, t);
     if (t + 1 < ntiles) step(st1, ck1, st0, ck0, t + 1);
@@ -299,7 +315,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
 
   const float ltot = xor32_sum(l);
   if (myq < N) {
-    const float inv = (DROP ? p.drop_r : 1.f) / ltot;
+    // A row whose blocks are all masked has no keys: O = 0, LSE = -inf.
+    const float inv = (SPARSE && ltot == 0.f) ? 0.f : (DROP ? p.drop_r : 1.f) / ltot;
     uint16_t* orow = p.o + base + (int64_t)myq * rs;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
@@ -330,6 +347,8 @@ struct FwdParamsF {
   int B, H, N;
   const int* cu;
   int total;
+  const uint8_t* bmask;
+  int64_t msb, msh;
   float c2;
   uint32_t drop_t;
   float drop_r;
@@ -375,8 +394,13 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
     arow = row_key(kbh, myq);
   }
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  const uint8_t* mrow = nullptr;  // this query block's row of the block mask
+  if (p.bmask != nullptr)
+    mrow = p.bmask + b * p.msb + h * p.msh +
+           (int64_t)(q0 / kSparseBlock) * ((N + kSparseBlock - 1) / kSparseBlock);
   float m = -INFINITY, l = 0.f;
   for (int k0 = 0; k0 < kend; k0 += BN) {
+    if (mrow != nullptr && mrow[k0 / kSparseBlock] == 0) continue;  // uniform over the block
     __syncthreads();
     for (int i = tid; i < BN * D / 4; i += 128) {
       const int r = i / (D / 4), c = (i - r * (D / 4)) * 4;
@@ -431,7 +455,8 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
     }
   }
   if (myq < N) {
-    const float inv = (DROP ? p.drop_r : 1.f) / l;
+    // A row whose blocks are all masked has no keys: O = 0, LSE = -inf.
+    const float inv = l == 0.f ? 0.f : (DROP ? p.drop_r : 1.f) / l;
     float* orow = p.o + base + (int64_t)myq * rs + part * DH;
 #pragma unroll
     for (int c = 0; c < DH; ++c) orow[c] = ov[c] * inv;
@@ -439,20 +464,28 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
   }
 }
 
-template <int D, bool CAUSAL, bool DROP>
+template <int D, bool CAUSAL, bool DROP, bool SPARSE>
 hipError_t launch_fwd_bf16_t(const FwdParams& prm, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROP>), dim3(nblocks), dim3(256), 0, s, prm);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROP, SPARSE>), dim3(nblocks), dim3(256), 0, s,
+                     prm);
   return hipGetLastError();
+}
+
+template <int D, bool SPARSE>
+hipError_t launch_fwd_bf16_ds(const FwdParams& prm, bool causal, bool drop, int nblocks,
+                              hipStream_t s) {
+  if (causal)
+    return drop ? launch_fwd_bf16_t<D, true, true, SPARSE>(prm, nblocks, s)
+                : launch_fwd_bf16_t<D, true, false, SPARSE>(prm, nblocks, s);
+  return drop ? launch_fwd_bf16_t<D, false, true, SPARSE>(prm, nblocks, s)
+              : launch_fwd_bf16_t<D, false, false, SPARSE>(prm, nblocks, s);
 }
 
 template <int D>
 hipError_t launch_fwd_bf16_d(const FwdParams& prm, bool causal, bool drop, int nblocks,
                              hipStream_t s) {
-  if (causal)
-    return drop ? launch_fwd_bf16_t<D, true, true>(prm, nblocks, s)
-                : launch_fwd_bf16_t<D, true, false>(prm, nblocks, s);
-  return drop ? launch_fwd_bf16_t<D, false, true>(prm, nblocks, s)
-              : launch_fwd_bf16_t<D, false, false>(prm, nblocks, s);
+  return prm.bmask ? launch_fwd_bf16_ds<D, true>(prm, causal, drop, nblocks, s)
+                   : launch_fwd_bf16_ds<D, false>(prm, causal, drop, nblocks, s);
 }
 
 template <int D, bool CAUSAL, bool DROP>
@@ -485,6 +518,9 @@ hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s) {
   prm.N = a.N;
   prm.cu = a.cu_seqlens;
   prm.total = a.total;
+  prm.bmask = a.block_mask;
+  prm.msb = a.mask_stride_b;
+  prm.msh = a.mask_stride_h;
   prm.c2 = a.scale * kLog2e;
   prm.drop_t = a.drop_threshold;
   prm.drop_r = a.drop_rescale;
@@ -511,6 +547,9 @@ hipError_t launch_forward_f32(const AttnArgs& a, hipStream_t s) {
   prm.N = a.N;
   prm.cu = a.cu_seqlens;
   prm.total = a.total;
+  prm.bmask = a.block_mask;
+  prm.msb = a.mask_stride_b;
+  prm.msh = a.mask_stride_h;
   prm.c2 = a.scale * kLog2e;
   prm.drop_t = a.drop_threshold;
   prm.drop_r = a.drop_rescale;

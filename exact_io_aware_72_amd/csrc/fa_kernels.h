@@ -7,6 +7,12 @@
 
 namespace fa {
 
+// Block-sparse masks: one byte per (128-query block, 128-key block) of a
+// (b, h) pair, row-major over an nb x nb grid (nb = ceil(N / 128)); nonzero
+// means the block is computed, zero that its scores are -inf.
+constexpr int kSparseBlock = 128;
+constexpr int kSparseMaxBlocks = 1024;  // so N <= 131072 with a block mask
+
 struct AttnArgs {
   // inputs
   const void* q = nullptr;
@@ -30,6 +36,11 @@ struct AttnArgs {
   int B = 0, H = 0, N = 0, d = 0;
   const int* cu_seqlens = nullptr;
   int total = 0;
+  // Block-sparse mask (fixed-length batches only): for (b, h), the nb x nb
+  // bytes at block_mask + b * mask_stride_b + h * mask_stride_h, nb =
+  // ceil(N / 128); nonzero = the 128 x 128 block is computed. nullptr: dense.
+  const uint8_t* block_mask = nullptr;
+  int64_t mask_stride_b = 0, mask_stride_h = 0;
   float scale = 0.f;
   bool causal = false;
   bool dropout = false;

@@ -163,6 +163,36 @@ int fa_backward_varlen(const void* q, const void* k, const void* v, const void* 
                        uint64_t seed, void* stream, int dtype);
 
 /*
+ * Block-sparse attention ("FlashAttention for Efficient Training", section 3.2,
+ * "Block-Sparse Attention Support": only the nonzero blocks of the attention
+ * matrix are computed). Fixed-length [B][N][H][d] tensors as for fa_forward /
+ * fa_backward, plus a mask over 128 x 128 blocks of the score matrix:
+ *   block_mask  DEVICE bytes; for head (b, h) the nb x nb row-major grid at
+ *               block_mask + b * mask_stride_b + h * mask_stride_h, with
+ *               nb = ceil(N / 128); entry [i][j] nonzero: the scores of query
+ *               block i against key block j are computed; zero: they are -inf
+ *               (no work is done for them). Strides are in bytes, >= 0 (0
+ *               shares one grid across batch items or heads); no alignment.
+ *   N <= 131072.
+ * With causal != 0 the causal mask applies as well. A query row whose
+ * visible keys are all masked gets O = 0 and LSE = -inf, and zero gradients.
+ * The backward takes the same mask as the forward that produced o and lse;
+ * its workspace is fa_backward_workspace_bytes(B, H, N, d). Other arguments
+ * and errors as for fa_forward / fa_backward; additionally FA_ERR_NULL for a
+ * null mask, FA_ERR_ARG for a negative stride, FA_ERR_SHAPE for N > 131072.
+ */
+int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const uint8_t* block_mask, int64_t mask_stride_b,
+                           int64_t mask_stride_h, int B, int H, int N, int d, float scale,
+                           int causal, float dropout_p, uint64_t seed, void* stream, int dtype);
+
+int fa_backward_blocksparse(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            float* workspace, const uint8_t* block_mask, int64_t mask_stride_b,
+                            int64_t mask_stride_h, int B, int H, int N, int d, float scale,
+                            int causal, float dropout_p, uint64_t seed, void* stream, int dtype);
+
+/*
  * Writes the dropout keep mask of head (b, h) for rows row0..row0+rows-1 and
  * columns col0..col0+cols-1 to out[rows][cols] (device, 1 = keep), with the
  * same device function the kernels use. The pages fuse dropout into the

@@ -16,6 +16,10 @@ Definitions followed ("FlashAttention for Efficient Training" unless noted):
     contribute nothing (the -inf masking of section 5.2 "Handling Variable
     Sequence Lengths"; causal use in section 5.1 "Memory-Efficient Backward
     Pass"). Queries and keys share positions 0..N-1 (top-left aligned).
+  * block-sparse: with a mask over 128 x 128 blocks of S, scores in zero
+    blocks are -inf ("Only non-zero blocks ... are computed", section 3.2
+    "Block-Sparse Attention Support"); a row left with no finite score gets
+    P = 0, O = 0 and LSE = -inf
   * numerically stable softmax: subtract the row max before exp (section 6.2
     "Hardware-Specific Optimizations")
   * per-row logsumexp LSE_i = log sum_j exp(S_ij), natural log (section 3.2,
@@ -52,6 +56,20 @@ def attention_scores(q, k, scale, causal, row0=0):
         kj = np.arange(s.shape[1])[None, :]
         s = np.where(kj > qi, -np.inf, s)
     return s
+
+
+BLOCK = 128  # side of a block-sparse mask block
+
+
+def apply_block_mask(s, bmask, rows, cols):
+    """Block-sparse attention ("FlashAttention for Efficient Training",
+    section 3.2 "Block-Sparse Attention Support"): scores of query i and key j
+    whose block bmask[i // 128][j // 128] is zero are -inf, i.e. not part of
+    the softmax. `rows`, `cols` are the positions of s's rows and columns."""
+    if bmask is None:
+        return s
+    keep = np.asarray(bmask, bool)[np.asarray(rows) // BLOCK][:, np.asarray(cols) // BLOCK]
+    return np.where(keep, s, -np.inf)
 
 
 def softmax_stats(s):
@@ -91,9 +109,10 @@ def _dropped(p_mat, seed, b, h, H, dropout_p, rows, cols):
     return p_mat * z * r
 
 
-def head_forward(qh, kh, vh, scale, causal, dropout_p, seed, b, h, H, panel=_PANEL):
+def head_forward(qh, kh, vh, scale, causal, dropout_p, seed, b, h, H, panel=_PANEL, bmask=None):
     """One head of one sequence: qh, kh, vh are [n, d] float64 arrays, (b, h, H)
-    key the dropout hash. Returns (O [n, d], LSE [n])."""
+    key the dropout hash, bmask is this head's block mask or None. Returns
+    (O [n, d], LSE [n]); rows with no unmasked key get O = 0, LSE = -inf."""
     n = qh.shape[0]
     o = np.zeros((n, vh.shape[1]), np.float64)
     lse = np.zeros(n, np.float64)
@@ -101,6 +120,7 @@ def head_forward(qh, kh, vh, scale, causal, dropout_p, seed, b, h, H, panel=_PAN
         r1 = min(r0 + panel, n)
         nc = _panel_cols(causal, r1, kh.shape[0])
         s = attention_scores(qh[r0:r1], kh[:nc], scale, causal, r0)
+        s = apply_block_mask(s, bmask, np.arange(r0, r1), np.arange(nc))
         _, _, l_ = softmax_stats(s)
         p = attention_probs(s, l_)
         pt = _dropped(p, seed, b, h, H, dropout_p, np.arange(r0, r1), np.arange(nc))
@@ -110,7 +130,7 @@ def head_forward(qh, kh, vh, scale, causal, dropout_p, seed, b, h, H, panel=_PAN
 
 
 def head_backward(qh, kh, vh, doh, scale, causal, dropout_p, seed, b, h, H, panel=_PANEL,
-                  check_d=True):
+                  check_d=True, bmask=None):
     """One head of one sequence ([n, d] float64 arrays). Returns
     (dQ, dK, dV, D) with D = rowsum(P * dP) of length n."""
     n = qh.shape[0]
@@ -125,6 +145,7 @@ def head_backward(qh, kh, vh, doh, scale, causal, dropout_p, seed, b, h, H, pane
         nc = _panel_cols(causal, r1, kh.shape[0])
         cols = np.arange(nc)
         s = attention_scores(qh[r0:r1], kh[:nc], scale, causal, r0)
+        s = apply_block_mask(s, bmask, rows, cols)
         _, _, l_ = softmax_stats(s)
         p = attention_probs(s, l_)
         if dropout_p != 0.0:
@@ -149,9 +170,11 @@ def head_backward(qh, kh, vh, doh, scale, causal, dropout_p, seed, b, h, H, pane
     return dq, dk, dv, dd
 
 
-def forward(q, k, v, scale, causal, dropout_p=0.0, seed=0, heads=None, panel=_PANEL):
+def forward(q, k, v, scale, causal, dropout_p=0.0, seed=0, heads=None, panel=_PANEL,
+            block_mask=None):
     """Returns (O [B,N,H,d] float64, LSE [B,H,N] float64).
-    Only the (b, h) pairs in `heads` are computed (others are left zero)."""
+    Only the (b, h) pairs in `heads` are computed (others are left zero).
+    block_mask: None, or [B,H,nb,nb] (nb = ceil(N/128)), nonzero = computed."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -161,12 +184,12 @@ def forward(q, k, v, scale, causal, dropout_p=0.0, seed=0, heads=None, panel=_PA
     for b, h in _heads(B, H, heads):
         o[b, :, h, :], lse[b, h, :] = head_forward(
             q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], scale, causal, dropout_p, seed, b, h, H,
-            panel)
+            panel, None if block_mask is None else block_mask[b][h])
     return o, lse
 
 
 def backward(q, k, v, do, scale, causal, dropout_p=0.0, seed=0, heads=None, panel=_PANEL,
-             check_d=True):
+             check_d=True, block_mask=None):
     """Returns (dQ, dK, dV, D) for L = sum(dO * O), float64.
     D is [B,H,N] = rowsum(P * dP). With check_d, also checks D against
     rowsum(dO * O) computed from this module's own forward output."""
@@ -182,18 +205,21 @@ def backward(q, k, v, do, scale, causal, dropout_p=0.0, seed=0, heads=None, pane
     for b, h in _heads(B, H, heads):
         dq[b, :, h, :], dk[b, :, h, :], dv[b, :, h, :], dd[b, h, :] = head_backward(
             q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], do[b, :, h, :], scale, causal,
-            dropout_p, seed, b, h, H, panel, check_d)
+            dropout_p, seed, b, h, H, panel, check_d,
+            None if block_mask is None else block_mask[b][h])
     return dq, dk, dv, dd
 
 
-def sampled_head(q, k, v, do, scale, causal, dropout_p, seed, b, h, rows, cols, panel=_PANEL):
+def sampled_head(q, k, v, do, scale, causal, dropout_p, seed, b, h, rows, cols, panel=_PANEL,
+                 bmask=None):
     """Oracle values for one head (b, h) at selected query rows and key columns.
 
     Computes LSE and O for every row of the head (needed by any key column),
     then O, LSE and dQ at `rows`, and dK and dV at `cols`, from the same
     definitions as forward()/backward(). Returns a dict of float64 arrays:
       o[rows, d], lse[rows], dq[rows, d], dk[cols, d], dv[cols, d], D[rows].
-    q, k, v, do are [B, N, H, d] arrays (any float dtype).
+    q, k, v, do are [B, N, H, d] arrays (any float dtype); bmask is this
+    head's block mask or None.
     """
     H = q.shape[2]
     qh = np.asarray(q[b, :, h, :], np.float64)
@@ -212,6 +238,7 @@ def sampled_head(q, k, v, do, scale, causal, dropout_p, seed, b, h, rows, cols, 
         r1 = min(r0 + panel, N)
         nc = _panel_cols(causal, r1, N)
         s = attention_scores(qh[r0:r1], kh[:nc], scale, causal, r0)
+        s = apply_block_mask(s, bmask, np.arange(r0, r1), np.arange(nc))
         _, _, l_ = softmax_stats(s)
         p = attention_probs(s, l_)
         pt = _dropped(p, seed, b, h, H, dropout_p, np.arange(r0, r1), np.arange(nc))
@@ -226,6 +253,7 @@ def sampled_head(q, k, v, do, scale, causal, dropout_p, seed, b, h, rows, cols, 
     s = attention_scores(qh[rows], kh, scale, False)
     if causal:
         s = np.where(np.arange(N)[None, :] > rows[:, None], -np.inf, s)
+    s = apply_block_mask(s, bmask, rows, np.arange(N))
     p = attention_probs(s, lse_all[rows])
     dpt = doh[rows] @ vh.T
     if dropout_p != 0.0:
@@ -242,6 +270,7 @@ def sampled_head(q, k, v, do, scale, causal, dropout_p, seed, b, h, rows, cols, 
     st = attention_scores(kh[cols], qh, scale, False).T  # [N, len(cols)] = scale q k^T
     if causal:
         st = np.where(cols[None, :] > np.arange(N)[:, None], -np.inf, st)
+    st = apply_block_mask(st, bmask, np.arange(N), cols)
     pc = attention_probs(st, lse_all)
     dpct = doh @ vh[cols].T
     if dropout_p != 0.0:

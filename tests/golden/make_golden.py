@@ -7,8 +7,11 @@ logsumexp and D terms). The inputs are regenerated from the seeded recipe of
 the `workloads` module; a SHA-256 of each stored input tensor is saved so a
 test can tell that it regenerated the same bytes.
 
+The block-sparse workload ("local_global") is written the same way, with
+its block mask, to sampled_sparse_local_global.npz.
+
 Only `oracle` and `workloads` are used. Run from the repository root:
-    python tests/golden/make_golden.py [config ...]
+    python tests/golden/make_golden.py [config ... | local_global]
 """
 import hashlib
 import os
@@ -21,7 +24,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__)
 sys.path.insert(0, ROOT)
 
 import oracle  # noqa: E402
-from workloads import WORKLOADS, make_inputs  # noqa: E402
+from workloads import SPARSE_WORKLOADS, WORKLOADS, block_mask_local_global, make_inputs  # noqa: E402
 
 OUT = os.path.dirname(os.path.abspath(__file__))
 
@@ -41,6 +44,9 @@ def heads_for(w):
 
 def main(cfgs):
     for cfg in cfgs:
+        if cfg in SPARSE_WORKLOADS:
+            sparse(cfg)
+            continue
         w = WORKLOADS[cfg]
         t0 = time.time()
         inp = make_inputs(w)
@@ -61,5 +67,27 @@ def main(cfgs):
         print(f"config {cfg}: wrote {path} in {time.time() - t0:.1f} s", flush=True)
 
 
+def sparse(name):
+    w, kw = SPARSE_WORKLOADS[name]
+    t0 = time.time()
+    inp = make_inputs(w)
+    mask = block_mask_local_global(w.N, **kw)
+    vals = {k: v[1] for k, v in inp.items()}
+    rows = sample_indices(w.N, 300)
+    cols = sample_indices(w.N, 400)
+    heads = [(0, 0), (0, w.H - 1)]
+    out = {"rows": rows, "cols": cols, "heads": np.array(heads, np.int64), "mask": mask}
+    for k, v in inp.items():
+        out[f"sha256_{k}"] = np.array(hashlib.sha256(np.ascontiguousarray(v[0]).tobytes()).hexdigest())
+    for hi, (b, h) in enumerate(heads):
+        s = oracle.sampled_head(vals["q"], vals["k"], vals["v"], vals["do"], w.scale, w.causal,
+                                w.dropout_p, w.dropout_seed, b, h, rows, cols, bmask=mask)
+        for key, arr in s.items():
+            out[f"h{hi}_{key}"] = arr
+    path = os.path.join(OUT, f"sampled_sparse_{name}.npz")
+    np.savez_compressed(path, **out)
+    print(f"{name}: wrote {path} in {time.time() - t0:.1f} s", flush=True)
+
+
 if __name__ == "__main__":
-    main([int(a) for a in sys.argv[1:]] or [2, 3, 4, 5])
+    main([a if a in SPARSE_WORKLOADS else int(a) for a in sys.argv[1:]] or [2, 3, 4, 5, "local_global"])

@@ -167,3 +167,41 @@ def test_backward_varlen_rejects():
     assert call(a12=0, a0=0) == OK
     assert fa.varlen_workspace_bytes(100, 3, 80) == 4 * 3 * 100
     assert fa.varlen_workspace_bytes(-1, 3, 80) == 0
+
+
+def _fwd_bs(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, m=P + 1, sb=0, sh=16, B=1, H=2, N=300, d=64, scale=0.1,
+             causal=0, p=0.0, seed=0, stream=None, dtype=1)
+    a.update(kw)
+    return fa.lib().fa_forward_blocksparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["m"], a["sb"],
+                                           a["sh"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                                           a["causal"], a["p"], a["seed"], a["stream"], a["dtype"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m=0), NULL), (dict(sb=-1), ARG), (dict(sh=-16), ARG), (dict(N=131073, H=1), SHAPE),
+    (dict(q=0), NULL), (dict(o=P + 4), ALIGN), (dict(d=100), HEADDIM), (dict(dtype=5), DTYPE),
+    (dict(p=2.0), DROPOUT), (dict(scale=-1.0), ARG), (dict(B=0), SHAPE),
+])
+def test_forward_blocksparse_rejects(kw, status):
+    assert _fwd_bs(**kw) == status
+
+
+def test_backward_blocksparse_rejects():
+    L = fa.lib()
+    args = [P] * 10 + [P + 3, 0, 0, 1, 2, 300, 64, 0.1, 1, 0.0, 0, None, 1]
+
+    def call(**ch):
+        a = list(args)
+        for idx, val in ch.items():
+            a[int(idx[1:])] = val
+        return L.fa_backward_blocksparse(*a)
+
+    assert call(a10=0) == NULL        # mask
+    assert call(a9=0) == NULL         # workspace
+    assert call(a11=-1) == ARG
+    assert call(a12=-1) == ARG
+    assert call(a15=131073, a14=1) == SHAPE
+    assert call(a16=96) == HEADDIM
+    assert call(a19=1.0) == DROPOUT
+    assert call(a22=4) == DTYPE

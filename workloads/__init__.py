@@ -40,6 +40,10 @@ __all__ = [
     "varlen_lengths",
     "make_varlen_inputs",
     "counted_flops_varlen",
+    "BLOCK",
+    "block_mask_local_global",
+    "block_mask_random",
+    "SPARSE_WORKLOADS",
 ]
 
 
@@ -225,3 +229,35 @@ def counted_flops_varlen(lengths, H: int, d: int, causal: bool, backward: bool) 
     """counted_flops summed over the sequences of a packed batch."""
     fwd = sum(counted_flops(1, H, int(n), d, causal, False)[0] for n in lengths)
     return fwd, (2.5 * fwd if backward else 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Block-sparse masks over 128 x 128 blocks of the score matrix ("FlashAttention
+# for Efficient Training", section 3.2 "Block-Sparse Attention Support", for
+# sequences beyond 16K tokens). Structure only: uint8 arrays, 1 = computed.
+BLOCK = 128
+
+
+def block_mask_local_global(N: int, window: int, n_global: int) -> np.ndarray:
+    """[nb, nb] mask: query block i sees key blocks |i - j| <= window (a
+    sliding window) and the first n_global key blocks (global tokens)."""
+    nb = -(-N // BLOCK)
+    i = np.arange(nb)[:, None]
+    j = np.arange(nb)[None, :]
+    return ((np.abs(i - j) <= window) | (j < n_global)).astype(np.uint8)
+
+
+def block_mask_random(shape, N: int, density: float, seed: int) -> np.ndarray:
+    """[..., nb, nb] Bernoulli(density) mask from default_rng(seed)."""
+    nb = -(-N // BLOCK)
+    rng = np.random.default_rng(seed)
+    return (rng.random(tuple(shape) + (nb, nb)) < density).astype(np.uint8)
+
+
+# Long-sequence block-sparse workload: local window of +-8 blocks plus two
+# global key blocks, shared by all heads; inputs drawn as for fixed-length
+# workloads with seed 1000 + config_id.
+SPARSE_WORKLOADS = {
+    "local_global": (Workload(6, "bf16_B1_H16_N32768_d128_full_blocksparse_w8g2_fwdbwd", 1, 16, 32768, 128,
+                              "bf16", False, 0.0, True), dict(window=8, n_global=2)),
+}
