@@ -9,8 +9,8 @@ Workload: B=2, H=16, N=8192, d=128, causal, bf16 (the N=8K headline shape);
 the N=32K, d=80 shape and a packed batch of sixteen causal sequences of
 512..8192 tokens (with the time the same sequences take padded to the
 longest), and a block-sparse N=32K sequence (local window plus global key
-blocks, with the dense time on the same shape) are reported alongside under
-"also".
+blocks, with the dense time on the same shape), and the split-KV forward on a
+decode shape and a small-batch prefill are reported alongside under "also".
 FLOP convention: forward 4*B*H*N^2*d, halved for causal; backward 2.5x.
 """
 from __future__ import annotations
@@ -26,8 +26,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import (SPARSE_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS, block_mask_local_global,  # noqa: E402
-                       counted_flops, counted_flops_varlen, make_inputs, make_varlen_inputs)
+from workloads import (SPARSE_WORKLOADS, SPLITKV_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS,  # noqa: E402
+                       block_mask_local_global, counted_flops, counted_flops_varlen, make_cross_inputs,
+                       make_inputs, make_varlen_inputs)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
@@ -225,6 +226,47 @@ def run_gpu_sparse(name, steps, warmup, torch, fa):
     }
 
 
+def run_gpu_splitkv(name, steps, warmup, torch, fa):
+    """Split-KV forward: HIP-event time per call with the automatic part count
+    and with one part. Decode is bound by reading K and V (reported in GB/s of
+    K, V, Q, O and LSE bytes); prefill by the matrix cores (TFLOP/s)."""
+    w = SPLITKV_WORKLOADS[name]
+    inp = make_cross_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed)
+    dev = {k: torch.from_numpy(v[0].view(np.int16)).view(torch.bfloat16).cuda() for k, v in inp.items()}
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+    res = {"workload": w.name}
+    for label, ns in (("auto", fa.splitkv_num_splits(w.B, w.H, w.Nq, w.Nk, w.d)), ("one_part", 1)):
+        ws = torch.empty(fa.splitkv_workspace_bytes(w.B, w.H, w.Nq, w.d, ns) // 4, dtype=torch.float32,
+                         device="cuda")
+        for _ in range(warmup):
+            fa.forward_splitkv(q, k, v, w.causal, ns, w.scale, out=o, lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fa.forward_splitkv(q, k, v, w.causal, ns, w.scale, out=o, lse=lse, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        kv_bytes = 2.0 * w.B * w.Nk * w.H * w.d * 2
+        io_bytes = kv_bytes + 2.0 * (w.B * w.Nq * w.H * w.d * 2) + 4.0 * w.B * w.H * w.Nq
+        elems = w.B * w.H * float(w.Nq) * w.Nk
+        if w.causal:
+            elems = w.B * w.H * float(sum(min(w.Nk, i + 1 + w.Nk - w.Nq) for i in range(w.Nq)))
+        res[label] = {"num_splits": ns, "ms": ms, "GB/s": io_bytes / (ms * 1e-3) / 1e9,
+                      "tflops": 4.0 * w.d * elems / (ms * 1e-3) / 1e12}
+        del ws
+    if w.Nq == 1:
+        res["roofline"] = {"bound": "hbm", "achieved": res["auto"]["GB/s"], "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": res["auto"]["GB/s"] / PEAK_HBM_GBS}
+    else:
+        res["roofline"] = {"bound": "mfma", "achieved": res["auto"]["tflops"], "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": res["auto"]["tflops"] / PEAK_BF16_TFLOPS}
+    return res
+
+
 def kernel_source_digest():
     """SHA-256 over the kernel sources and the build flags: HBM traffic
     figures recorded under profiles/ are valid only for this digest."""
@@ -312,6 +354,7 @@ def main():
     ap.add_argument("--also", type=int, nargs="*", default=[4])
     ap.add_argument("--also-varlen", nargs="*", default=["varlen16"])
     ap.add_argument("--also-sparse", nargs="*", default=["local_global"])
+    ap.add_argument("--also-splitkv", nargs="*", default=["decode", "prefill_small"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -380,6 +423,9 @@ def main():
         torch.cuda.empty_cache()
     for name in a.also_sparse:
         also.append(run_gpu_sparse(name, max(3, a.steps // 4), 2, torch, fa))
+        torch.cuda.empty_cache()
+    for name in a.also_splitkv:
+        also.append(run_gpu_splitkv(name, max(5, a.steps), 3, torch, fa))
         torch.cuda.empty_cache()
     line["also"] = also
     line["cpu_baseline"] = None if a.no_cpu_baseline else cpu_baseline(w, a.cpu_seconds)

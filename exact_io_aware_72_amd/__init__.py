@@ -21,6 +21,7 @@ __all__ = [
     "backward_dkdv", "backward_dq", "workspace_bytes", "dropout_mask", "FlashAttnFunction",
     "flash_attention", "forward_varlen", "backward_varlen", "varlen_workspace_bytes",
     "forward_blocksparse", "backward_blocksparse", "BLOCK",
+    "forward_splitkv", "splitkv_num_splits", "splitkv_workspace_bytes",
     "EXPORTED_SYMBOLS", "STATUS",
 ]
 
@@ -35,6 +36,7 @@ EXPORTED_SYMBOLS = (
     "fa_backward_dkdv", "fa_backward_dq", "fa_dropout_mask", "fa_status_string", "fa_version",
     "fa_forward_varlen", "fa_backward_varlen", "fa_backward_varlen_workspace_bytes",
     "fa_forward_blocksparse", "fa_backward_blocksparse",
+    "fa_splitkv_num_splits", "fa_forward_splitkv_workspace_bytes", "fa_forward_splitkv",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +69,9 @@ _SIGS = {
     "fa_backward_varlen": (_i, [_vp] * 11 + [_i, _i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
     "fa_forward_blocksparse": (_i, [_vp] * 6 + [_i64, _i64, _i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
     "fa_backward_blocksparse": (_i, [_vp] * 11 + [_i64, _i64, _i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
+    "fa_splitkv_num_splits": (_i, [_i, _i, _i, _i, _i]),
+    "fa_forward_splitkv_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "fa_forward_splitkv": (_i, [_vp] * 6 + [_i, _i, _i, _i, _i, _f, _i, _i, _vp, _i]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
     "fa_version": (ctypes.c_char_p, []),
 }
@@ -339,6 +344,42 @@ def backward_blocksparse(q, k, v, o, dout, lse, block_mask, causal=False, dropou
                                        int(seed), _stream(q), _code(q))
     _check(st, "fa_backward_blocksparse")
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Split-KV forward: queries (B, Nq, H, d) against keys/values (B, Nk, H, d).
+def splitkv_num_splits(B, H, Nq, Nk, d) -> int:
+    return int(lib().fa_splitkv_num_splits(B, H, Nq, Nk, d))
+
+
+def splitkv_workspace_bytes(B, H, Nq, d, num_splits) -> int:
+    return int(lib().fa_forward_splitkv_workspace_bytes(B, H, Nq, d, num_splits))
+
+
+def forward_splitkv(q, k, v, causal=False, num_splits=0, scale=None, out=None, lse=None,
+                    workspace=None):
+    """Returns (o, lse) with o like q and lse float32 (B, H, Nq). Causal
+    queries are the last Nq positions of the Nk keys. num_splits = 0 picks the
+    count with splitkv_num_splits."""
+    torch = _torch()
+    B, Nq, H, d = _shape(q)
+    Bk, Nk, Hk, dk = _shape(k, v)
+    if (Bk, Hk, dk) != (B, H, d) or k.dtype != q.dtype or k.device != q.device:
+        raise ValueError("k, v must be (B, Nk, H, d) like q on the same GPU")
+    ns = int(num_splits) if num_splits else splitkv_num_splits(B, H, Nq, Nk, d)
+    if ns < 1:
+        raise FAError(-2, "fa_forward_splitkv", "invalid shape")
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _shape(q, o)
+    if workspace is None:
+        nbytes = splitkv_workspace_bytes(B, H, Nq, d, ns)
+        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
+    st = lib().fa_forward_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse_t.data_ptr(), workspace.data_ptr(), B, H, Nq, Nk, d,
+                                  _scale(scale, d), int(bool(causal)), ns, _stream(q), _code(q))
+    _check(st, "fa_forward_splitkv")
+    return o, lse_t
 
 
 def dropout_mask(seed, b, h, H, dropout_p, row0, col0, rows, cols, device="cuda"):

@@ -3,6 +3,7 @@
 // rejected call launches nothing and writes nothing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -349,6 +350,71 @@ FA_EXPORT int fa_backward_blocksparse(const void* q, const void* k, const void* 
   FA_TRY(hip_status(fa::launch_bwd_preprocess(a, s, bf16)));
   FA_TRY(hip_status(bf16 ? fa::launch_bwd_dkdv_bf16(a, s) : fa::launch_bwd_dkdv_f32(a, s)));
   return hip_status(bf16 ? fa::launch_bwd_dq_bf16(a, s) : fa::launch_bwd_dq_f32(a, s));
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV forward.
+namespace {
+constexpr int kMaxSplits = 128;
+
+int check_splitkv(int B, int H, int Nq, int Nk, int d, int causal, int num_splits, int dtype) {
+  FA_TRY(check_problem(B, H, Nq, d, dtype));
+  FA_TRY(check_problem(B, H, Nk, d, dtype));
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (causal && Nk < Nq) return FA_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_ARG;
+  const int64_t wgs = (int64_t)((Nq + 127) / 128) * B * H * (num_splits ? num_splits : kMaxSplits);
+  if (wgs > (int64_t)INT32_MAX) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int pick_splits(int B, int H, int Nq, int Nk) {
+  // Enough work-groups for two per compute unit (256 CUs), and at least four
+  // 64-key tiles per part.
+  const int64_t wgs = (int64_t)((Nq + 127) / 128) * B * H;
+  if (wgs >= 512) return 1;
+  const int tiles = (Nk + 63) / 64;
+  int s = (int)((512 + wgs - 1) / wgs);
+  s = std::min(s, std::max(1, tiles / 4));
+  return std::max(1, std::min(s, kMaxSplits));
+}
+}  // namespace
+
+FA_EXPORT int fa_splitkv_num_splits(int B, int H, int Nq, int Nk, int d) {
+  if (check_splitkv(B, H, Nq, Nk, d, 0, 0, FA_BF16) != FA_OK) return 0;
+  return pick_splits(B, H, Nq, Nk);
+}
+
+FA_EXPORT size_t fa_forward_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits) {
+  if (num_splits < 1 || num_splits > kMaxSplits) return 0;
+  if (check_problem(B, H, Nq, d, FA_BF16) != FA_OK) return 0;
+  return (size_t)4 * (size_t)num_splits * (size_t)B * (size_t)H * (size_t)Nq * (size_t)(d + 1);
+}
+
+FA_EXPORT int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 float* workspace, int B, int H, int Nq, int Nk, int d,
+                                 float scale, int causal, int num_splits, void* stream,
+                                 int dtype) {
+  FA_TRY(check_splitkv(B, H, Nq, Nk, d, causal, num_splits, dtype));
+  FA_TRY(check_scale(scale));
+  FA_TRY(check_ptrs({q, k, v, o, lse, workspace}));
+  fa::AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o_out = o;
+  a.lse_out = lse;
+  a.B = B;
+  a.H = H;
+  a.N = Nq;
+  a.Nk = Nk;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.num_splits = num_splits ? num_splits : pick_splits(B, H, Nq, Nk);
+  a.split_o = workspace;
+  a.split_lse = workspace + (size_t)a.num_splits * B * H * Nq * d;
+  return hip_status(fa::launch_forward_splitkv_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
 FA_EXPORT int fa_dropout_mask(uint64_t seed, int b, int h, int H, float dropout_p, int row0,

@@ -32,6 +32,12 @@
 namespace fa {
 namespace {
 
+#define FA_HIP_RETURN_IF(x)            \
+  do {                                 \
+    const hipError_t e_ = (x);         \
+    if (e_ != hipSuccess) return e_;   \
+  } while (0)
+
 struct FwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -43,6 +49,11 @@ struct FwdParams {
   int total;
   const uint8_t* bmask;  // block-sparse mask, or nullptr
   int64_t msb, msh;
+  // Split-KV: Nk key rows per batch item (N query rows), the key range cut
+  // into nsplit parts; part s writes O_s (fp32, normalised) and LSE_s.
+  int Nk, nsplit;
+  float* ws_o;    // [nsplit][B][H][N][D]
+  float* ws_lse;  // [nsplit][B][H][N]
   float c2;  // scale * log2(e)
   uint32_t drop_t;
   float drop_r;
@@ -64,7 +75,7 @@ struct FwdCfg {
   static constexpr int LPW = (NLOAD + 3) / 4;          // per wave
 };
 
-template <int D, bool CAUSAL, bool DROP, bool SPARSE>
+template <int D, bool CAUSAL, bool DROP, bool SPARSE, bool SPLIT>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   using C = FwdCfg<D>;
   using KT = typename C::KT;
@@ -77,6 +88,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   __shared__ __align__(16) uint32_t ck1[DROP ? C::BN : 1];
   __shared__ uint16_t kept[SPARSE ? kSparseMaxBlocks : 1];  // kept key blocks
   static_assert(!SPARSE || C::BM == kSparseBlock, "a work-group covers one mask row");
+  static_assert(!(SPLIT && (SPARSE || DROP)), "split-KV runs without dropout or block masks");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -84,20 +96,30 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   const int l32 = lane & 31, hf = lane >> 5;
   const int H = p.H;
   const int nqb = (p.N + C::BM - 1) / C::BM;
-  const BlockMap bm = map_block(blockIdx.x, nqb, p.B * H);
+  int wgid = blockIdx.x, split = 0;
+  if constexpr (SPLIT) {
+    split = wgid % p.nsplit;
+    wgid /= p.nsplit;
+  }
+  const BlockMap bm = map_block(wgid, nqb, p.B * H);
   const int qb = CAUSAL ? (nqb - 1 - bm.rank) : bm.rank;
   const int b = bm.bh / H, h = bm.bh - b * H;
   const SeqRows sr = seq_rows(p.cu, p.total, b, h, H, D, p.N);
-  const int N = sr.n;
+  const int N = sr.n;             // query rows
+  const int Nk = SPLIT ? p.Nk : N;  // key rows
+  // Causal: key j is visible to query i iff j <= i + coff; with Nk > N the
+  // queries are the last N positions of the key sequence.
+  const int coff = Nk - N;
   const int q0 = qb * C::BM;
   if (q0 >= N) return;  // block past the end of a shorter sequence
   const int qw0 = q0 + wave * 32;
   const int myq = qw0 + l32;
   const int64_t rs = (int64_t)H * D;
   const int64_t base = sr.base;
+  const int64_t kbase = SPLIT ? ((int64_t)b * Nk * H + h) * D : base;
   const uint16_t* Qg = p.q + base;
-  const uint16_t* Kg = p.k + base;
-  const uint16_t* Vg = p.v + base;
+  const uint16_t* Kg = p.k + kbase;
+  const uint16_t* Vg = p.v + kbase;
   const uint32_t rs2 = (uint32_t)(H * D * 2);  // bytes between consecutive rows
 
   // Q operand (B of S^T = K Q^T): 8 d-values per lane per 16-wide chunk;
@@ -114,9 +136,15 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
     arow = row_key(kbh, myq);
   }
 
-  const int kend = CAUSAL ? min(N, q0 + C::BM) : N;
-  int ntiles;
-  if constexpr (SPARSE) {
+  const int kend = CAUSAL ? min(Nk, q0 + C::BM + coff) : Nk;
+  int ntiles, tfirst = 0;
+  if constexpr (SPLIT) {
+    // This part's share of the key tiles: parts of equal tile counts.
+    const int all = (kend + C::BN - 1) / C::BN;
+    const int per = (all + p.nsplit - 1) / p.nsplit;
+    tfirst = min(all, split * per);
+    ntiles = min(all, tfirst + per) - tfirst;
+  } else if constexpr (SPARSE) {
     // Kept key blocks of this query block, in ascending order.
     const int nb = (N + kSparseBlock - 1) / kSparseBlock;
     const uint8_t* mrow = p.bmask + b * p.msb + h * p.msh + (int64_t)qb * nb;
@@ -127,7 +155,9 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   } else {
     ntiles = (kend + C::BN - 1) / C::BN;
   }
-  auto tile_start = [&](int t) { return SPARSE ? kept_tile_start<C::BN>(kept, t) : t * C::BN; };
+  auto tile_start = [&](int t) {
+    return SPARSE ? kept_tile_start<C::BN>(kept, t) : (tfirst + t) * C::BN;
+  };
 
   // This wave's share of the tile loads: K instructions first, then V.
   uint32_t dsrc[C::LPW];
@@ -147,7 +177,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   }
   auto issue = [&](char* stage, uint32_t* ck, int k0) {
     // Resources start at row k0 and end at row N: rows past N arrive as zeros.
-    const uint32_t left = (uint32_t)(N - k0) * rs2;
+    const uint32_t left = (uint32_t)(Nk - k0) * rs2;
     const BufRes rk = make_bufres(Kg + (int64_t)k0 * rs, left);
     const BufRes rv = make_bufres(Vg + (int64_t)k0 * rs, left);
 #pragma unroll
@@ -199,7 +229,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
     __syncthreads();
     const int k0 = tile_start(t);
     if (t + 1 < ntiles) issue(nxt, ckn, tile_start(t + 1));
-    if (CAUSAL && k0 > qw0 + 31) return;  // every key of the tile is after this wave's queries
+    if (CAUSAL && k0 > qw0 + 31 + coff) return;  // every key is after this wave's queries
+    if (SPLIT && qw0 >= N) return;                // no query rows in this wave
 
     // S^T = K Q^T: lane = query, registers = keys (c_row layout).
     f32x16 s0 = f32x16{}, s1 = f32x16{};
@@ -217,8 +248,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
       s1 = mfma32x32x16(ld_lds_128(cur, o1), qreg[c], s1);
     }
     sched_lds_ahead<C::NKC, 2, 2>();
-    if ((k0 + C::BN > N) || (CAUSAL && k0 + C::BN - 1 > qw0)) {
-      const int lim = CAUSAL ? min(myq, N - 1) : N - 1;  // last visible key
+    if ((k0 + C::BN > Nk) || (CAUSAL && k0 + C::BN - 1 > qw0 + coff)) {
+      const int lim = CAUSAL ? min(myq + coff, Nk - 1) : Nk - 1;  // last visible key
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + c_row(r, hf);
@@ -235,13 +266,17 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
     const float mx = xor32_max(fmaxf(ma, mb)) * c2;
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
       const float mnew = fmaxf(m, mx);
-      const float alpha = exp2_hw(m - mnew);
+      // Rows without a visible key so far (only in a split key range) have
+      // l = 0 and O = 0: scale 0 instead of exp2(-inf - -inf).
+      const float alpha = (SPLIT && m == -INFINITY) ? 0.f : exp2_hw(m - mnew);
       m = mnew;
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) oacc[db] *= alpha;
     }
-    const float nm = -m;
+    // A part of a split key range can start with a tile in which some rows
+    // see no key yet (m = -inf); they take reference 0 so that exp2 gives 0.
+    const float nm = (SPLIT && m == -INFINITY) ? 0.f : -m;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       s0[r] = exp2_hw(fmaf(s0[r], c2, nm));
@@ -314,6 +349,29 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   }
 
   const float ltot = xor32_sum(l);
+  if constexpr (SPLIT) {
+    // Partial result of this key range, normalised by its own sum; a range
+    // with no visible key gives O_s = 0 and LSE_s = -inf.
+    if (myq < N) {
+      const int64_t row = (((int64_t)split * p.B + b) * H + h) * N + myq;
+      const float inv = ltot == 0.f ? 0.f : 1.f / ltot;
+      float* orow = p.ws_o + row * D;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = db * 32 + 8 * g + 4 * hf;
+          if (d0 < D) {
+            const f32x4 w = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
+                             oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
+            *reinterpret_cast<f32x4*>(orow + d0) = w;
+          }
+        }
+      }
+      if (hf == 0) p.ws_lse[row] = ltot == 0.f ? -INFINITY : (m + log2_hw(ltot)) * kLn2;
+    }
+    return;
+  }
   if (myq < N) {
     // A row whose blocks are all masked has no keys: O = 0, LSE = -inf.
     const float inv = (SPARSE && ltot == 0.f) ? 0.f : (DROP ? p.drop_r : 1.f) / ltot;
@@ -466,9 +524,54 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
 
 template <int D, bool CAUSAL, bool DROP, bool SPARSE>
 hipError_t launch_fwd_bf16_t(const FwdParams& prm, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROP, SPARSE>), dim3(nblocks), dim3(256), 0, s,
-                     prm);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROP, SPARSE, false>), dim3(nblocks), dim3(256),
+                     0, s, prm);
   return hipGetLastError();
+}
+
+// Split-KV combine: for each query row, LSE = ln sum_s e^{LSE_s} and
+// O = sum_s e^{LSE_s - LSE} O_s (the rescale of the online softmax applied
+// across the parts). Sixteen lanes per row; bound by HBM bandwidth.
+template <int D>
+__global__ __launch_bounds__(256) void splitkv_combine_kernel(const float* __restrict__ ws_o,
+                                                              const float* __restrict__ ws_lse,
+                                                              uint16_t* __restrict__ o,
+                                                              float* __restrict__ lse, int B,
+                                                              int H, int N, int nsplit) {
+  const int64_t rows = (int64_t)B * H * N;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // [b][h][q]
+  const int sub = threadIdx.x & 15;
+  if (row >= rows) return;
+  float mx = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, ws_lse[sp * rows + row]);
+  constexpr int PER = (D + 15) / 16;
+  float acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+  float sum = 0.f;
+  if (mx != -INFINITY) {
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float w = exp2_hw((ws_lse[sp * rows + row] - mx) * kLog2e);
+      sum += w;
+      const float* orow = ws_o + (sp * rows + row) * D;
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (sub + 16 * j < D) acc[j] = fmaf(w, orow[sub + 16 * j], acc[j]);
+    }
+  }
+  const int q = (int)(row % N);
+  const int64_t bh = row / N;
+  const int h = (int)(bh % H), b = (int)(bh / H);
+  uint16_t* orow = o + (((int64_t)b * N + q) * H + h) * D;
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (sub + 16 * j < D) {
+      const uint32_t w = pack_bf16x2(acc[j] * inv, 0.f);
+      orow[sub + 16 * j] = (uint16_t)(w & 0xffffu);
+    }
+  }
+  if (sub == 0) lse[row] = sum > 0.f ? mx + log2_hw(sum) * kLn2 : -INFINITY;
 }
 
 template <int D, bool SPARSE>
@@ -521,6 +624,10 @@ hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s) {
   prm.bmask = a.block_mask;
   prm.msb = a.mask_stride_b;
   prm.msh = a.mask_stride_h;
+  prm.Nk = a.N;
+  prm.nsplit = 1;
+  prm.ws_o = nullptr;
+  prm.ws_lse = nullptr;
   prm.c2 = a.scale * kLog2e;
   prm.drop_t = a.drop_threshold;
   prm.drop_r = a.drop_rescale;
@@ -533,6 +640,63 @@ hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s) {
     case 128: return launch_fwd_bf16_d<128>(prm, a.causal, a.dropout, nblocks, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_forward_splitkv_bf16(const AttnArgs& a, hipStream_t s) {
+  FwdParams prm{};
+  prm.q = static_cast<const uint16_t*>(a.q);
+  prm.k = static_cast<const uint16_t*>(a.k);
+  prm.v = static_cast<const uint16_t*>(a.v);
+  prm.o = nullptr;
+  prm.lse = nullptr;
+  prm.B = a.B;
+  prm.H = a.H;
+  prm.N = a.N;
+  prm.cu = nullptr;
+  prm.total = 0;
+  prm.bmask = nullptr;
+  prm.Nk = a.Nk;
+  prm.nsplit = a.num_splits;
+  prm.ws_o = a.split_o;
+  prm.ws_lse = a.split_lse;
+  prm.c2 = a.scale * kLog2e;
+  const int nqb = (a.N + 127) / 128;
+  const dim3 grid((unsigned)(nqb * a.B * a.H * a.num_splits)), block(256);
+#define FA_SPLIT(D)                                                                          \
+  case D:                                                                                    \
+    if (a.causal)                                                                            \
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, true, false, false, true>), grid, block, 0, s,  \
+                         prm);                                                               \
+    else                                                                                     \
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, false, false, false, true>), grid, block, 0, s, \
+                         prm);                                                               \
+    break;
+  switch (a.d) {
+    FA_SPLIT(64)
+    FA_SPLIT(80)
+    FA_SPLIT(128)
+    default: return hipErrorInvalidValue;
+  }
+#undef FA_SPLIT
+  FA_HIP_RETURN_IF(hipGetLastError());
+  const int64_t rows = (int64_t)a.B * a.H * a.N;
+  const dim3 cgrid((unsigned)((rows + 15) / 16));
+  uint16_t* o = static_cast<uint16_t*>(a.o_out);
+  switch (a.d) {
+    case 64:
+      hipLaunchKernelGGL((splitkv_combine_kernel<64>), cgrid, block, 0, s, a.split_o, a.split_lse,
+                         o, a.lse_out, a.B, a.H, a.N, a.num_splits);
+      break;
+    case 80:
+      hipLaunchKernelGGL((splitkv_combine_kernel<80>), cgrid, block, 0, s, a.split_o, a.split_lse,
+                         o, a.lse_out, a.B, a.H, a.N, a.num_splits);
+      break;
+    default:
+      hipLaunchKernelGGL((splitkv_combine_kernel<128>), cgrid, block, 0, s, a.split_o,
+                         a.split_lse, o, a.lse_out, a.B, a.H, a.N, a.num_splits);
+      break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_forward_f32(const AttnArgs& a, hipStream_t s) {

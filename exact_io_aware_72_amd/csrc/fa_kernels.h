@@ -41,6 +41,12 @@ struct AttnArgs {
   // ceil(N / 128); nonzero = the 128 x 128 block is computed. nullptr: dense.
   const uint8_t* block_mask = nullptr;
   int64_t mask_stride_b = 0, mask_stride_h = 0;
+  // Split-KV forward: N query rows against Nk key rows per batch item, the
+  // key range cut into num_splits parts whose partial results (O_s fp32
+  // [num_splits][B][H][N][d], LSE_s [num_splits][B][H][N]) are combined.
+  int Nk = 0, num_splits = 1;
+  float* split_o = nullptr;
+  float* split_lse = nullptr;
   float scale = 0.f;
   bool causal = false;
   bool dropout = false;
@@ -51,6 +57,7 @@ struct AttnArgs {
 
 hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_forward_f32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_forward_splitkv_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t s, bool bf16);
 hipError_t launch_bwd_dkdv_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const AttnArgs& a, hipStream_t s);

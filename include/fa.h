@@ -193,6 +193,34 @@ int fa_backward_blocksparse(const void* q, const void* k, const void* v, const v
                             int causal, float dropout_p, uint64_t seed, void* stream, int dtype);
 
 /*
+ * Split-KV forward for shapes with little parallelism (few batch items and
+ * heads, short query blocks against long key sequences, e.g. decoding):
+ * per-tile softmax results are merged by a reduction ("FlashAttention for
+ * Efficient Training", section 2.3, "Practical Implementation"; its section
+ * 6.1, "Limited Parallelism for Small Batch Sizes", names small batches and
+ * few heads as the case of idle compute units). The key range is cut into
+ * num_splits parts computed by separate work-groups; each part's normalised
+ * output O_s and logsumexp LSE_s are merged exactly:
+ * LSE = ln sum_s e^{LSE_s}, O = sum_s e^{LSE_s - LSE} O_s.
+ *   q, o      [B][Nq][H][d] bf16;  k, v  [B][Nk][H][d] bf16;  lse [B][H][Nq] fp32
+ *   causal    key j is visible to query i iff j <= i + (Nk - Nq): the queries
+ *             are the last Nq positions of the key sequence (needs Nk >= Nq)
+ *   num_splits  1..128, or 0 to let fa_splitkv_num_splits choose
+ *   workspace fa_forward_splitkv_workspace_bytes(B, H, Nq, d, num_splits)
+ *             bytes of device memory (fp32 partial results), 16-byte aligned;
+ *             with num_splits = 0 size it for 128 parts or for the number
+ *             fa_splitkv_num_splits returns
+ * No dropout (an inference path). dtype must be FA_BF16 (FA_ERR_UNSUPPORTED
+ * otherwise). Other arguments and errors as for fa_forward; FA_ERR_ARG for
+ * num_splits outside 0..128, FA_ERR_SHAPE for causal with Nk < Nq.
+ */
+int fa_splitkv_num_splits(int B, int H, int Nq, int Nk, int d);
+size_t fa_forward_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits);
+int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                       float* workspace, int B, int H, int Nq, int Nk, int d, float scale,
+                       int causal, int num_splits, void* stream, int dtype);
+
+/*
  * Writes the dropout keep mask of head (b, h) for rows row0..row0+rows-1 and
  * columns col0..col0+cols-1 to out[rows][cols] (device, 1 = keep), with the
  * same device function the kernels use. The pages fuse dropout into the

@@ -24,6 +24,7 @@ from .attention import (  # noqa: F401
     softmax_stats,
     attention_probs,
     forward,
+    forward_cross,
     backward,
     sampled_head,
 )

@@ -20,6 +20,9 @@ Definitions followed ("FlashAttention for Efficient Training" unless noted):
     blocks are -inf ("Only non-zero blocks ... are computed", section 3.2
     "Block-Sparse Attention Support"); a row left with no finite score gets
     P = 0, O = 0 and LSE = -inf
+  * queries against a longer key sequence (forward_cross): under the causal
+    mask the Nq queries are the last Nq of the Nk positions (a reading; the
+    pages only use queries and keys of one length)
   * numerically stable softmax: subtract the row max before exp (section 6.2
     "Hardware-Specific Optimizations")
   * per-row logsumexp LSE_i = log sum_j exp(S_ij), natural log (section 3.2,
@@ -109,17 +112,20 @@ def _dropped(p_mat, seed, b, h, H, dropout_p, rows, cols):
     return p_mat * z * r
 
 
-def head_forward(qh, kh, vh, scale, causal, dropout_p, seed, b, h, H, panel=_PANEL, bmask=None):
-    """One head of one sequence: qh, kh, vh are [n, d] float64 arrays, (b, h, H)
-    key the dropout hash, bmask is this head's block mask or None. Returns
-    (O [n, d], LSE [n]); rows with no unmasked key get O = 0, LSE = -inf."""
+def head_forward(qh, kh, vh, scale, causal, dropout_p, seed, b, h, H, panel=_PANEL, bmask=None,
+                 row_offset=0):
+    """One head of one sequence: qh is [n, d], kh, vh are [m, d] float64
+    arrays, (b, h, H) key the dropout hash, bmask is this head's block mask or
+    None. Query i sits at key position row_offset + i for the causal mask.
+    Returns (O [n, d], LSE [n]); rows with no unmasked key get O = 0,
+    LSE = -inf."""
     n = qh.shape[0]
     o = np.zeros((n, vh.shape[1]), np.float64)
     lse = np.zeros(n, np.float64)
     for r0 in range(0, n, panel):
         r1 = min(r0 + panel, n)
-        nc = _panel_cols(causal, r1, kh.shape[0])
-        s = attention_scores(qh[r0:r1], kh[:nc], scale, causal, r0)
+        nc = _panel_cols(causal, row_offset + r1, kh.shape[0])
+        s = attention_scores(qh[r0:r1], kh[:nc], scale, causal, row_offset + r0)
         s = apply_block_mask(s, bmask, np.arange(r0, r1), np.arange(nc))
         _, _, l_ = softmax_stats(s)
         p = attention_probs(s, l_)
@@ -185,6 +191,27 @@ def forward(q, k, v, scale, causal, dropout_p=0.0, seed=0, heads=None, panel=_PA
         o[b, :, h, :], lse[b, h, :] = head_forward(
             q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], scale, causal, dropout_p, seed, b, h, H,
             panel, None if block_mask is None else block_mask[b][h])
+    return o, lse
+
+
+def forward_cross(q, k, v, scale, causal, panel=_PANEL):
+    """Queries [B, Nq, H, d] against keys and values [B, Nk, H, d]. Under the
+    causal mask the queries are the last Nq of the Nk positions (query i at
+    position Nk - Nq + i), so query i sees keys j <= i + Nk - Nq; with
+    Nq = Nk this is forward(). Returns (O [B, Nq, H, d], LSE [B, H, Nq])."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, Nq, H, _ = q.shape
+    Nk = k.shape[1]
+    off = Nk - Nq if causal else 0
+    o = np.zeros((B, Nq, H, v.shape[3]), np.float64)
+    lse = np.zeros((B, H, Nq), np.float64)
+    for b in range(B):
+        for h in range(H):
+            o[b, :, h, :], lse[b, h, :] = head_forward(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :],
+                                                       scale, causal, 0.0, 0, b, h, H, panel,
+                                                       None, off)
     return o, lse
 
 

@@ -205,3 +205,29 @@ def test_backward_blocksparse_rejects():
     assert call(a16=96) == HEADDIM
     assert call(a19=1.0) == DROPOUT
     assert call(a22=4) == DTYPE
+
+
+def test_splitkv_rejects_and_sizes():
+    L = fa.lib()
+    args = [P] * 6 + [1, 2, 1, 1000, 128, 0.1, 1, 0, None, 1]
+
+    def call(**ch):
+        a = list(args)
+        for idx, val in ch.items():
+            a[int(idx[1:])] = val
+        return L.fa_forward_splitkv(*a)
+
+    assert call(a5=0) == NULL            # workspace
+    assert call(a5=P + 4) == ALIGN
+    assert call(a15=0) == UNSUP          # fp32 is not implemented for split-KV
+    assert call(a13=-1) == ARG           # num_splits
+    assert call(a13=129) == ARG
+    assert call(a8=1001) == SHAPE        # causal with Nk < Nq
+    assert call(a9=0) == SHAPE           # Nk
+    assert call(a10=96) == HEADDIM
+    assert call(a11=float("nan")) == ARG
+    assert L.fa_forward_splitkv_workspace_bytes(1, 2, 3, 128, 4) == 4 * 4 * 1 * 2 * 3 * 129
+    assert L.fa_forward_splitkv_workspace_bytes(1, 2, 3, 128, 0) == 0
+    assert L.fa_splitkv_num_splits(4, 16, 1, 65536, 128) > 1
+    assert L.fa_splitkv_num_splits(8, 32, 8192, 8192, 128) == 1
+    assert L.fa_splitkv_num_splits(1, 1, 1, 100, 128) == 1   # at least four key tiles per part

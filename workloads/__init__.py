@@ -44,6 +44,9 @@ __all__ = [
     "block_mask_local_global",
     "block_mask_random",
     "SPARSE_WORKLOADS",
+    "SplitKVWorkload",
+    "SPLITKV_WORKLOADS",
+    "make_cross_inputs",
 ]
 
 
@@ -261,3 +264,43 @@ SPARSE_WORKLOADS = {
     "local_global": (Workload(6, "bf16_B1_H16_N32768_d128_full_blocksparse_w8g2_fwdbwd", 1, 16, 32768, 128,
                               "bf16", False, 0.0, True), dict(window=8, n_global=2)),
 }
+
+
+# ---------------------------------------------------------------------------
+# Queries against a longer key sequence (split-KV forward): decoding (one new
+# query per sequence against its cached keys) and short-batch prefill, the
+# low-parallelism shapes of "FlashAttention for Efficient Training", section
+# 6.1 "Limited Parallelism for Small Batch Sizes".
+#
+# Recipe (fixed): rng = default_rng(seed); q = standard_normal([B, Nq, H, d]),
+# then k, v = standard_normal([B, Nk, H, d]) each, float32, rounded to bf16.
+@dataclasses.dataclass(frozen=True)
+class SplitKVWorkload:
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    seed: int
+    dtype: str = "bf16"
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+SPLITKV_WORKLOADS = {
+    "decode": SplitKVWorkload("bf16_decode_B4_H16_Nq1_Nk65536_d128", 4, 16, 1, 65536, 128, True, 3100),
+    "prefill_small": SplitKVWorkload("bf16_B1_H8_N4096_d128_causal_fwd", 1, 8, 4096, 4096, 128, True, 3101),
+}
+
+
+def make_cross_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, seed: int, amp: float = 1.0):
+    """dict name -> (stored, values) for q [B, Nq, H, d] and k, v [B, Nk, H, d]."""
+    rng = np.random.default_rng(seed)
+    out = {"q": make_tensor(rng, (B, Nq, H, d), amp, dtype)}
+    for name in ("k", "v"):
+        out[name] = make_tensor(rng, (B, Nk, H, d), amp, dtype)
+    return out
