@@ -10,7 +10,8 @@ the N=32K, d=80 shape and a packed batch of sixteen causal sequences of
 512..8192 tokens (with the time the same sequences take padded to the
 longest), and a block-sparse N=32K sequence (local window plus global key
 blocks, with the dense time on the same shape), and the split-KV forward on a
-decode shape and a small-batch prefill are reported alongside under "also".
+decode shape and a small-batch prefill, and the forward with FP8 scores on
+the N=8K shape are reported alongside under "also".
 FLOP convention: forward 4*B*H*N^2*d, halved for causal; backward 2.5x.
 """
 from __future__ import annotations
@@ -267,6 +268,41 @@ def run_gpu_splitkv(name, steps, warmup, torch, fa):
     return res
 
 
+def run_gpu_fp8(cfg, steps, warmup, torch, fa):
+    """Forward with FP8 scores on a fixed-length workload: HIP-event times of
+    the two quantisation launches (Q per 128 rows, K per 64 rows) and of the
+    forward, against the bf16 forward on the same inputs."""
+    w = WORKLOADS[cfg]
+    dev = _device_inputs(w, torch)
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    q8, qs = fa.quantize_fp8(q, 128)
+    k8, ks = fa.quantize_fp8(k, 64)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    fwd_f, _ = counted_flops(w.B, w.H, w.N, w.d, w.causal, False)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_quant = timed(lambda: (fa.quantize_fp8(q, 128, out=q8, scales=qs),
+                              fa.quantize_fp8(k, 64, out=k8, scales=ks)))
+    ms_fp8 = timed(lambda: fa.forward_fp8_quantized(q8, k8, v, qs, ks, w.causal, w.scale, out=o,
+                                                    lse=lse))
+    ms_bf16 = timed(lambda: fa.forward(q, k, v, w.causal, 0.0, 0, w.scale, out=o, lse=lse))
+    return {"workload": w.name + "_fp8_scores_fwd", "forward_fp8_ms": ms_fp8,
+            "forward_fp8_tflops": fwd_f / (ms_fp8 * 1e-3) / 1e12, "quantize_q_k_ms": ms_quant,
+            "forward_bf16_ms": ms_bf16, "forward_bf16_tflops": fwd_f / (ms_bf16 * 1e-3) / 1e12}
+
+
 def kernel_source_digest():
     """SHA-256 over the kernel sources and the build flags: HBM traffic
     figures recorded under profiles/ are valid only for this digest."""
@@ -355,6 +391,7 @@ def main():
     ap.add_argument("--also-varlen", nargs="*", default=["varlen16"])
     ap.add_argument("--also-sparse", nargs="*", default=["local_global"])
     ap.add_argument("--also-splitkv", nargs="*", default=["decode", "prefill_small"])
+    ap.add_argument("--also-fp8", type=int, nargs="*", default=[3])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -426,6 +463,9 @@ def main():
         torch.cuda.empty_cache()
     for name in a.also_splitkv:
         also.append(run_gpu_splitkv(name, max(5, a.steps), 3, torch, fa))
+        torch.cuda.empty_cache()
+    for cfg in a.also_fp8:
+        also.append(run_gpu_fp8(cfg, max(5, a.steps // 2), 2, torch, fa))
         torch.cuda.empty_cache()
     line["also"] = also
     line["cpu_baseline"] = None if a.no_cpu_baseline else cpu_baseline(w, a.cpu_seconds)

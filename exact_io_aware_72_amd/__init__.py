@@ -22,6 +22,7 @@ __all__ = [
     "flash_attention", "forward_varlen", "backward_varlen", "varlen_workspace_bytes",
     "forward_blocksparse", "backward_blocksparse", "BLOCK",
     "forward_splitkv", "splitkv_num_splits", "splitkv_workspace_bytes",
+    "quantize_fp8", "forward_fp8", "forward_fp8_quantized",
     "EXPORTED_SYMBOLS", "STATUS",
 ]
 
@@ -37,6 +38,7 @@ EXPORTED_SYMBOLS = (
     "fa_forward_varlen", "fa_backward_varlen", "fa_backward_varlen_workspace_bytes",
     "fa_forward_blocksparse", "fa_backward_blocksparse",
     "fa_splitkv_num_splits", "fa_forward_splitkv_workspace_bytes", "fa_forward_splitkv",
+    "fa_quantize_fp8", "fa_forward_fp8",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +74,8 @@ _SIGS = {
     "fa_splitkv_num_splits": (_i, [_i, _i, _i, _i, _i]),
     "fa_forward_splitkv_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "fa_forward_splitkv": (_i, [_vp] * 6 + [_i, _i, _i, _i, _i, _f, _i, _i, _vp, _i]),
+    "fa_quantize_fp8": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "fa_forward_fp8": (_i, [_vp] * 7 + [_i, _i, _i, _i, _f, _i, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
     "fa_version": (ctypes.c_char_p, []),
 }
@@ -380,6 +384,46 @@ def forward_splitkv(q, k, v, causal=False, num_splits=0, scale=None, out=None, l
                                   _scale(scale, d), int(bool(causal)), ns, _stream(q), _code(q))
     _check(st, "fa_forward_splitkv")
     return o, lse_t
+
+
+# ---------------------------------------------------------------------------
+# FP8 scores: per-block quantised Q and K (OCP E4M3 bytes) with fp32 scales.
+def quantize_fp8(x, block_rows, out=None, scales=None):
+    """x bf16 (B, N, H, d) -> (uint8 codes like x, float32 scales (B, H, nblk))."""
+    torch = _torch()
+    B, N, H, d = _shape(x)
+    xq = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    nblk = -(-N // int(block_rows))
+    sc = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device) if scales is None else scales
+    st = lib().fa_quantize_fp8(x.data_ptr(), xq.data_ptr(), sc.data_ptr(), B, N, H, d,
+                               int(block_rows), _stream(x))
+    _check(st, "fa_quantize_fp8")
+    return xq, sc
+
+
+def forward_fp8_quantized(q8, k8, v, q_scale, k_scale, causal=False, scale=None, out=None, lse=None):
+    """Forward with FP8 scores from pre-quantised q8 (128-row blocks) and k8
+    (64-row blocks); v bf16 (B, N, H, d). Returns (o, lse)."""
+    torch = _torch()
+    B, N, H, d = _shape(v)
+    for t in (q8, k8):
+        if t.dtype != torch.uint8 or tuple(t.shape) != (B, N, H, d) or not t.is_contiguous():
+            raise ValueError("q8, k8 must be contiguous uint8 tensors shaped like v")
+    o = torch.empty_like(v) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=v.device) if lse is None else lse
+    st = lib().fa_forward_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse_t.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(), B, H, N, d,
+                              _scale(scale, d), int(bool(causal)), _stream(v))
+    _check(st, "fa_forward_fp8")
+    return o, lse_t
+
+
+def forward_fp8(q, k, v, causal=False, scale=None):
+    """Quantises q (per 128 rows) and k (per 64 rows) and runs the FP8-score
+    forward. Returns (o, lse)."""
+    q8, qs = quantize_fp8(q, 128)
+    k8, ks = quantize_fp8(k, 64)
+    return forward_fp8_quantized(q8, k8, v, qs, ks, causal, scale)
 
 
 def dropout_mask(seed, b, h, H, dropout_p, row0, col0, rows, cols, device="cuda"):

@@ -417,6 +417,45 @@ FA_EXPORT int fa_forward_splitkv(const void* q, const void* k, const void* v, vo
   return hip_status(fa::launch_forward_splitkv_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
+// ---------------------------------------------------------------------------
+// FP8 scores.
+FA_EXPORT int fa_quantize_fp8(const void* x, uint8_t* xq, float* scales, int B, int N, int H,
+                              int d, int block_rows, void* stream) {
+  FA_TRY(check_problem(B, H, N, d, FA_BF16));
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (block_rows != 64 && block_rows != 128) return FA_ERR_ARG;
+  FA_TRY(check_ptrs({x, xq, scales}));
+  return hip_status(fa::launch_quantize_fp8(x, xq, scales, B, N, H, d, block_rows,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+FA_EXPORT int fa_forward_fp8(const uint8_t* q8, const uint8_t* k8, const void* v, void* o,
+                             float* lse, const float* q_scale, const float* k_scale, int B, int H,
+                             int N, int d, float scale, int causal, void* stream) {
+  FA_TRY(check_problem(B, H, N, d, FA_BF16));
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  FA_TRY(check_scale(scale));
+  FA_TRY(check_ptrs({q8, k8, v, o, lse}));
+  if (q_scale == nullptr || k_scale == nullptr) return FA_ERR_NULL;
+  if (((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale)) & 3u) != 0)
+    return FA_ERR_ALIGN;
+  fa::AttnArgs a;
+  a.q = q8;
+  a.k = k8;
+  a.v = v;
+  a.o_out = o;
+  a.lse_out = lse;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  return hip_status(fa::launch_forward_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
 FA_EXPORT int fa_dropout_mask(uint64_t seed, int b, int h, int H, float dropout_p, int row0,
                               int col0, int rows, int cols, uint8_t* out, void* stream) {
   FA_TRY(check_dropout(dropout_p));

@@ -41,6 +41,22 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// v_mfma_f32_32x32x64_f8f6f4 with both operands OCP FP8 E4M3 (format code
+// 0): A is 32 x 64, B is 64 x 32, 32 bytes per lane each (a0 then a1). Lane
+// L supplies row (A) or column (B) L % 32; the 32 bytes of lane half L / 32
+// cover 32 consecutive contraction indices, and A and B pair the same
+// indices, so both operands are loaded with one lane -> chunk map. Zero
+// scale operands select the unscaled instruction.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1,
+                                                   f32x16 c) {
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                   (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                   (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // Two floats -> two bf16 (round to nearest even) in one 32-bit word, lo first.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 f = {lo, hi};

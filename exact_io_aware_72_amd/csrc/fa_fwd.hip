@@ -25,6 +25,8 @@
 // a wave skips tiles wholly after its own last query; diagonal tiles are
 // masked per element.
 #include "fa_device.h"
+#include <type_traits>
+
 #include "fa_hash.h"
 #include "fa_kernels.h"
 #include "fa_tile.h"
@@ -54,13 +56,20 @@ struct FwdParams {
   int Nk, nsplit;
   float* ws_o;    // [nsplit][B][H][N][D]
   float* ws_lse;  // [nsplit][B][H][N]
+  // FP8 scores: Q and K as OCP E4M3 bytes [B][N][H][D] with one scale per
+  // 128 query rows ([B][H][ceil(N/128)]) and per 64 key rows
+  // ([B][H][ceil(N/64)]); scores are scale_q * scale_k * (Q8 . K8).
+  const uint8_t* q8;
+  const uint8_t* k8;
+  const float* q_scale;
+  const float* k_scale;
   float c2;  // scale * log2(e)
   uint32_t drop_t;
   float drop_r;
   uint64_t seed;
 };
 
-template <int D>
+template <int D, bool FP8 = false>
 struct FwdCfg {
   static constexpr int NT = 256;                 // 4 waves
   static constexpr int BM = 128;                 // query rows per work-group
@@ -68,16 +77,23 @@ struct FwdCfg {
   static constexpr int NKC = D / 16;             // k-steps of S^T = K Q^T
   static constexpr int DP = (D + 31) / 32 * 32;  // rows of O^T computed (d padded to 32)
   static constexpr int NDB = DP / 32;
-  using KT = Tile<BN, D, Swz::kRow>;             // K tile: 16-byte row reads
+  // K tile: 16-byte row reads. An FP8 row of D bytes is laid out as a bf16
+  // row of D / 2 elements.
+  using KT = typename std::conditional<FP8, Tile<BN, D / 2, Swz::kRow>,
+                                       Tile<BN, D, Swz::kRow>>::type;
   using VT = Tile<BN, D, Swz::kTr>;              // V tile: transposing reads
   static constexpr int STAGE = KT::BYTES + VT::BYTES;
   static constexpr int NLOAD = KT::NLOAD + VT::NLOAD;  // load instructions per tile
   static constexpr int LPW = (NLOAD + 3) / 4;          // per wave
 };
 
-template <int D, bool CAUSAL, bool DROP, bool SPARSE, bool SPLIT>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
-  using C = FwdCfg<D>;
+// At most two waves per SIMD: with the smaller FP8 tiles three work-groups
+// would fit a CU, and the register budget of three waves keeps the compiler
+// from issuing the V reads ahead of the P V products.
+template <int D, bool CAUSAL, bool DROP, bool SPARSE, bool SPLIT, bool FP8>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void fwd_bf16_kernel(
+    FwdParams p) {
+  using C = FwdCfg<D, FP8>;
   using KT = typename C::KT;
   using VT = typename C::VT;
   // Two stages of K and V tiles; separate arrays so that reads of one stage
@@ -89,6 +105,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   __shared__ uint16_t kept[SPARSE ? kSparseMaxBlocks : 1];  // kept key blocks
   static_assert(!SPARSE || C::BM == kSparseBlock, "a work-group covers one mask row");
   static_assert(!(SPLIT && (SPARSE || DROP)), "split-KV runs without dropout or block masks");
+  static_assert(!FP8 || (D == 128 && !SPLIT && !SPARSE && !DROP),
+                "FP8 scores: d = 128, without dropout, block masks or split-KV");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -118,16 +136,38 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
   const int64_t base = sr.base;
   const int64_t kbase = SPLIT ? ((int64_t)b * Nk * H + h) * D : base;
   const uint16_t* Qg = p.q + base;
-  const uint16_t* Kg = p.k + kbase;
   const uint16_t* Vg = p.v + kbase;
   const uint32_t rs2 = (uint32_t)(H * D * 2);  // bytes between consecutive rows
+  // K rows: bf16, or FP8 bytes (one byte per element).
+  const char* Kb = FP8 ? reinterpret_cast<const char*>(p.k8 + kbase)
+                       : reinterpret_cast<const char*>(p.k + kbase);
+  const uint32_t rsk = FP8 ? (uint32_t)(H * D) : rs2;
 
-  // Q operand (B of S^T = K Q^T): 8 d-values per lane per 16-wide chunk;
-  // rows >= N read as zeros through the buffer range check.
-  const BufRes rq = make_bufres(Qg, (uint32_t)N * rs2);
+  // Q operand (B of S^T = K Q^T): 8 d-values per lane per 16-wide chunk
+  // (bf16), or 32 bytes per lane per 64-wide chunk (FP8, in qreg[2c],
+  // qreg[2c+1]); rows >= N read as zeros through the buffer range check.
   u32x4 qreg[C::NKC];
+  float qsc = 1.f;  // FP8: this query block's scale
+  if constexpr (FP8) {
+    const BufRes rq = make_bufres(p.q8 + base, (uint32_t)N * rsk);
 #pragma unroll
-  for (int c = 0; c < C::NKC; ++c) qreg[c] = buf_load_128(rq, (uint32_t)myq * rs2 + (16 * c + 8 * hf) * 2);
+    for (int c = 0; c < D / 64; ++c) {
+      const uint32_t off = (uint32_t)myq * rsk + 64 * c + 32 * hf;
+      qreg[2 * c] = buf_load_128(rq, off);
+      qreg[2 * c + 1] = buf_load_128(rq, off + 16);
+    }
+    qsc = p.q_scale[((int64_t)b * H + h) * nqb + qb];
+  } else {
+    const BufRes rq = make_bufres(Qg, (uint32_t)N * rs2);
+#pragma unroll
+    for (int c = 0; c < C::NKC; ++c)
+      qreg[c] = buf_load_128(rq, (uint32_t)myq * rs2 + (16 * c + 8 * hf) * 2);
+  }
+  // FP8: the key tiles' scales, one per 64 keys; the next tile's is loaded
+  // with its tile (and so has arrived when that tile's loads have).
+  const BufRes rks = make_bufres(FP8 ? p.k_scale + ((int64_t)b * H + h) * ((Nk + 63) / 64) : nullptr,
+                                 FP8 ? (uint32_t)((Nk + 63) / 64) * 4 : 0u);
+  float ksn = 1.f;
 
   uint64_t kbh = 0;
   uint32_t arow = 0;
@@ -172,14 +212,14 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
       VT::load_slot(i - KT::NLOAD, lane, off, row, ch);
       off += KT::BYTES;
     }
-    dsrc[m] = (uint32_t)row * rs2 + 16 * ch;
+    dsrc[m] = (uint32_t)row * (i < KT::NLOAD ? rsk : rs2) + 16 * ch;
     dlds[m] = off;
   }
   auto issue = [&](char* stage, uint32_t* ck, int k0) {
     // Resources start at row k0 and end at row N: rows past N arrive as zeros.
-    const uint32_t left = (uint32_t)(Nk - k0) * rs2;
-    const BufRes rk = make_bufres(Kg + (int64_t)k0 * rs, left);
-    const BufRes rv = make_bufres(Vg + (int64_t)k0 * rs, left);
+    const BufRes rk = make_bufres(Kb + (int64_t)k0 * rsk, (uint32_t)(Nk - k0) * rsk);
+    const BufRes rv = make_bufres(Vg + (int64_t)k0 * rs, (uint32_t)(Nk - k0) * rs2);
+    if constexpr (FP8) ksn = buf_load_f32(rks, (uint32_t)(k0 >> 6) * 4);
 #pragma unroll
     for (int m = 0; m < C::LPW; ++m) {
       const int i = (wave & 3) + 4 * m;
@@ -198,6 +238,13 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) ka[u] = l32 * 128 + (((2 * u) ^ xk) << 4);
   const int ktl = KT::TAIL + l32 * 32 + ((hf ^ KT::swt(l32)) << 4);
+  // FP8: k-step c reads chunks 4c + 2hf + u (u = 0, 1) of row l32; row
+  // l32 + 32 has its swizzle with bit 2 flipped, i.e. k-step c ^ 1's offsets.
+  int fo[2][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) fo[c][u] = l32 * 128 + (((4 * c + 2 * hf + u) ^ KT::sw(l32)) << 4);
   // V: 16-lane group g reads rows 4(g/2) + j (+ 8h + 16kt), columns
   // 16(g%2) + 4a (+ 32db) for lane 4j + a of the group; the uniform part of
   // the swizzle selects one of four precomputed offsets.
@@ -228,12 +275,25 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
     wait_vmem();
     __syncthreads();
     const int k0 = tile_start(t);
+    // Exponent coefficient of this tile (FP8: times the two block scales).
+    const float c2t = FP8 ? c2 * qsc * ksn : c2;
     if (t + 1 < ntiles) issue(nxt, ckn, tile_start(t + 1));
     if (CAUSAL && k0 > qw0 + 31 + coff) return;  // every key is after this wave's queries
     if (SPLIT && qw0 >= N) return;                // no query rows in this wave
 
     // S^T = K Q^T: lane = query, registers = keys (c_row layout).
     f32x16 s0 = f32x16{}, s1 = f32x16{};
+    if constexpr (FP8) {
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c) {
+        const u32x4 x0 = ld_lds_128(cur, fo[c][0]), x1 = ld_lds_128(cur, fo[c][1]);
+        const u32x4 y0 = ld_lds_128(cur, 4096 + fo[c ^ 1][0]);
+        const u32x4 y1 = ld_lds_128(cur, 4096 + fo[c ^ 1][1]);
+        s0 = mfma32x32x64_fp8(x0, x1, qreg[2 * c], qreg[2 * c + 1], s0);
+        s1 = mfma32x32x64_fp8(y0, y1, qreg[2 * c], qreg[2 * c + 1], s1);
+      }
+      sched_lds_ahead<D / 64, 4, 2, 0, 1>();
+    } else {
 #pragma unroll
     for (int c = 0; c < C::NKC; ++c) {
       int o0, o1;
@@ -248,6 +308,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
       s1 = mfma32x32x16(ld_lds_128(cur, o1), qreg[c], s1);
     }
     sched_lds_ahead<C::NKC, 2, 2>();
+    }
     if ((k0 + C::BN > Nk) || (CAUSAL && k0 + C::BN - 1 > qw0 + coff)) {
       const int lim = CAUSAL ? min(myq + coff, Nk - 1) : Nk - 1;  // last visible key
 #pragma unroll
@@ -263,7 +324,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
       ma = fmaxf(fmaxf(ma, s0[r]), s0[r + 1]);
       mb = fmaxf(fmaxf(mb, s1[r]), s1[r + 1]);
     }
-    const float mx = xor32_max(fmaxf(ma, mb)) * c2;
+    const float mx = xor32_max(fmaxf(ma, mb)) * c2t;
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
       const float mnew = fmaxf(m, mx);
       // Rows without a visible key so far (only in a split key range) have
@@ -279,8 +340,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdParams p) {
     const float nm = (SPLIT && m == -INFINITY) ? 0.f : -m;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s0[r] = exp2_hw(fmaf(s0[r], c2, nm));
-      s1[r] = exp2_hw(fmaf(s1[r], c2, nm));
+      s0[r] = exp2_hw(fmaf(s0[r], c2t, nm));
+      s1[r] = exp2_hw(fmaf(s1[r], c2t, nm));
     }
     if constexpr (DROP) {
       // l sums the probabilities before dropout.
@@ -524,7 +585,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
 
 template <int D, bool CAUSAL, bool DROP, bool SPARSE>
 hipError_t launch_fwd_bf16_t(const FwdParams& prm, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROP, SPARSE, false>), dim3(nblocks), dim3(256),
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROP, SPARSE, false, false>), dim3(nblocks), dim3(256),
                      0, s, prm);
   return hipGetLastError();
 }
@@ -610,7 +671,7 @@ hipError_t launch_fwd_f32_d(const FwdParamsF& prm, bool causal, bool drop, int n
 }  // namespace
 
 hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s) {
-  FwdParams prm;
+  FwdParams prm{};
   prm.q = static_cast<const uint16_t*>(a.q);
   prm.k = static_cast<const uint16_t*>(a.k);
   prm.v = static_cast<const uint16_t*>(a.v);
@@ -665,10 +726,10 @@ hipError_t launch_forward_splitkv_bf16(const AttnArgs& a, hipStream_t s) {
 #define FA_SPLIT(D)                                                                          \
   case D:                                                                                    \
     if (a.causal)                                                                            \
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, true, false, false, true>), grid, block, 0, s,  \
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, true, false, false, true, false>), grid, block, 0, s,  \
                          prm);                                                               \
     else                                                                                     \
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, false, false, false, true>), grid, block, 0, s, \
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, false, false, false, true, false>), grid, block, 0, s, \
                          prm);                                                               \
     break;
   switch (a.d) {
@@ -696,6 +757,107 @@ hipError_t launch_forward_splitkv_bf16(const AttnArgs& a, hipStream_t s) {
                          a.split_lse, o, a.lse_out, a.B, a.H, a.N, a.num_splits);
       break;
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-block FP8 quantisation ("FlashAttention for Efficient Training", section
+// 6.2 "Quantization and Mixed-Precision Approaches": scores from quantised
+// queries and keys with scaling factors). One work-group per (b, h, block of
+// R rows): amax = max |x| over the block, codes = E4M3(x * (448 / amax)) with
+// round-to-nearest-even (v_cvt_pk_fp8_f32), scale = amax / 448 (1 for an
+// all-zero block), so that x ~ scale * code.
+template <int D, int R>
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __restrict__ x,
+                                                           uint8_t* __restrict__ xq,
+                                                           float* __restrict__ scales, int N,
+                                                           int H) {
+  constexpr int TPR = 256 / R;  // threads per row
+  constexpr int EPT = D / TPR;  // elements per thread
+  static_assert(EPT % 16 == 0, "whole 16-element groups per thread");
+  __shared__ float wmax[4];
+  const int nblk = (N + R - 1) / R;
+  const int blk = blockIdx.x % nblk;
+  const int bh = blockIdx.x / nblk;
+  const int b = bh / H, h = bh - b * H;
+  const int row = blk * R + (int)threadIdx.x / TPR;
+  const int c0 = ((int)threadIdx.x % TPR) * EPT;
+  const bool ok = row < N;
+  const int64_t off = (((int64_t)b * N + row) * H + h) * D + c0;
+  u32x4 v[EPT / 8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPT / 8; ++i) {
+    v[i] = ok ? ld_global_128(x + off + 8 * i) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[i][j])), fabsf(bf16_hi(v[i][j]))));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float inv = amax > 0.f ? 448.f / amax : 1.f;
+  if (threadIdx.x == 0) scales[(int64_t)bh * nblk + blk] = amax > 0.f ? amax / 448.f : 1.f;
+  if (!ok) return;
+#pragma unroll
+  for (int i = 0; i < EPT / 16; ++i) {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t e0 = v[2 * i + j / 2][2 * (j & 1)], e1 = v[2 * i + j / 2][2 * (j & 1) + 1];
+      int t = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(e0) * inv, bf16_hi(e0) * inv, 0, false);
+      t = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(e1) * inv, bf16_hi(e1) * inv, t, true);
+      w[j] = (uint32_t)t;
+    }
+    *reinterpret_cast<u32x4*>(xq + off + 16 * i) = w;
+  }
+}
+
+hipError_t launch_quantize_fp8(const void* x, uint8_t* xq, float* scales, int B, int N, int H,
+                               int d, int block_rows, hipStream_t s) {
+  if (d != 128) return hipErrorInvalidValue;
+  const int nblk = (N + block_rows - 1) / block_rows;
+  const dim3 grid((unsigned)(nblk * B * H)), block(256);
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  if (block_rows == 128)
+    hipLaunchKernelGGL((quantize_fp8_kernel<128, 128>), grid, block, 0, s, xs, xq, scales, N, H);
+  else if (block_rows == 64)
+    hipLaunchKernelGGL((quantize_fp8_kernel<128, 64>), grid, block, 0, s, xs, xq, scales, N, H);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_forward_fp8(const AttnArgs& a, hipStream_t s) {
+  FwdParams prm{};
+  prm.q = nullptr;
+  prm.k = nullptr;
+  prm.v = static_cast<const uint16_t*>(a.v);
+  prm.o = static_cast<uint16_t*>(a.o_out);
+  prm.lse = a.lse_out;
+  prm.B = a.B;
+  prm.H = a.H;
+  prm.N = a.N;
+  prm.cu = nullptr;
+  prm.total = 0;
+  prm.bmask = nullptr;
+  prm.Nk = a.N;
+  prm.nsplit = 1;
+  prm.q8 = static_cast<const uint8_t*>(a.q);
+  prm.k8 = static_cast<const uint8_t*>(a.k);
+  prm.q_scale = a.q_scale;
+  prm.k_scale = a.k_scale;
+  prm.c2 = a.scale * kLog2e;
+  if (a.d != 128) return hipErrorInvalidValue;
+  const int nblocks = ((a.N + 127) / 128) * a.B * a.H;
+  if (a.causal)
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, true, false, false, false, true>), dim3(nblocks),
+                       dim3(256), 0, s, prm);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, false, false, false, false, true>), dim3(nblocks),
+                       dim3(256), 0, s, prm);
   return hipGetLastError();
 }
 

@@ -47,6 +47,10 @@ struct AttnArgs {
   int Nk = 0, num_splits = 1;
   float* split_o = nullptr;
   float* split_lse = nullptr;
+  // FP8 scores: q and k hold OCP E4M3 bytes; scales per 128 query rows and
+  // per 64 key rows ([B][H][blocks]).
+  const float* q_scale = nullptr;
+  const float* k_scale = nullptr;
   float scale = 0.f;
   bool causal = false;
   bool dropout = false;
@@ -58,6 +62,9 @@ struct AttnArgs {
 hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_forward_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_forward_splitkv_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_forward_fp8(const AttnArgs& a, hipStream_t s);
+hipError_t launch_quantize_fp8(const void* x, uint8_t* xq, float* scales, int B, int N, int H,
+                               int d, int block_rows, hipStream_t s);
 hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t s, bool bf16);
 hipError_t launch_bwd_dkdv_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const AttnArgs& a, hipStream_t s);

@@ -221,6 +221,30 @@ int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, flo
                        int causal, int num_splits, void* stream, int dtype);
 
 /*
+ * FP8 scores ("FlashAttention for Efficient Training", section 6.2,
+ * "Quantization and Mixed-Precision Approaches": Q K^T ~ S_Q * Q8 * K8^T * S_K
+ * with quantised queries and keys and their scaling factors). Q K^T runs on
+ * the FP8 matrix cores; the softmax, P V (bf16) and outputs are as in
+ * fa_forward. An inference path: forward only, no dropout, d = 128.
+ *
+ * fa_quantize_fp8: x bf16 [B][N][H][d] -> xq OCP FP8 E4M3 bytes [B][N][H][d]
+ *   and scales fp32 [B][H][ceil(N / block_rows)], block_rows 128 (queries) or
+ *   64 (keys). Per (b, h, block): amax = max |x|, scale = amax / 448 (1 for
+ *   an all-zero block), xq = E4M3(x * (448 / amax)) rounded to nearest even,
+ *   all in fp32.
+ * fa_forward_fp8: q8, k8 from fa_quantize_fp8 (block_rows 128 and 64), v bf16
+ *   [B][N][H][d]; o bf16 and lse fp32 as fa_forward. Scores are
+ *   scale * q_scale[b][h][i / 128] * k_scale[b][h][j / 64] * (q8_i . k8_j).
+ * Errors as for fa_forward; FA_ERR_UNSUPPORTED for d != 128; FA_ERR_ARG for
+ * another block_rows. Scale arrays need 4-byte alignment.
+ */
+int fa_quantize_fp8(const void* x, uint8_t* xq, float* scales, int B, int N, int H, int d,
+                    int block_rows, void* stream);
+int fa_forward_fp8(const uint8_t* q8, const uint8_t* k8, const void* v, void* o, float* lse,
+                   const float* q_scale, const float* k_scale, int B, int H, int N, int d,
+                   float scale, int causal, void* stream);
+
+/*
  * Writes the dropout keep mask of head (b, h) for rows row0..row0+rows-1 and
  * columns col0..col0+cols-1 to out[rows][cols] (device, 1 = keep), with the
  * same device function the kernels use. The pages fuse dropout into the

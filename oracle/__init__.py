@@ -12,6 +12,8 @@ Contents:
                    SplitMix64 and MurmurHash3 finalizers
   varlen.py        the same attention over packed batches of sequences of
                    different lengths
+  fp8.py           OCP E4M3 per-block quantisation and attention with
+                   quantised scores
 
 Parity status: every function here is pinned by tests under tests/ against
 closed forms, invariants, brute force and finite differences, except the
