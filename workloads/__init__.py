@@ -47,6 +47,7 @@ __all__ = [
     "SplitKVWorkload",
     "SPLITKV_WORKLOADS",
     "make_cross_inputs",
+    "device_normal",
 ]
 
 
@@ -304,3 +305,15 @@ def make_cross_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, seed
     for name in ("k", "v"):
         out[name] = make_tensor(rng, (B, Nk, H, d), amp, dtype)
     return out
+
+
+def device_normal(shape, seed: int, dtype: str = "bf16", device: str = "cuda"):
+    """A standard normal tensor drawn on the device by torch's Philox
+    generator seeded with `seed` (float32 draws, then rounded to bf16 with
+    round-to-nearest-even), for shapes too large to draw on the host. The
+    same seed gives the same tensor on any run of the same torch build."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    return x.to(torch.bfloat16) if dtype == "bf16" else x
