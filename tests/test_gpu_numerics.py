@@ -1,0 +1,128 @@
+"""GPU parity on inputs that stress the online softmax: monotone logits
+(every key scores higher than the one before, so the running maximum keeps
+rising and the forward's rescale of O and l is taken repeatedly), peaked
+softmax (Q and K scaled x8, nearly one-hot rows), and logits shifted by a
+large constant (the max subtraction must absorb it). Forward and backward
+against the fp64 oracle on the same stored values.
+
+These inputs give K and Q large norms (keys of norm ~170 in the monotone
+case, a constant 40 in one key column, x8 scaling), and dQ = scale dS K,
+dK = scale dS^T Q multiply any error of D by those norms. D is formed from the
+stored bf16 O, so dQ and dK are held to the bf16 bar plus the bound that this
+rounding propagates to them (see _stored_o_bounds); O, LSE and dV to the bar
+scaled by magnitude above 1."""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import assert_close, to_device, to_host
+from workloads import Workload, f32_to_bf16_bits, bf16_bits_to_f32, make_inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import exact_io_aware_72_amd as fa  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _bf16(x):
+    bits = f32_to_bf16_bits(np.asarray(x, np.float32))
+    return bits, bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _stored_o_bounds(q, k, v, do, scale, causal):
+    """Extra error of dQ and dK that comes from forming D = rowsum(dO * O)
+    from the stored bf16 O (as fa_backward does, O being its input) instead of
+    the exact O: each stored O element is off by up to 2^-9 of itself
+    (2^-8 taken, to cover the forward's own rounding), so D_i is off by
+    dD_i <= 2^-8 sum_c |dO_ic O_ic|; dS_ij = P_ij (dP_ij - D_i) then carries
+    -P_ij dD_i, which gives dQ_i an error up to scale dD_i |(P K)_i| and dK_j
+    one up to scale sum_i P_ij dD_i |Q_i|. Computed from oracle values only."""
+    B, N, H, d = q.shape
+    eq = np.zeros(q.shape)
+    ek = np.zeros(k.shape)
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh, doh = q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h]
+            s = oracle.attention_scores(qh, kh, scale, causal)
+            _, _, lse = oracle.softmax_stats(s)
+            p = oracle.attention_probs(s, lse)
+            o = p @ vh
+            dd = 2.0 ** -8 * np.sum(np.abs(doh * o), axis=1) + 1e-4
+            eq[b, :, h] = scale * dd[:, None] * np.abs(p @ kh)
+            ek[b, :, h] = scale * (p * dd[:, None]).T @ np.abs(qh)
+    return eq, ek
+
+
+def _check(name, got, ref, extra):
+    """The bf16 bar scaled by magnitude above 1, plus `extra` per element;
+    the mean bar likewise plus the mean of `extra`."""
+    err = np.abs(got - ref)
+    bound = 2e-2 * np.maximum(1.0, np.abs(ref)) + extra
+    worst = float(np.max(err / bound))
+    assert worst <= 1.0, f"{name}: max|err|/bound = {worst:.3f} (max|err| {err.max():.3e})"
+    assert err.mean() <= 1e-3 + extra.mean(), f"{name}: mean|err| {err.mean():.3e}"
+
+
+def _run_and_check(q, k, v, do, scale, causal, dtype="bf16"):
+    dev = {n: to_device(x[0], dtype) for n, x in (("q", q), ("k", k), ("v", v), ("do", do))}
+    o, lse = fa.forward(dev["q"], dev["k"], dev["v"], causal, 0.0, 0, scale)
+    dq, dk, dv = fa.backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal, 0.0, 0, scale)
+    torch.cuda.synchronize()
+    o_r, lse_r = oracle.forward(q[1], k[1], v[1], scale, causal)
+    dq_r, dk_r, dv_r, _ = oracle.backward(q[1], k[1], v[1], do[1], scale, causal)
+    assert_close("O", to_host(o), o_r, dtype, scaled=True)
+    assert_close("LSE", to_host(lse), lse_r, dtype, scaled=True)
+    assert_close("dV", to_host(dv), dv_r, dtype, scaled=True)
+    eq, ek = _stored_o_bounds(q[1], k[1], v[1], do[1], scale, causal)
+    _check("dQ", to_host(dq), dq_r, eq)
+    _check("dK", to_host(dk), dk_r, ek)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 80, 128])
+def test_monotone_logits(causal, d):
+    """Q_i = a u and K_j = (j eps) u for a unit vector u: score_ij grows
+    linearly with j up to about 60 at the last key, crossing the rescale
+    threshold of the forward (2^8 in base 2) many times per row."""
+    B, N, H = 1, 700, 2
+    rng = np.random.default_rng(11 + d)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    a = 4.0
+    eps = 60.0 / (N * a * scale)
+    q = np.broadcast_to(a * u, (B, N, H, d)).copy()
+    k = (np.arange(N)[:, None] * eps * u[None, :])[None, :, None, :].repeat(H, axis=2)
+    v = rng.standard_normal((B, N, H, d))
+    do = rng.standard_normal((B, N, H, d))
+    _run_and_check(_bf16(q), _bf16(k), _bf16(v), _bf16(do), scale, causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_peaked_softmax(causal):
+    """Q and K scaled x8: logits with a standard deviation near 64, so most
+    rows put almost all their weight on one key."""
+    w = Workload(70, "peak", 1, 2, 300, 128, "bf16", causal, 0.0, True)
+    inp = make_inputs(w, with_grad=True)
+    q = _bf16(inp["q"][1] * 8.0)
+    k = _bf16(inp["k"][1] * 8.0)
+    _run_and_check(q, k, inp["v"], inp["do"], w.scale, causal)
+
+
+def test_large_common_shift():
+    """Query column 0 set to 16 and key column 0 to 40: every logit of a row
+    gains the same scale * 16 * 40 = 80, which the softmax ignores but the
+    running maximum must absorb without overflow or loss."""
+    w = Workload(71, "shift", 1, 2, 257, 64, "bf16", True, 0.0, True)
+    inp = make_inputs(w, with_grad=True)
+    q = inp["q"][1].copy()
+    k = inp["k"][1].copy()
+    q[..., 0] = 16.0
+    k[..., 0] = 40.0
+    _run_and_check(_bf16(q), _bf16(k), inp["v"], inp["do"], w.scale, True)
