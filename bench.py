@@ -304,14 +304,20 @@ def run_gpu_fp8(cfg, steps, warmup, torch, fa):
 
 
 def kernel_source_digest():
-    """SHA-256 over the kernel sources and the build flags: HBM traffic
-    figures recorded under profiles/ are valid only for this digest."""
+    """SHA-256 over the kernel sources (comments and blank lines removed, so
+    that only code counts) and the build flags: HBM traffic figures recorded
+    under profiles/ are valid only for this digest."""
     import hashlib
+    import re
     from exact_io_aware_72_amd import build as fa_build
     h = hashlib.sha256()
     for name in sorted(os.listdir(fa_build.CSRC)):
-        with open(os.path.join(fa_build.CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(fa_build.CSRC, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(name.encode() + b"\0" + code.encode())
     h.update(" ".join(f for f in fa_build.COMMON_FLAGS if not f.startswith("/")).encode())
     return h.hexdigest()
 

@@ -1,6 +1,7 @@
-// Device helpers for the gfx950 attention kernels: vector types, the bf16
-// matrix-core instruction, LDS/global 128-bit accesses, bf16 packing, and the
-// contraction-index permutation that lets a score tile held in accumulator
+// Device helpers for the gfx950 attention kernels: vector types, the bf16 and
+// FP8 matrix-core instructions, LDS/global accesses, bf16 packing, lane
+// exchanges, scheduling hints, sequence/block bookkeeping, and the
+// contraction-index relabelling that lets a score tile held in accumulator
 // registers feed the next matrix product without going through LDS.
 //
 // Matrix-core layout used throughout (v_mfma_f32_32x32x16_bf16, wave64):
@@ -13,8 +14,8 @@
 // unchanged. A C tile therefore serves directly as the B operand of a product
 // that contracts over its row index, provided the A operand is read with the
 // same relabelling: for the 16 rows 16t..16t+15 of a C tile, lane half s
-// supplies rows {16t + 4s + 0..3, 16t + 8 + 4s + 0..3}; LDS copies that feed
-// the matching A operand store those 8 rows contiguously (perm_pos below).
+// supplies rows {16t + 4s + 0..3, 16t + 8 + 4s + 0..3} (c_row below), and the
+// transposing LDS reads that build the matching A operand fetch those rows.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -102,18 +103,6 @@ __device__ __forceinline__ void st_global_64(void* p, u32x2 v) {
 __device__ __forceinline__ u32x4 ld_lds_128(const char* base, int off) {
   return *reinterpret_cast<const u32x4*>(base + off);
 }
-__device__ __forceinline__ void st_lds_128(char* base, int off, u32x4 v) {
-  *reinterpret_cast<u32x4*>(base + off) = v;
-}
-__device__ __forceinline__ void st_lds_64(char* base, int off, u32x2 v) {
-  *reinterpret_cast<u32x2*>(base + off) = v;
-}
-__device__ __forceinline__ f32x4 ld_lds_f32x4(const char* base, int off) {
-  return *reinterpret_cast<const f32x4*>(base + off);
-}
-__device__ __forceinline__ u32x4 ld_lds_u32x4(const char* base, int off) {
-  return *reinterpret_cast<const u32x4*>(base + off);
-}
 
 // Exchange between lane L and lane L ^ 32 without LDS (v_permlane32_swap):
 // swapping x with itself leaves {x_L, x_(L^32)} in the two results, in the
@@ -126,21 +115,6 @@ __device__ __forceinline__ float xor32_max(float x) {
 __device__ __forceinline__ float xor32_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Staging item for a tile that is stored both row-major and transposed.
-// Item `it` covers rows 4g..4g+3 of the tile and the 16-byte column chunk c.
-// Consecutive items take consecutive g (so the 8-byte transposed writes of
-// one LDS pass land in distinct banks) and a chunk skewed by g (so the
-// row-major 16-byte writes of one pass do too).
-struct StageItem {
-  int g, c;
-};
-__device__ __forceinline__ StageItem stage_item(int it, int ngroups, int nchunks) {
-  StageItem s;
-  s.g = it % ngroups;
-  s.c = (it / ngroups + s.g) % nchunks;
-  return s;
 }
 
 // Scheduling hint for a fully unrolled loop of `steps` steps, each issuing
@@ -165,32 +139,6 @@ __device__ __forceinline__ void sched_lds_ahead() {
 
 // Row index within a 32-row C tile held by accumulator register r of lane half s.
 __device__ __forceinline__ constexpr int c_row(int r, int s) { return 8 * (r >> 2) + 4 * s + (r & 3); }
-
-// Position in a permuted LDS copy of the first of 4 consecutive contraction
-// indices 4g..4g+3: within each group of 16, the 4-blocks are stored in the
-// order 0, 2, 1, 3 so that lane half s reads its 8 indices as one 16-byte run
-// starting at 16t + 8s.
-__device__ __forceinline__ int perm_pos4(int g) {
-  const int q = g & 3;
-  const int qp = (q == 1) ? 2 : (q == 2) ? 1 : q;
-  return ((g >> 2) << 4) | (qp << 2);
-}
-
-// Transposing store: four 16-byte rows (rows 4g..4g+3 of a tile, 8 columns
-// 8c..8c+7 each, bf16) written as 8 columns of a column-major copy:
-// dst[(8c + e) * stride + pos*2 .. +8] = {row0[e], row1[e], row2[e], row3[e]}.
-__device__ __forceinline__ void st_lds_transpose4x8(char* base, int row_bytes, int col0, int pos,
-                                                    const u32x4& r0, const u32x4& r1,
-                                                    const u32x4& r2, const u32x4& r3) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t a = r0[w], b = r1[w], c = r2[w], d = r3[w];
-    const u32x2 even = {(a & 0xffffu) | (b << 16), (c & 0xffffu) | (d << 16)};
-    const u32x2 odd = {(a >> 16) | (b & 0xffff0000u), (c >> 16) | (d & 0xffff0000u)};
-    st_lds_64(base, (col0 + 2 * w) * row_bytes + pos * 2, even);
-    st_lds_64(base, (col0 + 2 * w + 1) * row_bytes + pos * 2, odd);
-  }
-}
 
 // Rows of one (sequence, head) pair: the sequence length, the element offset
 // of its first row in the [.., H, d] tensors, and the offset of its first
