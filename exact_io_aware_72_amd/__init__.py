@@ -143,6 +143,23 @@ def _shape(q, *others):
     return B, N, H, d
 
 
+def _buf(t, shape, dtype, like, name):
+    """A caller-supplied buffer: the kernels trust its size, so shape, dtype,
+    device and contiguity are checked here."""
+    if (tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != like.device
+            or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"on {like.device} (got {tuple(t.shape)}, {t.dtype}, {t.device})")
+    return t
+
+
+def _out(t, shape, dtype, like, name):
+    """`t` checked as above, or a new tensor if None."""
+    if t is None:
+        return _torch().empty(tuple(shape), dtype=dtype, device=like.device)
+    return _buf(t, shape, dtype, like, name)
+
+
 def _stream(t):
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
@@ -156,9 +173,8 @@ def forward(q, k, v, causal=False, dropout_p=0.0, seed=0, scale=None, out=None, 
     """Returns (o, lse): o like q; lse float32 (B, H, N), natural log."""
     torch = _torch()
     B, N, H, d = _shape(q, k, v)
-    o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _shape(q, o)
+    o = _out(out, q.shape, q.dtype, q, "out")
+    lse_t = _out(lse, (B, H, N), torch.float32, q, "lse")
     st = lib().fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
                           B, H, N, d, _scale(scale, d), int(bool(causal)), float(dropout_p),
                           int(seed), _stream(q), _code(q))
@@ -171,10 +187,11 @@ def backward(q, k, v, o, dout, lse, causal=False, dropout_p=0.0, seed=0, scale=N
     """Returns (dq, dk, dv) for L = sum(dout * o)."""
     torch = _torch()
     B, N, H, d = _shape(q, k, v, o, dout)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
-    ws = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if workspace is None else workspace
+    _buf(lse, (B, H, N), torch.float32, q, "lse")
+    dq = _out(dq, q.shape, q.dtype, q, "dq")
+    dk = _out(dk, q.shape, q.dtype, q, "dk")
+    dv = _out(dv, q.shape, q.dtype, q, "dv")
+    ws = _out(workspace, (B, H, N), torch.float32, q, "workspace")
     st = lib().fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                            ws.data_ptr(), B, H, N, d, _scale(scale, d), int(bool(causal)),
@@ -187,7 +204,7 @@ def backward_preprocess(o, dout, workspace=None):
     """Step B1 alone: returns D = rowsum(dout * o) as float32 (B, H, N)."""
     torch = _torch()
     B, N, H, d = _shape(o, dout)
-    ws = torch.empty((B, H, N), dtype=torch.float32, device=o.device) if workspace is None else workspace
+    ws = _out(workspace, (B, H, N), torch.float32, o, "workspace")
     st = lib().fa_backward_preprocess(o.data_ptr(), dout.data_ptr(), ws.data_ptr(), B, H, N, d,
                                       _stream(o), _code(o))
     _check(st, "fa_backward_preprocess")
@@ -199,8 +216,10 @@ def backward_dkdv(q, k, v, dout, lse, workspace, causal=False, dropout_p=0.0, se
     """Step B2 alone: returns (dk, dv)."""
     torch = _torch()
     B, N, H, d = _shape(q, k, v, dout)
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    _buf(lse, (B, H, N), torch.float32, q, "lse")
+    _buf(workspace, (B, H, N), torch.float32, q, "workspace")
+    dk = _out(dk, q.shape, q.dtype, q, "dk")
+    dv = _out(dv, q.shape, q.dtype, q, "dv")
     st = lib().fa_backward_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
                                 lse.data_ptr(), workspace.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                 B, H, N, d, _scale(scale, d), int(bool(causal)), float(dropout_p),
@@ -214,7 +233,9 @@ def backward_dq(q, k, v, dout, lse, workspace, causal=False, dropout_p=0.0, seed
     """Step B3 alone: returns dq."""
     torch = _torch()
     B, N, H, d = _shape(q, k, v, dout)
-    dq = torch.empty_like(q) if dq is None else dq
+    _buf(lse, (B, H, N), torch.float32, q, "lse")
+    _buf(workspace, (B, H, N), torch.float32, q, "workspace")
+    dq = _out(dq, q.shape, q.dtype, q, "dq")
     st = lib().fa_backward_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
                               lse.data_ptr(), workspace.data_ptr(), dq.data_ptr(), B, H, N, d,
                               _scale(scale, d), int(bool(causal)), float(dropout_p), int(seed),
@@ -260,9 +281,8 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, dropout_p=0.0,
     torch = _torch()
     total, H, d = _shape_varlen(q, k, v)
     nseq = _cu(cu_seqlens, q)
-    o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((H, total), dtype=torch.float32, device=q.device) if lse is None else lse
-    _shape_varlen(q, o)
+    o = _out(out, q.shape, q.dtype, q, "out")
+    lse_t = _out(lse, (H, total), torch.float32, q, "lse")
     st = lib().fa_forward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                  lse_t.data_ptr(), cu_seqlens.data_ptr(), nseq, total,
                                  int(max_seqlen), H, d, _scale(scale, d), int(bool(causal)),
@@ -277,10 +297,11 @@ def backward_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen, causal=False,
     torch = _torch()
     total, H, d = _shape_varlen(q, k, v, o, dout)
     nseq = _cu(cu_seqlens, q)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
-    ws = torch.empty((H, total), dtype=torch.float32, device=q.device) if workspace is None else workspace
+    _buf(lse, (H, total), torch.float32, q, "lse")
+    dq = _out(dq, q.shape, q.dtype, q, "dq")
+    dk = _out(dk, q.shape, q.dtype, q, "dk")
+    dv = _out(dv, q.shape, q.dtype, q, "dv")
+    ws = _out(workspace, (H, total), torch.float32, q, "workspace")
     st = lib().fa_backward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                   dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                   dv.data_ptr(), ws.data_ptr(), cu_seqlens.data_ptr(), nseq, total,
@@ -320,9 +341,8 @@ def forward_blocksparse(q, k, v, block_mask, causal=False, dropout_p=0.0, seed=0
     torch = _torch()
     B, N, H, d = _shape(q, k, v)
     mp, sb, sh = _mask_args(block_mask, q, B, H, N)
-    o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _shape(q, o)
+    o = _out(out, q.shape, q.dtype, q, "out")
+    lse_t = _out(lse, (B, H, N), torch.float32, q, "lse")
     st = lib().fa_forward_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                       lse_t.data_ptr(), mp, sb, sh, B, H, N, d, _scale(scale, d),
                                       int(bool(causal)), float(dropout_p), int(seed), _stream(q),
@@ -337,10 +357,11 @@ def backward_blocksparse(q, k, v, o, dout, lse, block_mask, causal=False, dropou
     torch = _torch()
     B, N, H, d = _shape(q, k, v, o, dout)
     mp, sb, sh = _mask_args(block_mask, q, B, H, N)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
-    ws = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if workspace is None else workspace
+    _buf(lse, (B, H, N), torch.float32, q, "lse")
+    dq = _out(dq, q.shape, q.dtype, q, "dq")
+    dk = _out(dk, q.shape, q.dtype, q, "dk")
+    dv = _out(dv, q.shape, q.dtype, q, "dv")
+    ws = _out(workspace, (B, H, N), torch.float32, q, "workspace")
     st = lib().fa_backward_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                        dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                        dv.data_ptr(), ws.data_ptr(), mp, sb, sh, B, H, N, d,
@@ -373,12 +394,14 @@ def forward_splitkv(q, k, v, causal=False, num_splits=0, scale=None, out=None, l
     ns = int(num_splits) if num_splits else splitkv_num_splits(B, H, Nq, Nk, d)
     if ns < 1:
         raise FAError(-2, "fa_forward_splitkv", "invalid shape")
-    o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _shape(q, o)
+    o = _out(out, q.shape, q.dtype, q, "out")
+    lse_t = _out(lse, (B, H, Nq), torch.float32, q, "lse")
+    nbytes = splitkv_workspace_bytes(B, H, Nq, d, ns)
     if workspace is None:
-        nbytes = splitkv_workspace_bytes(B, H, Nq, d, ns)
         workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
+    elif (workspace.dtype != torch.float32 or workspace.device != q.device
+          or not workspace.is_contiguous() or workspace.numel() * 4 < nbytes):
+        raise ValueError(f"workspace must be a contiguous float32 GPU tensor of >= {nbytes} bytes")
     st = lib().fa_forward_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                   lse_t.data_ptr(), workspace.data_ptr(), B, H, Nq, Nk, d,
                                   _scale(scale, d), int(bool(causal)), ns, _stream(q), _code(q))
@@ -392,9 +415,9 @@ def quantize_fp8(x, block_rows, out=None, scales=None):
     """x bf16 (B, N, H, d) -> (uint8 codes like x, float32 scales (B, H, nblk))."""
     torch = _torch()
     B, N, H, d = _shape(x)
-    xq = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    xq = _out(out, x.shape, torch.uint8, x, "out")
     nblk = -(-N // int(block_rows))
-    sc = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device) if scales is None else scales
+    sc = _out(scales, (B, H, nblk), torch.float32, x, "scales")
     st = lib().fa_quantize_fp8(x.data_ptr(), xq.data_ptr(), sc.data_ptr(), B, N, H, d,
                                int(block_rows), _stream(x))
     _check(st, "fa_quantize_fp8")
@@ -406,11 +429,12 @@ def forward_fp8_quantized(q8, k8, v, q_scale, k_scale, causal=False, scale=None,
     (64-row blocks); v bf16 (B, N, H, d). Returns (o, lse)."""
     torch = _torch()
     B, N, H, d = _shape(v)
-    for t in (q8, k8):
-        if t.dtype != torch.uint8 or tuple(t.shape) != (B, N, H, d) or not t.is_contiguous():
-            raise ValueError("q8, k8 must be contiguous uint8 tensors shaped like v")
-    o = torch.empty_like(v) if out is None else out
-    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=v.device) if lse is None else lse
+    _buf(q8, v.shape, torch.uint8, v, "q8")
+    _buf(k8, v.shape, torch.uint8, v, "k8")
+    _buf(q_scale, (B, H, -(-N // 128)), torch.float32, v, "q_scale")
+    _buf(k_scale, (B, H, -(-N // 64)), torch.float32, v, "k_scale")
+    o = _out(out, v.shape, v.dtype, v, "out")
+    lse_t = _out(lse, (B, H, N), torch.float32, v, "lse")
     st = lib().fa_forward_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), o.data_ptr(),
                               lse_t.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(), B, H, N, d,
                               _scale(scale, d), int(bool(causal)), _stream(v))
