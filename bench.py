@@ -33,6 +33,7 @@ from workloads import (SPARSE_WORKLOADS, SPLITKV_WORKLOADS, VARLEN_WORKLOADS, WO
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 matrix-core peak (published)
 METRIC = "attention fwd+bwd TFLOP/s & % of bf16 MFMA peak, causal, N=8K/32K"
 
 
@@ -109,6 +110,11 @@ def run_gpu(w, steps, warmup, torch, fa):
     }
 
 
+def _mfma_roofline(tflops):
+    return {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / PEAK_BF16_TFLOPS}
+
+
 def run_gpu_varlen(wv, steps, warmup, torch, fa):
     """Packed variable-length batch: forward_varlen + backward_varlen per step,
     FLOPs counted per sequence. Also times the same sequences padded to the
@@ -160,6 +166,7 @@ def run_gpu_varlen(wv, steps, warmup, torch, fa):
         / PEAK_BF16_TFLOPS,
         "fwd_tflops": fwd_f / (fwd_ms * 1e-3) / 1e12, "bwd_tflops": bwd_f / (bwd_ms * 1e-3) / 1e12,
         "padded_fixed_length_ms_per_step": rp["ms_per_step"],
+        "roofline": _mfma_roofline((fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12),
     }
 
 
@@ -224,6 +231,7 @@ def run_gpu_sparse(name, steps, warmup, torch, fa):
         / PEAK_BF16_TFLOPS,
         "fwd_tflops": fwd_f / (fwd_ms * 1e-3) / 1e12, "bwd_tflops": bwd_f / (bwd_ms * 1e-3) / 1e12,
         "dense_ms_per_step": rd["ms_per_step"],
+        "roofline": _mfma_roofline((fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12),
     }
 
 
@@ -298,7 +306,13 @@ def run_gpu_fp8(cfg, steps, warmup, torch, fa):
     ms_fp8 = timed(lambda: fa.forward_fp8_quantized(q8, k8, v, qs, ks, w.causal, w.scale, out=o,
                                                     lse=lse))
     ms_bf16 = timed(lambda: fa.forward(q, k, v, w.causal, 0.0, 0, w.scale, out=o, lse=lse))
+    # QK^T runs on the FP8 matrix cores (5.0 PFLOP/s dense), P V on bf16 (2.5):
+    # half the counted forward FLOPs each, so the bound is 2 / (1/5 + 1/2.5).
+    peak_mixed = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
+    tf8 = fwd_f / (ms_fp8 * 1e-3) / 1e12
     return {"workload": w.name + "_fp8_scores_fwd", "forward_fp8_ms": ms_fp8,
+            "roofline": {"bound": "mfma", "achieved": tf8, "peak": peak_mixed, "unit": "TFLOP/s",
+                         "frac": tf8 / peak_mixed},
             "forward_fp8_tflops": fwd_f / (ms_fp8 * 1e-3) / 1e12, "quantize_q_k_ms": ms_quant,
             "forward_bf16_ms": ms_bf16, "forward_bf16_tflops": fwd_f / (ms_bf16 * 1e-3) / 1e12}
 
