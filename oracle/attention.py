@@ -1,7 +1,7 @@
 """Plain fp64 exact attention, forward and backward, on the CPU.
 
-Test infrastructure only (see the package docstring). This is the
-"standard attention" of the pages, written out: it materialises the score
+Test infrastructure only (see the package docstring). This is the standard
+(unfused) attention the pages compare against, written out: it materialises the score
 matrix S and the probability matrix P (as described in "How FlashAttention
 Optimizes GPU Memory for Fast AI Training", section "The Flaw in Standard
 Attention"), row panel by row panel so that long sequences fit in host memory.
@@ -31,7 +31,7 @@ Definitions followed ("FlashAttention for Efficient Training" unless noted):
     with Z the keep mask of dropout_hash.py; the row statistics use the
     undropped P
   * dV = P~^T dO (section 3.2 "Integration with Autograd Engines"); dQ and dK
-    "by the chain rule" (same section):
+    follow from the chain rule, which the same section leaves to the reader:
         dP~ = dO V^T,  dP = dP~ * Z / (1 - p),  D_i = sum_j P_ij dP_ij,
         dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
     D_i also equals sum_c dO_ic O_ic; both are computed and must agree.
