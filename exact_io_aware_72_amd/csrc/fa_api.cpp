@@ -422,7 +422,6 @@ FA_EXPORT int fa_forward_splitkv(const void* q, const void* k, const void* v, vo
 FA_EXPORT int fa_quantize_fp8(const void* x, uint8_t* xq, float* scales, int B, int N, int H,
                               int d, int block_rows, void* stream) {
   FA_TRY(check_problem(B, H, N, d, FA_BF16));
-  if (d != 128) return FA_ERR_UNSUPPORTED;
   if (block_rows != 64 && block_rows != 128) return FA_ERR_ARG;
   FA_TRY(check_ptrs({x, xq, scales}));
   return hip_status(fa::launch_quantize_fp8(x, xq, scales, B, N, H, d, block_rows,
@@ -433,7 +432,6 @@ FA_EXPORT int fa_forward_fp8(const uint8_t* q8, const uint8_t* k8, const void* v
                              float* lse, const float* q_scale, const float* k_scale, int B, int H,
                              int N, int d, float scale, int causal, void* stream) {
   FA_TRY(check_problem(B, H, N, d, FA_BF16));
-  if (d != 128) return FA_ERR_UNSUPPORTED;
   FA_TRY(check_scale(scale));
   FA_TRY(check_ptrs({q8, k8, v, o, lse}));
   if (q_scale == nullptr || k_scale == nullptr) return FA_ERR_NULL;

@@ -77,10 +77,8 @@ struct FwdCfg {
   static constexpr int NKC = D / 16;             // k-steps of S^T = K Q^T
   static constexpr int DP = (D + 31) / 32 * 32;  // rows of O^T computed (d padded to 32)
   static constexpr int NDB = DP / 32;
-  // K tile: 16-byte row reads. An FP8 row of D bytes is laid out as a bf16
-  // row of D / 2 elements.
-  using KT = typename std::conditional<FP8, Tile<BN, D / 2, Swz::kRow>,
-                                       Tile<BN, D, Swz::kRow>>::type;
+  // K tile: 16-byte row reads (bf16, or FP8 bytes).
+  using KT = typename std::conditional<FP8, Fp8Tile<BN, D>, Tile<BN, D, Swz::kRow>>::type;
   using VT = Tile<BN, D, Swz::kTr>;              // V tile: transposing reads
   static constexpr int STAGE = KT::BYTES + VT::BYTES;
   static constexpr int NLOAD = KT::NLOAD + VT::NLOAD;  // load instructions per tile
@@ -105,8 +103,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   __shared__ uint16_t kept[SPARSE ? kSparseMaxBlocks : 1];  // kept key blocks
   static_assert(!SPARSE || C::BM == kSparseBlock, "a work-group covers one mask row");
   static_assert(!(SPLIT && (SPARSE || DROP)), "split-KV runs without dropout or block masks");
-  static_assert(!FP8 || (D == 128 && !SPLIT && !SPARSE && !DROP),
-                "FP8 scores: d = 128, without dropout, block masks or split-KV");
+  static_assert(!FP8 || (!SPLIT && !SPARSE && !DROP),
+                "FP8 scores run without dropout, block masks or split-KV");
+  constexpr int NK8 = (D + 63) / 64;  // FP8: 64-wide contraction steps of S^T = K Q^T
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -151,11 +150,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   if constexpr (FP8) {
     const BufRes rq = make_bufres(p.q8 + base, (uint32_t)N * rsk);
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c) {
-      const uint32_t off = (uint32_t)myq * rsk + 64 * c + 32 * hf;
-      qreg[2 * c] = buf_load_128(rq, off);
-      qreg[2 * c + 1] = buf_load_128(rq, off + 16);
-    }
+    for (int c = 0; c < NK8; ++c)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        // chunks past D (D = 80) read as zeros through an out-of-range offset
+        const int ch = 4 * c + 2 * hf + u;
+        qreg[2 * c + u] = buf_load_128(rq, ch < KT::VALID ? (uint32_t)myq * rsk + 16 * ch : 0x80000000u);
+      }
     qsc = p.q_scale[((int64_t)b * H + h) * nqb + qb];
   } else {
     const BufRes rq = make_bufres(Qg, (uint32_t)N * rs2);
@@ -213,6 +214,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       off += KT::BYTES;
     }
     dsrc[m] = (uint32_t)row * (i < KT::NLOAD ? rsk : rs2) + 16 * ch;
+    if constexpr (FP8) {
+      // Chunks past D in a padded FP8 row: an offset beyond every buffer
+      // range makes the load return zeros.
+      if (i < KT::NLOAD && ch >= KT::VALID) dsrc[m] = 0x80000000u;
+    }
     dlds[m] = off;
   }
   auto issue = [&](char* stage, uint32_t* ck, int k0) {
@@ -234,17 +240,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   // K rows l32 (scores s0) and l32 + 32 (s1), chunk 2c + hf: the swizzle of
   // row l32 + 32 is that of row l32 with bit 2 flipped.
   const int xk = hf ^ KT::sw(l32);
-  int ka[4];
+  int ka[4] = {0, 0, 0, 0};
+  int ktl = 0;
+  if constexpr (!FP8) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) ka[u] = l32 * 128 + (((2 * u) ^ xk) << 4);
-  const int ktl = KT::TAIL + l32 * 32 + ((hf ^ KT::swt(l32)) << 4);
-  // FP8: k-step c reads chunks 4c + 2hf + u (u = 0, 1) of row l32; row
-  // l32 + 32 has its swizzle with bit 2 flipped, i.e. k-step c ^ 1's offsets.
-  int fo[2][2];
+    for (int u = 0; u < 4; ++u) ka[u] = l32 * 128 + (((2 * u) ^ xk) << 4);
+    ktl = KT::TAIL + l32 * 32 + ((hf ^ KT::swt(l32)) << 4);
+  }
+  // FP8: 64-wide k-step c reads chunks 4c + 2hf + u (u = 0, 1) of rows l32
+  // (fo) and l32 + 32 (fo2).
+  int fo[NK8][2], fo2[NK8][2];
+  if constexpr (FP8) {
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < NK8; ++c)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) fo[c][u] = l32 * 128 + (((4 * c + 2 * hf + u) ^ KT::sw(l32)) << 4);
+      for (int u = 0; u < 2; ++u) {
+        fo[c][u] = KT::off(l32, 4 * c + 2 * hf + u);
+        fo2[c][u] = KT::off(l32 + 32, 4 * c + 2 * hf + u);
+      }
+  }
   // V: 16-lane group g reads rows 4(g/2) + j (+ 8h + 16kt), columns
   // 16(g%2) + 4a (+ 32db) for lane 4j + a of the group; the uniform part of
   // the swizzle selects one of four precomputed offsets.
@@ -285,14 +299,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     f32x16 s0 = f32x16{}, s1 = f32x16{};
     if constexpr (FP8) {
 #pragma unroll
-      for (int c = 0; c < D / 64; ++c) {
+      for (int c = 0; c < NK8; ++c) {
         const u32x4 x0 = ld_lds_128(cur, fo[c][0]), x1 = ld_lds_128(cur, fo[c][1]);
-        const u32x4 y0 = ld_lds_128(cur, 4096 + fo[c ^ 1][0]);
-        const u32x4 y1 = ld_lds_128(cur, 4096 + fo[c ^ 1][1]);
+        const u32x4 y0 = ld_lds_128(cur, fo2[c][0]), y1 = ld_lds_128(cur, fo2[c][1]);
         s0 = mfma32x32x64_fp8(x0, x1, qreg[2 * c], qreg[2 * c + 1], s0);
         s1 = mfma32x32x64_fp8(y0, y1, qreg[2 * c], qreg[2 * c + 1], s1);
       }
-      sched_lds_ahead<D / 64, 4, 2, 0, 1>();
+      sched_lds_ahead<NK8, 4, 2, 0, 1>();
     } else {
 #pragma unroll
     for (int c = 0; c < C::NKC; ++c) {
@@ -772,26 +785,34 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __res
                                                            uint8_t* __restrict__ xq,
                                                            float* __restrict__ scales, int N,
                                                            int H) {
-  constexpr int TPR = 256 / R;  // threads per row
-  constexpr int EPT = D / TPR;  // elements per thread
-  static_assert(EPT % 16 == 0, "whole 16-element groups per thread");
+  // Work in 16-element chunks (32 bytes in, 16 bytes out): chunk c of the
+  // block is row c / CPR, columns 16 (c % CPR) ..; thread t takes chunks
+  // t, t + 256, ...
+  constexpr int CPR = D / 16;
+  constexpr int NCH = R * CPR;
+  constexpr int PER = (NCH + 255) / 256;
   __shared__ float wmax[4];
   const int nblk = (N + R - 1) / R;
   const int blk = blockIdx.x % nblk;
   const int bh = blockIdx.x / nblk;
   const int b = bh / H, h = bh - b * H;
-  const int row = blk * R + (int)threadIdx.x / TPR;
-  const int c0 = ((int)threadIdx.x % TPR) * EPT;
-  const bool ok = row < N;
-  const int64_t off = (((int64_t)b * N + row) * H + h) * D + c0;
-  u32x4 v[EPT / 8];
+  u32x4 v[PER][2];
+  int64_t off[PER];
+  bool ok[PER];
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < EPT / 8; ++i) {
-    v[i] = ok ? ld_global_128(x + off + 8 * i) : u32x4{0, 0, 0, 0};
+  for (int i = 0; i < PER; ++i) {
+    const int c = (int)threadIdx.x + 256 * i;
+    const int row = blk * R + c / CPR;
+    ok[i] = c < NCH && row < N;
+    off[i] = (((int64_t)b * N + row) * H + h) * D + 16 * (c % CPR);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[i][j])), fabsf(bf16_hi(v[i][j]))));
+    for (int j = 0; j < 2; ++j) {
+      v[i][j] = ok[i] ? ld_global_128(x + off[i] + 8 * j) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[i][j][e])), fabsf(bf16_hi(v[i][j][e]))));
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
@@ -800,33 +821,42 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __res
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const float inv = amax > 0.f ? 448.f / amax : 1.f;
   if (threadIdx.x == 0) scales[(int64_t)bh * nblk + blk] = amax > 0.f ? amax / 448.f : 1.f;
-  if (!ok) return;
 #pragma unroll
-  for (int i = 0; i < EPT / 16; ++i) {
+  for (int i = 0; i < PER; ++i) {
+    if (!ok[i]) continue;
     u32x4 w;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t e0 = v[2 * i + j / 2][2 * (j & 1)], e1 = v[2 * i + j / 2][2 * (j & 1) + 1];
+    for (int q = 0; q < 4; ++q) {  // output word q: elements 4q .. 4q + 3
+      const uint32_t e0 = v[i][q / 2][2 * (q & 1)], e1 = v[i][q / 2][2 * (q & 1) + 1];
       int t = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(e0) * inv, bf16_hi(e0) * inv, 0, false);
       t = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(e1) * inv, bf16_hi(e1) * inv, t, true);
-      w[j] = (uint32_t)t;
+      w[q] = (uint32_t)t;
     }
-    *reinterpret_cast<u32x4*>(xq + off + 16 * i) = w;
+    *reinterpret_cast<u32x4*>(xq + off[i]) = w;
   }
+}
+
+template <int D>
+void launch_quantize_fp8_d(const uint16_t* xs, uint8_t* xq, float* scales, int N, int H,
+                           int block_rows, dim3 grid, hipStream_t s) {
+  if (block_rows == 128)
+    hipLaunchKernelGGL((quantize_fp8_kernel<D, 128>), grid, dim3(256), 0, s, xs, xq, scales, N, H);
+  else
+    hipLaunchKernelGGL((quantize_fp8_kernel<D, 64>), grid, dim3(256), 0, s, xs, xq, scales, N, H);
 }
 
 hipError_t launch_quantize_fp8(const void* x, uint8_t* xq, float* scales, int B, int N, int H,
                                int d, int block_rows, hipStream_t s) {
-  if (d != 128) return hipErrorInvalidValue;
+  if (block_rows != 128 && block_rows != 64) return hipErrorInvalidValue;
   const int nblk = (N + block_rows - 1) / block_rows;
-  const dim3 grid((unsigned)(nblk * B * H)), block(256);
+  const dim3 grid((unsigned)(nblk * B * H));
   const uint16_t* xs = static_cast<const uint16_t*>(x);
-  if (block_rows == 128)
-    hipLaunchKernelGGL((quantize_fp8_kernel<128, 128>), grid, block, 0, s, xs, xq, scales, N, H);
-  else if (block_rows == 64)
-    hipLaunchKernelGGL((quantize_fp8_kernel<128, 64>), grid, block, 0, s, xs, xq, scales, N, H);
-  else
-    return hipErrorInvalidValue;
+  switch (d) {
+    case 64: launch_quantize_fp8_d<64>(xs, xq, scales, N, H, block_rows, grid, s); break;
+    case 80: launch_quantize_fp8_d<80>(xs, xq, scales, N, H, block_rows, grid, s); break;
+    case 128: launch_quantize_fp8_d<128>(xs, xq, scales, N, H, block_rows, grid, s); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -850,14 +880,23 @@ hipError_t launch_forward_fp8(const AttnArgs& a, hipStream_t s) {
   prm.q_scale = a.q_scale;
   prm.k_scale = a.k_scale;
   prm.c2 = a.scale * kLog2e;
-  if (a.d != 128) return hipErrorInvalidValue;
-  const int nblocks = ((a.N + 127) / 128) * a.B * a.H;
-  if (a.causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, true, false, false, false, true>), dim3(nblocks),
-                       dim3(256), 0, s, prm);
-  else
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, false, false, false, false, true>), dim3(nblocks),
-                       dim3(256), 0, s, prm);
+  const dim3 grid((unsigned)(((a.N + 127) / 128) * a.B * a.H)), block(256);
+#define FA_FP8(D)                                                                            \
+  case D:                                                                                    \
+    if (a.causal)                                                                            \
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, true, false, false, false, true>), grid, block, 0, \
+                         s, prm);                                                            \
+    else                                                                                     \
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, false, false, false, false, true>), grid, block, \
+                         0, s, prm);                                                         \
+    break;
+  switch (a.d) {
+    FA_FP8(64)
+    FA_FP8(80)
+    FA_FP8(128)
+    default: return hipErrorInvalidValue;
+  }
+#undef FA_FP8
   return hipGetLastError();
 }
 

@@ -71,6 +71,39 @@ struct Tile {
   }
 };
 
+// LDS tile of R rows of D FP8 bytes (one byte per element), for 16-byte row
+// reads (matrix-core operands along D). Rows are 64 bytes (D = 64) or 128
+// bytes (D = 80 or 128; the chunks past D are filled with zeros); the chunk
+// position is XOR-swizzled by the row so that the 16 lanes of one LDS pass
+// (16 consecutive rows, one chunk column) hit 16 distinct 16-byte bank
+// groups: (r ^ r >> 3) & 7 for 8-chunk rows as in Tile<.., kRow>, (r >> 2) & 3
+// for 4-chunk rows (rows r, r + 4, r + 8, r + 12 share a bank group base).
+template <int R, int D>
+struct Fp8Tile {
+  static_assert(D == 64 || D == 80 || D == 128, "head dim must be 64, 80 or 128");
+  static constexpr int RB = D == 64 ? 64 : 128;  // LDS bytes per row
+  static constexpr int CPR = RB / 16;             // chunks per row
+  static constexpr int VALID = (D + 15) / 16;     // chunks holding data
+  static constexpr int BYTES = R * RB;
+  static constexpr int RPL = 64 / CPR;            // rows per load instruction
+  static_assert(R % RPL == 0, "whole load instructions");
+  static constexpr int NLOAD = R / RPL;
+
+  __device__ __forceinline__ static int sw(int r) {
+    return CPR == 8 ? ((r ^ (r >> 3)) & 7) : ((r >> 2) & 3);
+  }
+  // Load instruction i: LDS byte offset (uniform), and the row and chunk
+  // this lane fetches; chunk >= VALID must be fetched as zeros.
+  __device__ __forceinline__ static void load_slot(int i, int lane, int& lds_off, int& row,
+                                                   int& chunk) {
+    row = i * RPL + lane / CPR;
+    chunk = (lane % CPR) ^ sw(row);
+    lds_off = i * 1024;
+  }
+  // Byte offset of chunk c of row r.
+  __device__ __forceinline__ static int off(int r, int c) { return r * RB + ((c ^ sw(r)) << 4); }
+};
+
 // Direct global->LDS load of 16 bytes per lane: lane L's data lands at
 // lds + 16 * L. `lds` must be the same for the whole wave.
 __device__ __forceinline__ void lds_dma_16(BufRes r, void* lds, uint32_t voff) {

@@ -225,7 +225,7 @@ int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, flo
  * "Quantization and Mixed-Precision Approaches": Q K^T ~ S_Q * Q8 * K8^T * S_K
  * with quantised queries and keys and their scaling factors). Q K^T runs on
  * the FP8 matrix cores; the softmax, P V (bf16) and outputs are as in
- * fa_forward. An inference path: forward only, no dropout, d = 128.
+ * fa_forward. An inference path: forward only, no dropout; d = 64, 80, 128.
  *
  * fa_quantize_fp8: x bf16 [B][N][H][d] -> xq OCP FP8 E4M3 bytes [B][N][H][d]
  *   and scales fp32 [B][H][ceil(N / block_rows)], block_rows 128 (queries) or
@@ -235,8 +235,9 @@ int fa_forward_splitkv(const void* q, const void* k, const void* v, void* o, flo
  * fa_forward_fp8: q8, k8 from fa_quantize_fp8 (block_rows 128 and 64), v bf16
  *   [B][N][H][d]; o bf16 and lse fp32 as fa_forward. Scores are
  *   scale * q_scale[b][h][i / 128] * k_scale[b][h][j / 64] * (q8_i . k8_j).
- * Errors as for fa_forward; FA_ERR_UNSUPPORTED for d != 128; FA_ERR_ARG for
- * another block_rows. Scale arrays need 4-byte alignment.
+ * Errors as for fa_forward; FA_ERR_ARG for another block_rows. Scale arrays
+ * need 4-byte alignment. xq rows of d bytes must be 16-byte aligned like the
+ * other tensors (d is a multiple of 16).
  */
 int fa_quantize_fp8(const void* x, uint8_t* xq, float* scales, int B, int N, int H, int d,
                     int block_rows, void* stream);

@@ -236,7 +236,7 @@ def test_splitkv_rejects_and_sizes():
 def test_fp8_rejects():
     L = fa.lib()
     assert L.fa_quantize_fp8(0, P, P, 1, 16, 1, 128, 128, None) == NULL
-    assert L.fa_quantize_fp8(P, P, P, 1, 16, 1, 64, 128, None) == UNSUP
+    assert L.fa_quantize_fp8(P, P, P, 1, 16, 1, 96, 128, None) == HEADDIM
     assert L.fa_quantize_fp8(P, P, P, 1, 16, 1, 128, 32, None) == ARG
     assert L.fa_quantize_fp8(P, P, P, 1, 0, 1, 128, 128, None) == SHAPE
     args = [P] * 7 + [1, 2, 300, 128, 0.1, 1, None]
@@ -244,8 +244,8 @@ def test_fp8_rejects():
     assert L.fa_forward_fp8(*a) == NULL         # q_scale
     a = list(args); a[6] = P + 2
     assert L.fa_forward_fp8(*a) == ALIGN        # k_scale
-    a = list(args); a[10] = 64
-    assert L.fa_forward_fp8(*a) == UNSUP        # d != 128
+    a = list(args); a[10] = 96
+    assert L.fa_forward_fp8(*a) == HEADDIM      # d not in {64, 80, 128}
     a = list(args); a[11] = 0.0
     assert L.fa_forward_fp8(*a) == ARG          # scale
     a = list(args); a[0] = 0

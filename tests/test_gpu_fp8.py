@@ -1,7 +1,8 @@
 """GPU parity for the FP8-score forward: the quantisation kernel's E4M3 codes
 and block scales bit for bit against the oracle's fp32 rule, and the forward
 against the fp64 oracle on the same quantised inputs (bf16 bar), causal and
-full, with ragged tails; the full-size N=8192 shape at sampled rows."""
+full, with ragged tails, for head dims 64, 80 (rows padded to 128 bytes in
+LDS) and 128; the full-size N=8192 shape at sampled rows."""
 import numpy as np
 import pytest
 
@@ -34,10 +35,11 @@ def _decode_table():
     return t
 
 
+@pytest.mark.parametrize("d", [64, 80, 128])
 @pytest.mark.parametrize("block_rows", [128, 64])
 @pytest.mark.parametrize("amp", [1.0, 1e-3, 300.0])
-def test_quantize_matches_oracle_bitwise(block_rows, amp):
-    w = Workload(60, "q8", 2, 3, 300, 128, "bf16", False, 0.0, False, amp=amp)
+def test_quantize_matches_oracle_bitwise(d, block_rows, amp):
+    w = Workload(60, "q8", 2, 3, 300, d, "bf16", False, 0.0, False, amp=amp)
     inp = make_inputs(w, with_grad=False)
     stored, vals = inp["q"]
     vals = vals.copy()
@@ -53,15 +55,17 @@ def test_quantize_matches_oracle_bitwise(block_rows, amp):
     np.testing.assert_array_equal(sc.cpu().numpy(), scales)
 
 
-CASES = [(1, 2, 300, True), (2, 1, 77, False), (1, 3, 1000, True), (1, 1, 1, True),
-         (1, 2, 513, False), (2, 2, 130, True)]
+CASES = [(1, 2, 300, True, 128), (2, 1, 77, False, 128), (1, 3, 1000, True, 128),
+         (1, 1, 1, True, 128), (1, 2, 513, False, 128), (2, 2, 130, True, 128),
+         (1, 2, 300, True, 64), (2, 1, 257, False, 64), (1, 2, 700, True, 80),
+         (1, 1, 129, False, 80), (1, 1, 1, True, 80)]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}H{c[1]}N{c[2]}-{'causal' if c[3] else 'full'}"
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}H{c[1]}N{c[2]}-{'causal' if c[3] else 'full'}-d{c[4]}"
                                              for c in CASES])
 def test_forward_fp8_matches_oracle(case):
-    B, H, N, causal = case
-    w = Workload(61, "f8", B, H, N, 128, "bf16", causal, 0.0, False)
+    B, H, N, causal, d = case
+    w = Workload(61, "f8", B, H, N, d, "bf16", causal, 0.0, False)
     inp = make_inputs(w, with_grad=False)
     dev = {k: to_device(v[0], "bf16") for k, v in inp.items()}
     o, lse = fa.forward_fp8(dev["q"], dev["k"], dev["v"], causal, w.scale)
