@@ -53,10 +53,13 @@ int check_dropout(float p) {
 // needs scale > 0 (the pages' scale is 1/sqrt(d)).
 int check_scale(float scale) { return (std::isfinite(scale) && scale > 0.0f) ? FA_OK : FA_ERR_ARG; }
 
+// Keep threshold T = floor(p * 2^16) on the 16-bit draws; p < 1 keeps T <= 65535.
+uint32_t drop_threshold16(float p) { return (uint32_t)std::floor((double)p * 65536.0); }
+
 void set_dropout(fa::AttnArgs& a, float p, uint64_t seed) {
   a.dropout = p > 0.0f;
   a.seed = seed;
-  a.drop_threshold = (uint32_t)std::floor((double)p * 4294967296.0);
+  a.drop_threshold = drop_threshold16(p);
   a.drop_rescale = (float)(1.0 / (1.0 - (double)p));
 }
 
@@ -462,7 +465,7 @@ FA_EXPORT int fa_dropout_mask(uint64_t seed, int b, int h, int H, float dropout_
     return FA_ERR_ARG;
   if ((int64_t)rows * cols >= ((int64_t)1 << 31)) return FA_ERR_ARG;
   if ((int64_t)row0 + rows > INT32_MAX || (int64_t)col0 + cols > INT32_MAX) return FA_ERR_ARG;
-  const uint32_t thr = (uint32_t)std::floor((double)dropout_p * 4294967296.0);
+  const uint32_t thr = drop_threshold16(dropout_p);
   return hip_status(fa::launch_dropout_mask(seed, b, h, H, thr, row0, col0, rows, cols, out,
                                             static_cast<hipStream_t>(stream)));
 }

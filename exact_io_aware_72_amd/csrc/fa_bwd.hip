@@ -273,11 +273,20 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
   for (int u = 0; u < 4; ++u) vrow[u] = vr * 128 + (((2 * u) ^ vx) << 4);
   const int vrow_tail = VB::TAIL + vr * 32 + ((hf ^ VB::swt(vr)) << 4);
 
+  // Dropout: lanes 2c and 2c + 1 hold the two keys of one pair (mykey is
+  // kw0 + l32 with kw0 even) over the same query rows, so one hash serves
+  // both. Each lane of the two hashes two of every four rows (even lane rows
+  // 0, 1, odd lane rows 2, 3) and passes the 16-bit draws of its partner's
+  // key across; byte selectors pick the halves: own = this key's draws of the
+  // two rows, send = the partner key's.
   uint64_t kbh = 0;
-  uint32_t bcol = 0;
+  uint32_t bpair = 0, sel_own = 0, sel_send = 0;
+  const bool odd = (lane & 1) != 0;
   if constexpr (DROP) {
     kbh = head_key(p.seed, b, h, H);
-    bcol = col_key(kbh, mykey);
+    bpair = pair_key(kbh, mykey >> 1);
+    sel_own = odd ? 0x07060302u : 0x05040100u;  // high (odd key) or low (even key) halves
+    sel_send = odd ? 0x05040100u : 0x07060302u;
   }
 
   const int qstart = CAUSAL ? k0 : 0;
@@ -393,8 +402,20 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
           const int g = 2 * kt + gg;
           const f32x4 l2 = *reinterpret_cast<const f32x4*>(lsc + 8 * g + 4 * hf);
           const f32x4 dd = *reinterpret_cast<const f32x4*>(ddc + 8 * g + 4 * hf);
-          u32x4 ar = {0, 0, 0, 0};
-          if constexpr (DROP) ar = *reinterpret_cast<const u32x4*>(arc + 8 * g + 4 * hf);
+          // Dropout draws of rows 8g + 4hf + e: e = 0, 1 in dr01, e = 2, 3 in
+          // dr23 (low half, high half).
+          uint32_t dr01 = 0, dr23 = 0;
+          if constexpr (DROP) {
+            const u32x2 ar = *reinterpret_cast<const u32x2*>(arc + 8 * g + 4 * hf + (odd ? 2 : 0));
+            uint32_t fa = pair_mix(ar[0], bpair), fb = pair_mix(ar[1], bpair);
+            fa ^= fa >> 16;  // fmix32: low half the even key's draw, high half the odd key's
+            fb ^= fb >> 16;
+            const uint32_t own = __builtin_amdgcn_perm(fb, fa, sel_own);
+            const uint32_t send = __builtin_amdgcn_perm(fb, fa, sel_send);
+            const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+            dr01 = odd ? recv : own;
+            dr23 = odd ? own : recv;
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
@@ -402,9 +423,11 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
             float dpv = dp[r];
             float ptv = pv;
             if constexpr (DROP) {
-              const bool kp = keep(ar[e], bcol, p.drop_t);
-              ptv = kp ? pv * p.drop_r : 0.f;
-              dpv = kp ? dpv * p.drop_r : 0.f;
+              const uint32_t dw = e < 2 ? dr01 : dr23;
+              const bool kp = (e & 1) ? dw >= (p.drop_t << 16) : (dw & 0xFFFFu) >= p.drop_t;
+              const float mr = kp ? p.drop_r : 0.f;
+              ptv = pv * mr;
+              dpv *= mr;
             }
             pt[4 * gg + e] = ptv;
             dsv[4 * gg + e] = pv * (dpv - dd[e]);
@@ -489,8 +512,8 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
   using VT = typename C::VT;
   __shared__ __align__(16) char st0[C::STAGE];
   __shared__ __align__(16) char st1[C::STAGE];
-  __shared__ __align__(16) uint32_t bc0[DROP ? C::BK : 1];
-  __shared__ __align__(16) uint32_t bc1[DROP ? C::BK : 1];
+  __shared__ __align__(16) uint32_t bc0[DROP ? C::BK / 2 : 1];  // dropout keys of the tile's key pairs
+  __shared__ __align__(16) uint32_t bc1[DROP ? C::BK / 2 : 1];
   __shared__ uint16_t kept[SPARSE ? kSparseMaxBlocks : 1];  // kept key blocks
   static_assert(!SPARSE || C::BQ == kSparseBlock, "a work-group covers one mask row");
 
@@ -579,7 +602,7 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
       if (i < C::NLOAD) lds_dma_16(i < KT::NLOAD ? rk : rv, stage + dlds[m], dsrc[m]);
     }
     if constexpr (DROP) {
-      if (tid < C::BK) bc[tid] = col_key(kbh, k0 + tid);
+      if (tid < C::BK / 2) bc[tid] = pair_key(kbh, (k0 >> 1) + tid);
     }
   };
 
@@ -617,8 +640,14 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
         const int g = 2 * kt + gg;
-        u32x4 bc = {0, 0, 0, 0};
-        if constexpr (DROP) bc = *reinterpret_cast<const u32x4*>(bcc + 8 * g + 4 * hf);
+        // Registers 4g + e hold keys 8g + 4hf + e; keys (e, e + 1), e = 0, 2,
+        // are a pair and share one dropout hash.
+        uint32_t yd[2] = {0, 0};
+        if constexpr (DROP) {
+          const u32x2 bc = *reinterpret_cast<const u32x2*>(bcc + 4 * g + 2 * hf);
+          yd[0] = pair_mix(arow, bc[0]);
+          yd[1] = pair_mix(arow, bc[1]);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
@@ -628,7 +657,10 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
             if (key >= N || (CAUSAL && key > myq)) pv = 0.f;
           }
           float dpv = dp[r];
-          if constexpr (DROP) dpv = keep(arow, bc[e], p.drop_t) ? dpv * p.drop_r : 0.f;
+          if constexpr (DROP) {
+            const bool kp = (e & 1) ? keep_odd(yd[e >> 1], p.drop_t) : keep_even(yd[e >> 1], p.drop_t);
+            dpv = kp ? dpv * p.drop_r : 0.f;
+          }
           dsv[4 * gg + e] = pv * (dpv - dq_d);
         }
       }
@@ -706,10 +738,10 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdParams p) {
     dv[c] = 0.f;
   }
   uint64_t kbh = 0;
-  uint32_t bcol = 0;
+  uint32_t bpair = 0;
   if constexpr (DROP) {
     kbh = head_key(p.seed, b, h, H);
-    bcol = col_key(kbh, mykey);
+    bpair = pair_key(kbh, mykey >> 1);
   }
   const int qstart = CAUSAL ? k0 : 0;
   const int nb = (N + kSparseBlock - 1) / kSparseBlock;
@@ -753,7 +785,7 @@ __global__ __launch_bounds__(128) void bwd_dkdv_f32_kernel(BwdParams p) {
       if (CAUSAL && mykey > q) pv = 0.f;
       float ptv = pv;
       if constexpr (DROP) {
-        const bool kp = keep(ars[i], bcol, p.drop_t);
+        const bool kp = keep_key(pair_mix(ars[i], bpair), mykey, p.drop_t);
         ptv = kp ? pv * p.drop_r : 0.f;
         dpv = kp ? dpv * p.drop_r : 0.f;
       }
@@ -781,7 +813,7 @@ __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdParams p) {
   constexpr int BQW = 32, BK = 16, DQ = D / 4;
   __shared__ __align__(16) float ks[BK][D];
   __shared__ __align__(16) float vs[BK][D];
-  __shared__ uint32_t bcs[BK];
+  __shared__ uint32_t bcs[BK / 2];  // dropout keys of the tile's key pairs
 
   const int tid = threadIdx.x;
   const int qi = tid >> 2, part = tid & 3;
@@ -839,7 +871,7 @@ __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdParams p) {
       *reinterpret_cast<f32x4*>(&vs[r][c]) = vx;
     }
     if constexpr (DROP) {
-      if (tid < BK) bcs[tid] = col_key(kbh, k0 + tid);
+      if (tid < BK / 2) bcs[tid] = pair_key(kbh, (k0 >> 1) + tid);
     }
     __syncthreads();
 #pragma unroll 4
@@ -857,7 +889,7 @@ __global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdParams p) {
       const int key = k0 + j;
       float pv = exp2_hw(sv * p.c2 - lse2);
       if (key >= N || (CAUSAL && key > myq)) pv = 0.f;
-      if constexpr (DROP) dpv = keep(arow, bcs[j], p.drop_t) ? dpv * p.drop_r : 0.f;
+      if constexpr (DROP) dpv = keep_key(pair_mix(arow, bcs[j >> 1]), j, p.drop_t) ? dpv * p.drop_r : 0.f;
       const float dsv = pv * (dpv - dd);
 #pragma unroll
       for (int c = 0; c < DQ; ++c) dq[c] = fmaf(dsv, ks[j][part * DQ + c], dq[c]);
@@ -879,7 +911,8 @@ __global__ __launch_bounds__(256) void dropout_mask_kernel(uint64_t seed, int b,
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * 256) {
     const int r = (int)(i / cols), c = (int)(i - (int64_t)r * cols);
-    out[i] = keep(row_key(kbh, row0 + r), col_key(kbh, col0 + c), thr) ? 1 : 0;
+    const int j = col0 + c;
+    out[i] = keep_key(pair_mix(row_key(kbh, row0 + r), pair_key(kbh, j >> 1)), j, thr) ? 1 : 0;
   }
 }
 

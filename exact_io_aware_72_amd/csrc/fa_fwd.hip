@@ -98,8 +98,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   // only wait for the loads into that stage.
   __shared__ __align__(16) char st0[C::STAGE];
   __shared__ __align__(16) char st1[C::STAGE];
-  __shared__ __align__(16) uint32_t ck0[DROP ? C::BN : 1];
-  __shared__ __align__(16) uint32_t ck1[DROP ? C::BN : 1];
+  __shared__ __align__(16) uint32_t ck0[DROP ? C::BN / 2 : 1];  // dropout keys of the tile's key pairs
+  __shared__ __align__(16) uint32_t ck1[DROP ? C::BN / 2 : 1];
   __shared__ uint16_t kept[SPARSE ? kSparseMaxBlocks : 1];  // kept key blocks
   static_assert(!SPARSE || C::BM == kSparseBlock, "a work-group covers one mask row");
   static_assert(!(SPLIT && (SPARSE || DROP)), "split-KV runs without dropout or block masks");
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       if (i < C::NLOAD) lds_dma_16(i < KT::NLOAD ? rk : rv, stage + dlds[m], dsrc[m]);
     }
     if constexpr (DROP) {
-      if (tid < C::BN) ck[tid] = col_key(kbh, k0 + tid);
+      if (tid < C::BN / 2) ck[tid] = pair_key(kbh, (k0 >> 1) + tid);
     }
   };
 
@@ -365,14 +365,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         ps1 += s1[r];
       }
       l += ps0 + ps1;
+      // Register 4g + e holds key 8g + 4hf + e: keys (e, e + 1) for e = 0, 2
+      // are a pair and share one hash.
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const u32x4 c0 = *reinterpret_cast<const u32x4*>(ckc + 8 * g + 4 * hf);
-        const u32x4 c1 = *reinterpret_cast<const u32x4*>(ckc + 32 + 8 * g + 4 * hf);
+        const u32x2 c0 = *reinterpret_cast<const u32x2*>(ckc + 4 * g + 2 * hf);
+        const u32x2 c1 = *reinterpret_cast<const u32x2*>(ckc + 16 + 4 * g + 2 * hf);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s0[4 * g + e] = keep(arow, c0[e], p.drop_t) ? s0[4 * g + e] : 0.f;
-          s1[4 * g + e] = keep(arow, c1[e], p.drop_t) ? s1[4 * g + e] : 0.f;
+        for (int e = 0; e < 4; e += 2) {
+          const uint32_t y0 = pair_mix(arow, c0[e >> 1]);
+          const uint32_t y1 = pair_mix(arow, c1[e >> 1]);
+          s0[4 * g + e] = keep_even(y0, p.drop_t) ? s0[4 * g + e] : 0.f;
+          s0[4 * g + e + 1] = keep_odd(y0, p.drop_t) ? s0[4 * g + e + 1] : 0.f;
+          s1[4 * g + e] = keep_even(y1, p.drop_t) ? s1[4 * g + e] : 0.f;
+          s1[4 * g + e + 1] = keep_odd(y1, p.drop_t) ? s1[4 * g + e + 1] : 0.f;
         }
       }
     }
@@ -492,7 +498,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
   constexpr int BM = 64, BN = 16, DH = D / 2;
   __shared__ __align__(16) float ks[BN][D];
   __shared__ __align__(16) float vs[BN][D];
-  __shared__ uint32_t bk[BN];
+  __shared__ uint32_t bk[BN / 2];  // dropout keys of the tile's key pairs
 
   const int tid = threadIdx.x;
   const int qi = tid >> 1, part = tid & 1;
@@ -546,7 +552,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
       *reinterpret_cast<f32x4*>(&vs[r][c]) = vx;
     }
     if constexpr (DROP) {
-      if (tid < BN) bk[tid] = col_key(kbh, k0 + tid);
+      if (tid < BN / 2) bk[tid] = pair_key(kbh, (k0 >> 1) + tid);
     }
     __syncthreads();
     float s[BN];
@@ -574,7 +580,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
       psum += pv;
       s[j] = pv;
       if constexpr (DROP) {
-        if (!keep(arow, bk[j], p.drop_t)) s[j] = 0.f;
+        if (!keep_key(pair_mix(arow, bk[j >> 1]), j, p.drop_t)) s[j] = 0.f;
       }
     }
     l = l * alpha + psum;

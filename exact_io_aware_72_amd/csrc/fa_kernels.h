@@ -54,7 +54,7 @@ struct AttnArgs {
   float scale = 0.f;
   bool causal = false;
   bool dropout = false;
-  uint32_t drop_threshold = 0;  // keep iff hash >= threshold
+  uint32_t drop_threshold = 0;  // keep iff the 16-bit draw >= threshold
   float drop_rescale = 1.f;     // 1 / (1 - p) in fp32
   uint64_t seed = 0;
 };

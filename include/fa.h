@@ -253,8 +253,11 @@ int fa_forward_fp8(const uint8_t* q8, const uint8_t* k8, const void* v, void* o,
  *   G = 0x9E3779B97F4A7C15;  mix64 = SplitMix64 output function;
  *   fmix32 = MurmurHash3 32-bit finalizer;
  *   K_bh = mix64(seed + G*(1 + b*H + h));
- *   A_i = lo32(mix64(K_bh + G*(2i+1)));  B_j = lo32(mix64(K_bh + G*(2j+2)));
- *   keep(i, j) = fmix32(A_i ^ B_j) >= floor(dropout_p * 2^32)   (all mod 2^64 / 2^32).
+ *   A_i = lo32(mix64(K_bh + G*(2i+1)));  B_c = lo32(mix64(K_bh + G*(2c+2)));
+ *   w = fmix32(A_i ^ B_c), whose low 16 bits are the draw u_ij of column j = 2c
+ *   and whose high 16 bits that of j = 2c + 1   (all mod 2^64 / 2^32);
+ *   keep(i, j) = u_ij >= floor(dropout_p * 2^16), a keep probability within
+ *   2^-16 of 1 - dropout_p.
  * Requires 0 <= b, 0 <= h < H, row0, col0 >= 0, rows, cols >= 1,
  * rows * cols < 2^31, out non-NULL (any alignment).
  */

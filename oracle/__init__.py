@@ -35,7 +35,8 @@ from .dropout_hash import (  # noqa: F401
     fmix32,
     head_key,
     row_keys,
-    col_keys,
+    pair_keys,
+    uniforms16,
     keep_threshold,
     keep_mask,
 )

@@ -19,13 +19,16 @@ same mask from a seed instead of storing N x N bits:
                 x ^= x >> 16
   K_bh      = mix64(seed + G * (1 + b*H + h))
   A_i       = low 32 bits of mix64(K_bh + G * (2*i + 1))     (one per query row)
-  B_j       = low 32 bits of mix64(K_bh + G * (2*j + 2))     (one per key column)
-  w_ij      = fmix32(A_i XOR B_j)
-  T         = floor(p * 2^32), p taken as the float32 value the kernel receives
-  keep_ij   = (w_ij >= T)
+  B_c       = low 32 bits of mix64(K_bh + G * (2*c + 2))     (one per pair of key
+              columns j = 2c, 2c + 1)
+  w_ic      = fmix32(A_i XOR B_c)
+  u_ij      = low 16 bits of w_ic for even j, high 16 bits for odd j
+  T         = floor(p * 2^16), p taken as the float32 value the kernel receives
+  keep_ij   = (u_ij >= T)
 
-The keep probability is exactly 1 - T / 2^32. Kept probabilities are scaled
-by 1 / (1 - p).
+One hash thus gives the draws of two neighbouring keys of a row, each a
+16-bit uniform; the keep probability is exactly 1 - T / 2^16, within 2^-16 of
+1 - p. Kept probabilities are scaled by 1 / (1 - p).
 """
 from __future__ import annotations
 
@@ -81,23 +84,30 @@ def row_keys(key: int, rows):
     return _keyed(key, rows, 1)
 
 
-def col_keys(key: int, cols):
-    """B_j = lo32(mix64(K_bh + G*(2j+2)))."""
-    return _keyed(key, cols, 2)
+def pair_keys(key: int, pairs):
+    """B_c = lo32(mix64(K_bh + G*(2c+2))), c indexing pairs of key columns."""
+    return _keyed(key, pairs, 2)
 
 
 def keep_threshold(p: float) -> int:
-    """T = floor(p_f32 * 2^32), exact in float64."""
+    """T = floor(p_f32 * 2^16), exact in float64."""
     pf = float(np.float32(p))
     if not (0.0 <= pf < 1.0):
         raise ValueError("dropout probability must lie in [0, 1)")
-    return int(np.floor(pf * 4294967296.0))
+    return int(np.floor(pf * 65536.0))
+
+
+def uniforms16(seed: int, b: int, h: int, H: int, rows, cols):
+    """The 16-bit draws u_ij, shape (len(rows), len(cols)), for head (b, h)."""
+    key = head_key(seed, b, h, H)
+    cols = np.asarray(cols, dtype=np.int64)
+    a = row_keys(key, rows)
+    c = pair_keys(key, cols // 2)
+    w = fmix32(a[:, None] ^ c[None, :])
+    odd = (cols % 2 == 1)[None, :]
+    return np.where(odd, w >> np.uint32(16), w & np.uint32(0xFFFF)).astype(np.uint32)
 
 
 def keep_mask(seed: int, b: int, h: int, H: int, p: float, rows, cols):
     """Boolean keep mask, shape (len(rows), len(cols)), for head (b, h)."""
-    key = head_key(seed, b, h, H)
-    a = row_keys(key, rows)
-    c = col_keys(key, cols)
-    w = fmix32(a[:, None] ^ c[None, :])
-    return w >= np.uint32(keep_threshold(p))
+    return uniforms16(seed, b, h, H, rows, cols) >= np.uint32(keep_threshold(p))

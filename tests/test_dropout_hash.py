@@ -60,9 +60,11 @@ def test_murmur3_published_outputs():
 
 
 def test_threshold_for_p_0_1():
-    # 0.1 in float32 is 13421773 * 2^-27, so floor(p * 2^32) = 13421773 * 32
-    assert DH.keep_threshold(0.1) == 13421773 * 32 == 429496736
+    # 0.1 in float32 is 13421773 * 2^-27, so p * 2^16 = 13421773 / 2048 = 6553.6...
+    assert DH.keep_threshold(0.1) == 13421773 // 2048 == 6553
     assert DH.keep_threshold(0.0) == 0
+    assert DH.keep_threshold(0.5) == 32768
+    assert DH.keep_threshold(float(np.float32(1.0) - np.float32(2.0 ** -24))) == 65535
     with pytest.raises(ValueError):
         DH.keep_threshold(1.0)
 
@@ -72,7 +74,7 @@ def test_keep_rate_and_independence():
     rows, cols = np.arange(0, 4096), np.arange(1000, 1000 + 4096)
     m = DH.keep_mask(2026, 0, 3, 8, p, rows, cols)  # 16.8M draws
     n = m.size
-    q = 1.0 - DH.keep_threshold(p) / 2.0 ** 32
+    q = 1.0 - DH.keep_threshold(p) / 2.0 ** 16
     sigma = np.sqrt(q * (1 - q) / n)
     assert abs(m.mean() - q) <= 5 * sigma
     # no drift of the keep rate across rows or columns
@@ -100,3 +102,57 @@ def test_mask_is_layout_independent():
     big = DH.keep_mask(7, 1, 2, 3, 0.3, np.arange(100), np.arange(100))
     win = DH.keep_mask(7, 1, 2, 3, 0.3, np.arange(40, 70), np.arange(13, 91))
     assert np.array_equal(big[40:70, 13:91], win)
+
+
+def test_pair_convention():
+    """Columns 2c and 2c + 1 of row i take the low and the high 16 bits of
+    fmix32(A_i ^ B_c), built here from the separately pinned mixers."""
+    seed, b, h, H = 99, 1, 2, 5
+    key = int(DH.mix64(np.array([(seed + DH.GOLDEN_GAMMA * (1 + b * H + h)) & DH.MASK64], np.uint64))[0])
+    assert key == DH.head_key(seed, b, h, H)
+    rows, cols = np.array([0, 7, 1000]), np.array([0, 1, 2, 3, 4095, 4096])
+    u = DH.uniforms16(seed, b, h, H, rows, cols)
+    for ri, i in enumerate(rows):
+        a = int(DH.mix64(np.array([(key + DH.GOLDEN_GAMMA * (2 * int(i) + 1)) & DH.MASK64], np.uint64))[0])
+        for ci, j in enumerate(cols):
+            c = int(j) // 2
+            bc = int(DH.mix64(np.array([(key + DH.GOLDEN_GAMMA * (2 * c + 2)) & DH.MASK64], np.uint64))[0])
+            w = int(DH.fmix32(np.array([(a ^ bc) & 0xFFFFFFFF], np.uint32))[0])
+            assert int(u[ri, ci]) == ((w >> 16) if j % 2 else (w & 0xFFFF))
+
+
+def test_draws_uniform_16_bit():
+    """Both halves of the hash are uniform: chi-square over 256 bins of the
+    high and the low byte of the draws of even and of odd columns."""
+    u = DH.uniforms16(5, 0, 0, 1, np.arange(1024), np.arange(2048))  # 2M draws
+    for sub in (u[:, 0::2], u[:, 1::2]):
+        for byte in (sub >> 8, sub & 0xFF):
+            cnt = np.bincount(byte.ravel().astype(np.int64), minlength=256)
+            e = byte.size / 256
+            chi2 = float(np.sum((cnt - e) ** 2 / e))
+            assert chi2 < 255 + 6 * np.sqrt(2 * 255), chi2  # mean 255, sd 22.6
+
+
+def test_pair_halves_and_rectangles_independent():
+    """The two draws of one hash are uncorrelated, and so are the four keep
+    decisions of rectangles (i, j), (i, j'), (i', j), (i', j'), whose hash
+    inputs A ^ B XOR to zero (a structure the finalizer must break)."""
+    p = 0.5
+    rows, cols = np.arange(2048), np.arange(2048)
+    u = DH.uniforms16(11, 0, 1, 2, rows, cols).astype(np.float64) / 65536.0 - 0.5
+    n = u[:, 0::2].size
+    corr = np.mean(u[:, 0::2] * u[:, 1::2]) / (1.0 / 12.0)
+    assert abs(corr) <= 5.0 / np.sqrt(n)
+    m = DH.keep_mask(11, 0, 1, 2, p, rows, cols).astype(np.float64) - 0.5
+    rng = np.random.default_rng(0)
+    i, i2 = rng.integers(0, 2048, 200000), rng.integers(0, 2048, 200000)
+    j, j2 = rng.integers(0, 2048, 200000), rng.integers(0, 2048, 200000)
+    ok = (i != i2) & (j != j2)
+    prod = (m[i, j] * m[i, j2] * m[i2, j] * m[i2, j2])[ok] / 0.0625  # each factor +-0.5
+    assert abs(prod.mean()) <= 5.0 / np.sqrt(ok.sum())
+    # the same statistic does detect the structure when the finalizer is skipped
+    key = DH.head_key(11, 0, 1, 2)
+    raw = DH.row_keys(key, rows)[:, None] ^ DH.pair_keys(key, cols // 2)[None, :]
+    mr = ((raw >> np.uint32(31)) & np.uint32(1)).astype(np.float64) - 0.5
+    prod_raw = (mr[i, j] * mr[i, j2] * mr[i2, j] * mr[i2, j2])[ok] / 0.0625
+    assert abs(prod_raw.mean()) > 0.9
