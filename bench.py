@@ -6,7 +6,10 @@ HIP events between them time each kernel. Inputs are resident in HBM before
 the timed region. Prints one JSON line.
 
 Workload: B=2, H=16, N=8192, d=128, causal, bf16 (the N=8K headline shape);
-the N=32K, d=80 shape and a packed batch of sixteen causal sequences of
+the N=32K, d=80 shape, the other three configurations (the fp32 N=256
+forward, the bf16 N=2048 d=64 causal forward and the N=65536 causal
+forward + backward with dropout 0.1; forward-only ones time the forward
+alone) and a packed batch of sixteen causal sequences of
 512..8192 tokens (with the time the same sequences take padded to the
 longest), and a block-sparse N=32K sequence (local window plus global key
 blocks, with the dense time on the same shape), and the split-KV forward on a
@@ -34,11 +37,14 @@ from workloads import (SPARSE_WORKLOADS, SPLITKV_WORKLOADS, VARLEN_WORKLOADS, WO
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 matrix-core peak (published)
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector peak (published; counts packed fp32)
 METRIC = "attention fwd+bwd TFLOP/s & % of bf16 MFMA peak, causal, N=8K/32K"
 
 
 def _device_inputs(w, torch):
     inp = make_inputs(w, with_grad=True)
+    if w.dtype == "f32":
+        return {k: torch.from_numpy(v[0]).cuda() for k, v in inp.items()}
     return {k: torch.from_numpy(v[0].view(np.int16)).view(torch.bfloat16).cuda() for k, v in inp.items()}
 
 
@@ -50,6 +56,9 @@ def kernel_units(w):
     O and dO read plus D written."""
     elems = w.B * w.H * float(w.N) * w.N / (2.0 if w.causal else 1.0)
     tensor_bytes = w.B * w.N * w.H * w.d * 2
+    if w.dtype == "f32":
+        # fp32 runs on the vector ALUs (fused multiply-adds), not the matrix cores
+        return {"forward": ("alu", 2 * 2 * w.d * elems)}
     return {
         "forward": ("mfma", 2 * 2 * w.d * elems),
         "bwd_preprocess": ("hbm", 2 * tensor_bytes + 4 * w.B * w.H * w.N),
@@ -59,6 +68,9 @@ def kernel_units(w):
 
 
 def run_gpu(w, steps, warmup, torch, fa):
+    """One step = fa_forward, then (for workloads with a backward pass) the
+    D preprocess, dK/dV and dQ kernels; HIP events between the calls time
+    each kernel."""
     dev = _device_inputs(w, torch)
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
     o = torch.empty_like(q)
@@ -66,7 +78,8 @@ def run_gpu(w, steps, warmup, torch, fa):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     ws = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
     args = (w.causal, w.dropout_p, w.dropout_seed, w.scale)
-    names = ("forward", "bwd_preprocess", "bwd_dkdv", "bwd_dq")
+    names = ("forward", "bwd_preprocess", "bwd_dkdv", "bwd_dq") if w.backward else ("forward",)
+    nev = len(names) + 1
 
     def step(ev=None):
         if ev:
@@ -74,6 +87,8 @@ def run_gpu(w, steps, warmup, torch, fa):
         fa.forward(q, k, v, *args, out=o, lse=lse)
         if ev:
             ev[1].record()
+        if not w.backward:
+            return
         fa.backward_preprocess(o, do, workspace=ws)
         if ev:
             ev[2].record()
@@ -87,17 +102,17 @@ def run_gpu(w, steps, warmup, torch, fa):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = evs[0][0].elapsed_time(evs[-1][4]) / steps
+    ms_step = evs[0][0].elapsed_time(evs[-1][-1]) / steps
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
-    fwd_f, bwd_f = counted_flops(w.B, w.H, w.N, w.d, w.causal, True)
+    fwd_f, bwd_f = counted_flops(w.B, w.H, w.N, w.d, w.causal, w.backward)
     fwd_ms = per["forward"]
-    bwd_ms = per["bwd_preprocess"] + per["bwd_dkdv"] + per["bwd_dq"]
+    bwd_ms = per["bwd_preprocess"] + per["bwd_dkdv"] + per["bwd_dq"] if w.backward else None
     return {
         "ms_per_step": ms_step,
         "wall_s": wall,
@@ -105,7 +120,7 @@ def run_gpu(w, steps, warmup, torch, fa):
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
         "fwd_tflops": fwd_f / (fwd_ms * 1e-3) / 1e12,
-        "bwd_tflops": bwd_f / (bwd_ms * 1e-3) / 1e12,
+        "bwd_tflops": bwd_f / (bwd_ms * 1e-3) / 1e12 if w.backward else None,
         "kernel_ms": per,
     }
 
@@ -363,6 +378,8 @@ def roofline(w, kernel_ms):
     sec = kernel_ms[name] * 1e-3
     if bound == "mfma":
         achieved, peak, unit = work / sec / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    elif bound == "alu":
+        achieved, peak, unit = work / sec / 1e12, PEAK_FP32_VECTOR_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = work / sec / 1e9, PEAK_HBM_GBS, "GB/s"
     rec = recorded_traffic(w.name, name)
@@ -407,7 +424,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3)
-    ap.add_argument("--also", type=int, nargs="*", default=[4])
+    ap.add_argument("--also", type=int, nargs="*", default=[4, 1, 2, 5])
     ap.add_argument("--also-varlen", nargs="*", default=["varlen16"])
     ap.add_argument("--also-sparse", nargs="*", default=["local_global"])
     ap.add_argument("--also-splitkv", nargs="*", default=["decode", "prefill_small"])
@@ -455,7 +472,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if w.dtype == "f32" else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "dropout_p": w.dropout_p, "global_batch": w.B, "seq_len": w.N,
@@ -469,9 +486,11 @@ def main():
     also = []
     for cfg in a.also:
         wa = WORKLOADS[cfg]
-        ra = run_gpu(wa, max(3, a.steps // 4), 2, torch, fa)
-        also.append({"workload": wa.name, "tflops": ra["tflops"], "ms_per_step": ra["ms_per_step"],
-                     "pct_of_peak": 100.0 * ra["tflops"] / PEAK_BF16_TFLOPS,
+        ra = run_gpu(wa, max(3, a.steps // 4) if wa.backward else a.steps, 2, torch, fa)
+        peak = PEAK_FP32_VECTOR_TFLOPS if wa.dtype == "f32" else PEAK_BF16_TFLOPS
+        also.append({"workload": wa.name, "dtype": wa.dtype, "passes": "fwd+bwd" if wa.backward else "fwd",
+                     "tflops": ra["tflops"], "ms_per_step": ra["ms_per_step"],
+                     "pct_of_peak": 100.0 * ra["tflops"] / peak,
                      "fwd_tflops": ra["fwd_tflops"], "bwd_tflops": ra["bwd_tflops"],
                      "kernel_ms": ra["kernel_ms"], "roofline": roofline(wa, ra["kernel_ms"])})
         torch.cuda.empty_cache()
