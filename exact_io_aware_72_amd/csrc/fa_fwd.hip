@@ -69,10 +69,11 @@ struct FwdParams {
   uint64_t seed;
 };
 
-template <int D, bool FP8 = false>
+template <int D, bool FP8 = false, int NW_ = 4>
 struct FwdCfg {
-  static constexpr int NT = 256;                 // 4 waves
-  static constexpr int BM = 128;                 // query rows per work-group
+  static constexpr int NW = NW_;                 // waves, 32 query rows each
+  static constexpr int NT = 64 * NW;
+  static constexpr int BM = 32 * NW;             // query rows per work-group
   static constexpr int BN = 64;                  // keys per tile
   static constexpr int NKC = D / 16;             // k-steps of S^T = K Q^T
   static constexpr int DP = (D + 31) / 32 * 32;  // rows of O^T computed (d padded to 32)
@@ -82,16 +83,16 @@ struct FwdCfg {
   using VT = Tile<BN, D, Swz::kTr>;              // V tile: transposing reads
   static constexpr int STAGE = KT::BYTES + VT::BYTES;
   static constexpr int NLOAD = KT::NLOAD + VT::NLOAD;  // load instructions per tile
-  static constexpr int LPW = (NLOAD + 3) / 4;          // per wave
+  static constexpr int LPW = (NLOAD + NW - 1) / NW;    // per wave
 };
 
 // At most two waves per SIMD: with the smaller FP8 tiles three work-groups
 // would fit a CU, and the register budget of three waves keeps the compiler
 // from issuing the V reads ahead of the P V products.
-template <int D, bool CAUSAL, bool DROP, bool SPARSE, bool SPLIT, bool FP8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void fwd_bf16_kernel(
+template <int D, bool CAUSAL, bool DROP, bool SPARSE, bool SPLIT, bool FP8, int NW = 4>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 2))) void fwd_bf16_kernel(
     FwdParams p) {
-  using C = FwdCfg<D, FP8>;
+  using C = FwdCfg<D, FP8, NW>;
   using KT = typename C::KT;
   using VT = typename C::VT;
   // Two stages of K and V tiles; separate arrays so that reads of one stage
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   int dlds[C::LPW];
 #pragma unroll
   for (int m = 0; m < C::LPW; ++m) {
-    const int i = (wave & 3) + 4 * m;
+    const int i = (wave % C::NW) + C::NW * m;
     int off = 0, row = 0, ch = 0;
     if (i < KT::NLOAD) {
       KT::load_slot(i, lane, off, row, ch);
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     if constexpr (FP8) ksn = buf_load_f32(rks, (uint32_t)(k0 >> 6) * 4);
 #pragma unroll
     for (int m = 0; m < C::LPW; ++m) {
-      const int i = (wave & 3) + 4 * m;
+      const int i = (wave % C::NW) + C::NW * m;
       if (i < C::NLOAD) lds_dma_16(i < KT::NLOAD ? rk : rv, stage + dlds[m], dsrc[m]);
     }
     if constexpr (DROP) {
@@ -602,10 +603,32 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
   }
 }
 
+// Eight waves (256 query rows) per work-group share each K/V tile, which
+// halves the tile loads and L2 reads per query row but leaves the waves of a
+// group less balanced under the causal mask. Measured on MI355X, eight waves
+// pay for head dims up to 80 from N = 8192 (d = 64: 16% faster at N = 8192;
+// d = 80: 5% at N = 8192, 11% at N = 32768) and for the vector-ALU-bound
+// dropout kernels at N >= 32768 (d = 128: 6% at N = 65536), and cost the
+// d = 128 kernels without dropout 7-10% (N = 8192..32768).
+template <int D, bool DROP>
+bool fwd_eight_waves(int N) {
+  return (D <= 80 && N >= 8192) || (DROP && N >= 32768);
+}
+
 template <int D, bool CAUSAL, bool DROP, bool SPARSE>
-hipError_t launch_fwd_bf16_t(const FwdParams& prm, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROP, SPARSE, false, false>), dim3(nblocks), dim3(256),
-                     0, s, prm);
+hipError_t launch_fwd_bf16_t(const FwdParams& prm, hipStream_t s) {
+  // A block mask row covers 128 queries: block-sparse runs keep four waves.
+  if constexpr (!SPARSE) {
+    if (fwd_eight_waves<D, DROP>(prm.N)) {
+      const int nblocks = (prm.N + 255) / 256 * prm.B * prm.H;
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROP, SPARSE, false, false, 8>), dim3(nblocks),
+                         dim3(512), 0, s, prm);
+      return hipGetLastError();
+    }
+  }
+  const int nblocks = (prm.N + 127) / 128 * prm.B * prm.H;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROP, SPARSE, false, false, 4>), dim3(nblocks),
+                     dim3(256), 0, s, prm);
   return hipGetLastError();
 }
 
@@ -655,20 +678,20 @@ __global__ __launch_bounds__(256) void splitkv_combine_kernel(const float* __res
 }
 
 template <int D, bool SPARSE>
-hipError_t launch_fwd_bf16_ds(const FwdParams& prm, bool causal, bool drop, int nblocks,
+hipError_t launch_fwd_bf16_ds(const FwdParams& prm, bool causal, bool drop,
                               hipStream_t s) {
   if (causal)
-    return drop ? launch_fwd_bf16_t<D, true, true, SPARSE>(prm, nblocks, s)
-                : launch_fwd_bf16_t<D, true, false, SPARSE>(prm, nblocks, s);
-  return drop ? launch_fwd_bf16_t<D, false, true, SPARSE>(prm, nblocks, s)
-              : launch_fwd_bf16_t<D, false, false, SPARSE>(prm, nblocks, s);
+    return drop ? launch_fwd_bf16_t<D, true, true, SPARSE>(prm, s)
+                : launch_fwd_bf16_t<D, true, false, SPARSE>(prm, s);
+  return drop ? launch_fwd_bf16_t<D, false, true, SPARSE>(prm, s)
+              : launch_fwd_bf16_t<D, false, false, SPARSE>(prm, s);
 }
 
 template <int D>
-hipError_t launch_fwd_bf16_d(const FwdParams& prm, bool causal, bool drop, int nblocks,
+hipError_t launch_fwd_bf16_d(const FwdParams& prm, bool causal, bool drop,
                              hipStream_t s) {
-  return prm.bmask ? launch_fwd_bf16_ds<D, true>(prm, causal, drop, nblocks, s)
-                   : launch_fwd_bf16_ds<D, false>(prm, causal, drop, nblocks, s);
+  return prm.bmask ? launch_fwd_bf16_ds<D, true>(prm, causal, drop, s)
+                   : launch_fwd_bf16_ds<D, false>(prm, causal, drop, s);
 }
 
 template <int D, bool CAUSAL, bool DROP>
@@ -712,12 +735,10 @@ hipError_t launch_forward_bf16(const AttnArgs& a, hipStream_t s) {
   prm.drop_t = a.drop_threshold;
   prm.drop_r = a.drop_rescale;
   prm.seed = a.seed;
-  const int nqb = (a.N + 127) / 128;
-  const int nblocks = nqb * a.B * a.H;
   switch (a.d) {
-    case 64: return launch_fwd_bf16_d<64>(prm, a.causal, a.dropout, nblocks, s);
-    case 80: return launch_fwd_bf16_d<80>(prm, a.causal, a.dropout, nblocks, s);
-    case 128: return launch_fwd_bf16_d<128>(prm, a.causal, a.dropout, nblocks, s);
+    case 64: return launch_fwd_bf16_d<64>(prm, a.causal, a.dropout, s);
+    case 80: return launch_fwd_bf16_d<80>(prm, a.causal, a.dropout, s);
+    case 128: return launch_fwd_bf16_d<128>(prm, a.causal, a.dropout, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -57,6 +57,11 @@ FWD_CASES = [
     _case(3, B=1, H=2, N=17),
     _case(4, B=1, H=1, N=100, causal=False),
     _case(2, B=1, H=1, N=129, dropout_p=0.5),
+    # Head dims up to 80 from N = 8192 (and dropout from N = 32768) take the
+    # eight-wave forward: 256-row work-groups with a ragged last one.
+    _case(2, B=1, H=2, N=8200),
+    _case(4, B=1, H=1, N=8300, causal=False),
+    _case(2, B=1, H=1, N=8250, causal=False, dropout_p=0.1),
 ]
 
 
