@@ -3,7 +3,8 @@ sequence, key range split over work-groups, partial results merged by their
 logsumexps): the HIP path through the C ABI against the fp64 cross-length
 oracle, element by element, for decode and prefill shapes, split counts from
 1 to more parts than key tiles, and bit equality with fa_forward for one part
-at equal lengths."""
+at equal lengths. Decode-like cases include one to four query rows, parts
+left without keys, and a query that sees a single key.""" 
 import numpy as np
 import pytest
 
@@ -33,6 +34,13 @@ CASES = [
     (1, 2, 200, 200, 64, True, 128),
     (2, 1, 64, 1000, 80, False, 0),
     (1, 2, 513, 1100, 128, True, 5),
+    # a few query rows against many keys
+    (1, 2, 2, 777, 80, True, 3),
+    (2, 2, 4, 3001, 128, False, 128),
+    (1, 1, 4, 4, 64, True, 2),       # query 0 sees one key; part 2 none for it
+    (1, 3, 1, 17, 64, False, 16),    # parts 9..15 hold no keys
+    (1, 1, 1, 1, 128, True, 0),
+    (3, 2, 3, 70000, 80, True, 0),
 ]
 
 
