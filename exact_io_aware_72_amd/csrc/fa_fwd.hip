@@ -474,9 +474,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 2)))
 }
 
 // ---------------------------------------------------------------------------
-// fp32 path: the same tiled online softmax on the vector ALUs, two threads
-// per query row (each owns half of the head dimension). Used for fp32 inputs,
-// where the bf16 matrix cores do not apply.
+// fp32 path: the same tiled online softmax on the vector ALUs, sixteen
+// threads per query row (each owns d/16 of the head dimension; a score is
+// summed over the sixteen by four lane exchanges), 8 rows per work-group.
+// Used for fp32 inputs, where the bf16 matrix cores do not apply. Spreading a
+// row over more threads shortens each thread's dependent chain, which is what
+// the small fp32 problems wait on: at B=1 H=1 N=256 d=64 the forward takes
+// 173 us with two threads per row, 75 us with eight and 51 us with sixteen.
 struct FwdParamsF {
   const float* q;
   const float* k;
@@ -494,15 +498,18 @@ struct FwdParamsF {
   uint64_t seed;
 };
 
+constexpr int kF32Tpr = 16;            // threads per query row (each owns d/16 columns)
+constexpr int kF32Bm = 128 / kF32Tpr;  // query rows per work-group
+
 template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
-  constexpr int BM = 64, BN = 16, DH = D / 2;
+  constexpr int BM = kF32Bm, BN = 16, DH = D / kF32Tpr;
   __shared__ __align__(16) float ks[BN][D];
   __shared__ __align__(16) float vs[BN][D];
   __shared__ uint32_t bk[BN / 2];  // dropout keys of the tile's key pairs
 
   const int tid = threadIdx.x;
-  const int qi = tid >> 1, part = tid & 1;
+  const int qi = tid / kF32Tpr, part = tid % kF32Tpr;
   const int H = p.H;
   const int nqb = (p.N + BM - 1) / BM;
   const BlockMap bm = map_block(blockIdx.x, nqb, p.B * H);
@@ -563,7 +570,8 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
       float acc = 0.f;
 #pragma unroll
       for (int c = 0; c < DH; ++c) acc = fmaf(qv[c], ks[j][part * DH + c], acc);
-      acc += __shfl_xor(acc, 1);
+#pragma unroll
+      for (int x = 1; x < kF32Tpr; x <<= 1) acc += __shfl_xor(acc, x, kF32Tpr);
       float x = acc * p.c2;
       const int key = k0 + j;
       if (key >= N || (CAUSAL && key > myq)) x = -INFINITY;
@@ -946,7 +954,7 @@ hipError_t launch_forward_f32(const AttnArgs& a, hipStream_t s) {
   prm.drop_t = a.drop_threshold;
   prm.drop_r = a.drop_rescale;
   prm.seed = a.seed;
-  const int nqb = (a.N + 63) / 64;
+  const int nqb = (a.N + kF32Bm - 1) / kF32Bm;
   const int nblocks = nqb * a.B * a.H;
   switch (a.d) {
     case 64: return launch_fwd_f32_d<64>(prm, a.causal, a.dropout, nblocks, s);
