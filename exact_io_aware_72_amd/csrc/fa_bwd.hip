@@ -202,27 +202,39 @@ struct DkdvCfg {
   static constexpr int VLPW = (VB::NLOAD + NW - 1) / NW;
 };
 
-template <int D, bool CAUSAL, bool DROP, bool SPARSE>
-__global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams p) {
+// QG query groups: with QG = 2 the work-group has two groups of NW waves
+// over the same keys; group g takes query tiles g, g + 2, ... with its own LDS
+// stages, and the groups' dK/dV partial sums are added in LDS in a fixed
+// order at the end. Block-sparse runs use it: a key block whose mask column
+// keeps many query blocks (a global key block) otherwise sets the critical
+// path of the whole launch.
+template <int D, bool CAUSAL, bool DROP, bool SPARSE, int QG = 1>
+__global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdParams p) {
   using C = DkdvCfg<D>;
   using QT = typename C::QT;
   using VB = typename C::VB;
   __shared__ __align__(16) char vblk[VB::BYTES];
-  __shared__ __align__(16) char st0[C::STAGE];
-  __shared__ __align__(16) char st1[C::STAGE];
+  __shared__ __align__(16) char st0[QG][C::STAGE];
+  __shared__ __align__(16) char st1[QG][C::STAGE];
   // Per-stage statistics of the tile's queries: lse * log2(e), D, row keys.
-  __shared__ __align__(16) float ls0[C::BQ];
-  __shared__ __align__(16) float ls1[C::BQ];
-  __shared__ __align__(16) float dd0[C::BQ];
-  __shared__ __align__(16) float dd1[C::BQ];
-  __shared__ __align__(16) uint32_t ar0[DROP ? C::BQ : 1];
-  __shared__ __align__(16) uint32_t ar1[DROP ? C::BQ : 1];
+  __shared__ __align__(16) float ls0[QG][C::BQ];
+  __shared__ __align__(16) float ls1[QG][C::BQ];
+  __shared__ __align__(16) float dd0[QG][C::BQ];
+  __shared__ __align__(16) float dd1[QG][C::BQ];
+  __shared__ __align__(16) uint32_t ar0[QG][DROP ? C::BQ : 1];
+  __shared__ __align__(16) uint32_t ar1[QG][DROP ? C::BQ : 1];
   __shared__ uint16_t kept[SPARSE ? kSparseMaxBlocks : 1];  // kept query blocks
   static_assert(!SPARSE || C::BK == kSparseBlock, "a work-group covers one mask column");
+  static_assert(QG == 1 || QG == 2, "one or two query groups");
+  // The group-sum buffer (one accumulator block of every wave) fits in st0.
+  static_assert(QG == 1 || C::NW * 16 * 64 * 4 <= QG * C::STAGE, "reduction buffer");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qg = QG == 1 ? 0 : wave / C::NW;       // query group
+  const int wv = QG == 1 ? wave : wave % C::NW;    // wave within the group: keys kw0 .. kw0 + 31
+  const int gt = QG == 1 ? tid : tid - qg * C::NT;  // thread within the group
   const int l32 = lane & 31, hf = lane >> 5;
   const int H = p.H;
   const int nkb = (p.N + C::BK - 1) / C::BK;
@@ -233,7 +245,7 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
   const int N = sr.n;
   const int k0 = kblk * C::BK;
   if (k0 >= N) return;  // block past the end of a shorter sequence
-  const int kw0 = k0 + wave * 32;
+  const int kw0 = k0 + wv * 32;
   const int mykey = kw0 + l32;
   const int64_t rs = (int64_t)H * D;
   const int64_t base = sr.base;
@@ -251,8 +263,8 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
     const BufRes rvb = make_bufres(Vg + (int64_t)k0 * rs, (uint32_t)(N - k0) * rs2);
 #pragma unroll
     for (int m = 0; m < C::VLPW; ++m) {
-      const int i = (wave % C::NW) + C::NW * m;
-      if (i < VB::NLOAD) {
+      const int i = wv + C::NW * m;
+      if ((QG == 1 || qg == 0) && i < VB::NLOAD) {
         int off, row, ch;
         VB::load_slot(i, lane, off, row, ch);
         lds_dma_16(rvb, vblk + off, (uint32_t)row * rs2 + 16 * ch);
@@ -266,7 +278,7 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
   for (int c = 0; c < C::NKC; ++c)
     kreg[c] = buf_load_128(rk, (uint32_t)mykey * rs2 + (16 * c + 8 * hf) * 2);
   // This lane's V row in LDS (B operand of dP = dO V^T).
-  const int vr = wave * 32 + l32;
+  const int vr = wv * 32 + l32;
   const int vx = hf ^ VB::sw(vr);
   int vrow[4];
 #pragma unroll
@@ -311,7 +323,7 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
   int dlds[C::LPW];
 #pragma unroll
   for (int m = 0; m < C::LPW; ++m) {
-    const int i = (wave % C::NW) + C::NW * m;
+    const int i = wv + C::NW * m;
     int off = 0, row = 0, ch = 0;
     if (i < QT::NLOAD) {
       QT::load_slot(i, lane, off, row, ch);
@@ -322,26 +334,26 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
     dsrc[m] = (uint32_t)row * rs2 + 16 * ch;
     dlds[m] = off;
   }
-  // Statistics of a query tile: threads 0-31 load lse, 32-63 load D,
-  // 64-95 hash the row keys; stored after the tile's compute. Rows past N
-  // read zeros (their Q and dO rows are zero too, so they add nothing).
+  // Statistics of a query tile: threads 0-31 of the group load lse, 32-63
+  // load D, 64-95 hash the row keys; stored after the tile's compute. Rows
+  // past N read zeros (their Q and dO rows are zero too, so they add nothing).
   float sx = 0.f;
   auto stat_load = [&](int qt0) {
-    if (tid < 32) {
-      sx = buf_load_f32(rl, (uint32_t)(qt0 + tid) * 4);
-    } else if (tid < 64) {
-      sx = buf_load_f32(rd, (uint32_t)(qt0 + tid - 32) * 4);
-    } else if (DROP && tid < 96) {
-      sx = __uint_as_float(row_key(kbh, qt0 + tid - 64));
+    if (gt < 32) {
+      sx = buf_load_f32(rl, (uint32_t)(qt0 + gt) * 4);
+    } else if (gt < 64) {
+      sx = buf_load_f32(rd, (uint32_t)(qt0 + gt - 32) * 4);
+    } else if (DROP && gt < 96) {
+      sx = __uint_as_float(row_key(kbh, qt0 + gt - 64));
     }
   };
   auto stat_store = [&](float* ls, float* dd, uint32_t* ar) {
-    if (tid < 32) {
-      ls[tid] = sx * kLog2e;
-    } else if (tid < 64) {
-      dd[tid - 32] = sx;
-    } else if (DROP && tid < 96) {
-      ar[tid - 64] = __float_as_uint(sx);
+    if (gt < 32) {
+      ls[gt] = sx * kLog2e;
+    } else if (gt < 64) {
+      dd[gt - 32] = sx;
+    } else if (DROP && gt < 96) {
+      ar[gt - 64] = __float_as_uint(sx);
     }
   };
   auto issue = [&](char* stage, int qt0) {
@@ -350,7 +362,7 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
     const BufRes ro = make_bufres(dOg + (int64_t)qt0 * rs, left);
 #pragma unroll
     for (int m = 0; m < C::LPW; ++m) {
-      const int i = (wave % C::NW) + C::NW * m;
+      const int i = wv + C::NW * m;
       if (i < C::NLOAD) lds_dma_16(i < QT::NLOAD ? rq : ro, stage + dlds[m], dsrc[m]);
     }
   };
@@ -365,18 +377,21 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
     dvacc[db] = f32x16{};
   }
 
+  // Step of this group over kept query tile t (t >= ntiles: the group has
+  // no tile in this step and only takes part in the barrier).
   auto step = [&](const char* cur, const float* lsc, const float* ddc, const uint32_t* arc,
                   char* nxt, float* lsn, float* ddn, uint32_t* arn, int t) {
     wait_vmem();
     __syncthreads();
-    const int qt0 = tile_start(t);
-    const bool more = t + 1 < ntiles;
+    const bool valid = QG == 1 || t < ntiles;  // one group: every step has a tile
+    const int qt0 = valid ? tile_start(t) : 0;
+    const bool more = t + QG < ntiles;
     if (more) {
-      const int qn = tile_start(t + 1);
+      const int qn = tile_start(t + QG);
       stat_load(qn);
       issue(nxt, qn);
     }
-    if (!CAUSAL || qt0 + C::BQ - 1 >= kw0) {
+    if (valid && (!CAUSAL || qt0 + C::BQ - 1 >= kw0)) {
       // S = Q K^T and dP = dO V^T : lane = key, register r -> query qt0 + c_row(r, hf)
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -451,17 +466,42 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT) void bwd_dkdv_bf16_kernel(BwdParams
     if (more) stat_store(lsn, ddn, arn);
   };
 
-  if (ntiles > 0) {
-    stat_load(tile_start(0));
-    issue(st0, tile_start(0));
-    stat_store(ls0, dd0, ar0);
+  const int nsteps = (ntiles + QG - 1) / QG;  // the same count for every group
+  if (qg < ntiles) {
+    stat_load(tile_start(qg));
+    issue(st0[qg], tile_start(qg));
+    stat_store(ls0[qg], dd0[qg], ar0[qg]);
   }
-  for (int t = 0; t < ntiles; t += 2) {
-    step(st0, ls0, dd0, ar0, st1, ls1, dd1, ar1, t);
-    if (t + 1 < ntiles) step(st1, ls1, dd1, ar1, st0, ls0, dd0, ar0, t + 1);
+  for (int s = 0; s < nsteps; s += 2) {
+    step(st0[qg], ls0[qg], dd0[qg], ar0[qg], st1[qg], ls1[qg], dd1[qg], ar1[qg], qg + QG * s);
+    if (s + 1 < nsteps)
+      step(st1[qg], ls1[qg], dd1[qg], ar1[qg], st0[qg], ls0[qg], dd0[qg], ar0[qg], qg + QG * (s + 1));
   }
 
-  if (mykey < N) {
+  if constexpr (QG == 2) {
+    // Group 1's sums into group 0's, one accumulator block at a time through
+    // st0 (free once every wave has passed the barrier): slot (wave, r, lane).
+    float* red = reinterpret_cast<float*>(&st0[0][0]);
+#pragma unroll
+    for (int tsel = 0; tsel < 2; ++tsel) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        f32x16& acc = tsel ? dvacc[db] : dkacc[db];
+        __syncthreads();
+        if (qg == 1) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[(wv * 16 + r) * 64 + lane] = acc[r];
+        }
+        __syncthreads();
+        if (qg == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] += red[(wv * 16 + r) * 64 + lane];
+        }
+      }
+    }
+  }
+
+  if ((QG == 1 || qg == 0) && mykey < N) {
     uint16_t* dkrow = static_cast<uint16_t*>(p.dk) + base + (int64_t)mykey * rs;
     uint16_t* dvrow = static_cast<uint16_t*>(p.dv) + base + (int64_t)mykey * rs;
     const float sc = p.scale;
@@ -946,16 +986,19 @@ __global__ __launch_bounds__(256) void dropout_mask_kernel(uint64_t seed, int b,
 template <int D, bool SPARSE>
 hipError_t launch_dkdv_ds(const BwdParams& prm, bool causal, bool drop, dim3 grid, dim3 block,
                           hipStream_t s) {
+  // Block-sparse: two query groups per work-group (see the kernel).
+  constexpr int QG = SPARSE ? 2 : 1;
+  block.x *= QG;
   if (causal) {
     if (drop)
-      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, true, true, SPARSE>), grid, block, 0, s, prm);
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, true, true, SPARSE, QG>), grid, block, 0, s, prm);
     else
-      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, true, false, SPARSE>), grid, block, 0, s, prm);
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, true, false, SPARSE, QG>), grid, block, 0, s, prm);
   } else {
     if (drop)
-      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, false, true, SPARSE>), grid, block, 0, s, prm);
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, false, true, SPARSE, QG>), grid, block, 0, s, prm);
     else
-      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, false, false, SPARSE>), grid, block, 0, s, prm);
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, false, false, SPARSE, QG>), grid, block, 0, s, prm);
   }
   return hipGetLastError();
 }

@@ -100,9 +100,13 @@ def test_blocksparse_matches_oracle(case):
 
 @pytest.mark.parametrize("dtype,d,causal,p", [("bf16", 128, True, 0.1), ("bf16", 80, False, 0.0),
                                               ("bf16", 64, True, 0.0), ("f32", 64, True, 0.0)])
-def test_masks_removing_nothing_equal_dense_bitwise(dtype, d, causal, p):
+def test_masks_removing_nothing_equal_dense(dtype, d, causal, p):
     """All-ones masks (and, under the causal mask, the block-lower triangle)
-    visit the same tiles in the same order as the dense kernels."""
+    visit the same tiles in the same order as the dense kernels, so O, LSE
+    and dQ are bitwise equal. The block-sparse bf16 dK/dV kernel splits each
+    key block's query tiles over two groups of waves and adds the two fp32
+    partial sums at the end, so dK and dV differ from the dense (sequential)
+    sums by fp32 reassociation: at most one bf16 unit in the last place."""
     w = _w(dtype, 2, 2, 333, d, causal, p, 48)
     inp = make_inputs(w, with_grad=True)
     dev, _ = device_inputs(inp, dtype)
@@ -117,8 +121,13 @@ def test_masks_removing_nothing_equal_dense_bitwise(dtype, d, causal, p):
                                      3, w.scale)
         torch.cuda.synchronize()
         assert torch.equal(o, o2) and torch.equal(lse, lse2)
-        for a, b in zip(g, g2):
-            assert torch.equal(a, b)
+        assert torch.equal(g[0], g2[0])  # dQ
+        for a, b in zip(g[1:], g2[1:]):  # dK, dV
+            if dtype == "f32":
+                assert torch.equal(a, b)
+            else:
+                a32, b32 = a.float(), b.float()
+                assert torch.all((a32 - b32).abs() <= 2.0 ** -7 * a32.abs() + 1e-6)
 
 
 def test_mask_broadcasting():
