@@ -27,6 +27,7 @@ from .attention import (  # noqa: F401
     attention_probs,
     forward,
     forward_cross,
+    head_forward,
     backward,
     sampled_head,
 )

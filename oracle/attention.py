@@ -113,10 +113,13 @@ def _dropped(p_mat, seed, b, h, H, dropout_p, rows, cols):
 
 
 def head_forward(qh, kh, vh, scale, causal, dropout_p, seed, b, h, H, panel=_PANEL, bmask=None,
-                 row_offset=0):
+                 row_offset=0, hash_row_offset=0):
     """One head of one sequence: qh is [n, d], kh, vh are [m, d] float64
     arrays, (b, h, H) key the dropout hash, bmask is this head's block mask or
-    None. Query i sits at key position row_offset + i for the causal mask.
+    None. Query i sits at key position row_offset + i for the causal mask,
+    and is row hash_row_offset + i of the dropout hash and the block mask (a
+    panel of rows cut from a larger square problem passes its first row as
+    both offsets).
     Returns (O [n, d], LSE [n]); rows with no unmasked key get O = 0,
     LSE = -inf."""
     n = qh.shape[0]
@@ -126,10 +129,11 @@ def head_forward(qh, kh, vh, scale, causal, dropout_p, seed, b, h, H, panel=_PAN
         r1 = min(r0 + panel, n)
         nc = _panel_cols(causal, row_offset + r1, kh.shape[0])
         s = attention_scores(qh[r0:r1], kh[:nc], scale, causal, row_offset + r0)
-        s = apply_block_mask(s, bmask, np.arange(r0, r1), np.arange(nc))
+        rows = np.arange(hash_row_offset + r0, hash_row_offset + r1)
+        s = apply_block_mask(s, bmask, rows, np.arange(nc))
         _, _, l_ = softmax_stats(s)
         p = attention_probs(s, l_)
-        pt = _dropped(p, seed, b, h, H, dropout_p, np.arange(r0, r1), np.arange(nc))
+        pt = _dropped(p, seed, b, h, H, dropout_p, rows, np.arange(nc))
         o[r0:r1] = pt @ vh[:nc]
         lse[r0:r1] = l_
     return o, lse

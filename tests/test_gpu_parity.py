@@ -81,6 +81,25 @@ def test_forward_matches_oracle(w):
     assert_close("LSE", lse, lse_ref, w.dtype)
 
 
+def test_eight_wave_dropout_forward_rows():
+    """Dropout runs from N = 32768 take the eight-wave forward; at N = 32800
+    the last 256-row work-group holds 32 rows. Rows at the start, across a
+    256-row group boundary and at the end are checked against the oracle,
+    which computes those row panels alone (query i at row r0 + i for the
+    causal mask and the dropout hash)."""
+    w = _case(5, B=1, H=2, N=32800)
+    inp = make_inputs(w, with_grad=False)
+    dev, val = device_inputs(inp, w.dtype)
+    o, lse = _run_fwd(dev, w)
+    for h in range(w.H):
+        for r0, r1 in ((0, 40), (16360, 16424), (32704, 32800)):
+            po, pl = oracle.head_forward(val["q"][0, r0:r1, h], val["k"][0, :, h], val["v"][0, :, h],
+                                         w.scale, w.causal, w.dropout_p, w.dropout_seed, 0, h, w.H,
+                                         row_offset=r0, hash_row_offset=r0)
+            assert_close(f"O[{h},{r0}:{r1}]", o[0, r0:r1, h], po, w.dtype)
+            assert_close(f"LSE[{h},{r0}:{r1}]", lse[0, h, r0:r1], pl, w.dtype)
+
+
 BWD_CASES = [
     _case(3, B=1, H=2, N=300),
     _case(3, B=1, H=1, N=260, causal=False),

@@ -231,6 +231,24 @@ def test_panels_do_not_change_results():
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_row_panel_with_offsets_matches_full(causal):
+    """Rows r0..r1 computed alone (query i at row and key position r0 + i)
+    equal those rows of the whole problem, dropout included: the offsets key
+    the causal mask and the dropout hash by absolute row."""
+    B, N, H, d = 1, 50, 2, 4
+    q, k, v = (_rand(B, N, H, d) for _ in range(3))
+    scale, p_drop, seed = 0.5, 0.3, 21
+    o, lse = oracle.forward(q, k, v, scale, causal, p_drop, seed)
+    for h in range(H):
+        for r0, r1 in ((0, 7), (13, 29), (44, 50)):
+            po, pl = oracle.head_forward(q[0, r0:r1, h].astype(np.float64), k[0, :, h].astype(np.float64),
+                                         v[0, :, h].astype(np.float64), scale, causal, p_drop, seed, 0, h,
+                                         H, row_offset=r0, hash_row_offset=r0)
+            assert np.max(np.abs(po - o[0, r0:r1, h])) <= 1e-13
+            assert np.max(np.abs(pl - lse[0, h, r0:r1])) <= 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("p_drop", [0.0, 0.15])
 def test_sampled_head_matches_full(causal, p_drop):
     B, N, H, d = 2, 45, 3, 5
