@@ -233,7 +233,7 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdP
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qg = QG == 1 ? 0 : wave / C::NW;       // query group
-  const int wv = QG == 1 ? wave : wave % C::NW;    // wave within the group: keys kw0 .. kw0 + 31
+  const int wv = wave % C::NW;                      // wave within the group: keys kw0 .. kw0 + 31
   const int gt = QG == 1 ? tid : tid - qg * C::NT;  // thread within the group
   const int l32 = lane & 31, hf = lane >> 5;
   const int H = p.H;
