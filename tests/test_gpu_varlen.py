@@ -37,6 +37,10 @@ CASES = [
     _vw("f32-d64-causal", [100, 0, 37, 256], 2, 64, "f32", True, 0.0, seed=3106),
     _vw("f32-d80-full-drop", [70, 130], 1, 80, "f32", False, 0.15, seed=3107),
     _vw("f32-d128-causal", [1, 65, 190], 1, 128, "f32", True, 0.0, seed=3108),
+    # longest sequence >= 8192 at d <= 80: the eight-wave forward (256-row
+    # work-groups), with sequences shorter than one such group beside it
+    _vw("bf16-d64-causal-long", [8300, 0, 300, 1], 1, 64, "bf16", True, 0.0, seed=3109),
+    _vw("bf16-d80-full-long-drop", [257, 8200], 1, 80, "bf16", False, 0.1, amp=0.5, seed=3110),
 ]
 
 
