@@ -332,6 +332,42 @@ def run_gpu_fp8(cfg, steps, warmup, torch, fa):
             "forward_bf16_ms": ms_bf16, "forward_bf16_tflops": fwd_f / (ms_bf16 * 1e-3) / 1e12}
 
 
+def mfma_ceiling(torch, fa, blocks=512, iters=20000, reps=5):
+    """Sustained bf16 matrix-core rate of the probe kernel (fa_probe_mfma_rate:
+    32x32x16 products on register-resident operands, nothing else in the
+    loop) on operands drawn like the workload's inputs (iid N(0,1) rounded to
+    bf16) and on constant operands (all 1.0). 512 work-groups of four waves
+    give two waves per SIMD, the occupancy of the attention kernels. The
+    random-operand rate is what the matrix cores sustain on this data at the
+    chip's power limit; the constant-operand rate shows the instruction stream
+    itself is not the limit."""
+    rng = np.random.default_rng(2026)
+    res = {"blocks": blocks, "iters": iters,
+           "operands": "16 fragments of 64 lanes x 8 bf16: iid N(0,1) rounded to bf16, or all 1.0"}
+    flops = float(blocks) * 4 * iters * 16 * 32768
+    for label, x in (("random", rng.standard_normal(16 * 64 * 8).astype(np.float32)),
+                     ("constant", np.ones(16 * 64 * 8, np.float32))):
+        ops = torch.from_numpy(x).cuda().to(torch.bfloat16)
+        out = fa.probe_mfma_rate(ops, blocks, 16)  # warm-up
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fa.probe_mfma_rate(ops, blocks, iters, out=out)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        res[f"{label}_operands_tflops"] = flops / (float(np.median(times)) * 1e-3) / 1e12
+    return res
+
+
+def _add_ceiling_frac(entry, ceiling):
+    rl = entry.get("roofline") if isinstance(entry, dict) else None
+    if rl and rl.get("bound") == "mfma" and rl.get("unit") == "TFLOP/s" and rl.get("peak") == PEAK_BF16_TFLOPS:
+        rl["frac_of_data_ceiling"] = rl["achieved"] / ceiling
+
+
 def kernel_source_digest():
     """SHA-256 over the kernel sources (comments and blank lines removed, so
     that only code counts) and the build flags: HBM traffic figures recorded
@@ -341,6 +377,8 @@ def kernel_source_digest():
     from exact_io_aware_72_amd import build as fa_build
     h = hashlib.sha256()
     for name in sorted(os.listdir(fa_build.CSRC)):
+        if name == "fa_probe.hip":  # the matrix-core rate probe, not an attention kernel
+            continue
         with open(os.path.join(fa_build.CSRC, name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -483,6 +521,7 @@ def main():
         "kernel_ms": r["kernel_ms"],
         "roofline": roofline(w, r["kernel_ms"]),
     }
+    line["mfma_ceiling"] = mfma_ceiling(torch, fa)
     also = []
     for cfg in a.also:
         wa = WORKLOADS[cfg]
@@ -507,6 +546,8 @@ def main():
         also.append(run_gpu_fp8(cfg, max(5, a.steps // 2), 2, torch, fa))
         torch.cuda.empty_cache()
     line["also"] = also
+    for entry in [line] + also:
+        _add_ceiling_frac(entry, line["mfma_ceiling"]["random_operands_tflops"])
     line["cpu_baseline"] = None if a.no_cpu_baseline else cpu_baseline(w, a.cpu_seconds)
     print(json.dumps(line), flush=True)
 

@@ -22,7 +22,7 @@ __all__ = [
     "flash_attention", "forward_varlen", "backward_varlen", "varlen_workspace_bytes",
     "forward_blocksparse", "backward_blocksparse", "BLOCK",
     "forward_splitkv", "splitkv_num_splits", "splitkv_workspace_bytes",
-    "quantize_fp8", "forward_fp8", "forward_fp8_quantized",
+    "quantize_fp8", "forward_fp8", "forward_fp8_quantized", "probe_mfma_rate",
     "EXPORTED_SYMBOLS", "STATUS",
 ]
 
@@ -38,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "fa_forward_varlen", "fa_backward_varlen", "fa_backward_varlen_workspace_bytes",
     "fa_forward_blocksparse", "fa_backward_blocksparse",
     "fa_splitkv_num_splits", "fa_forward_splitkv_workspace_bytes", "fa_forward_splitkv",
-    "fa_quantize_fp8", "fa_forward_fp8",
+    "fa_quantize_fp8", "fa_forward_fp8", "fa_probe_mfma_rate",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -76,6 +76,7 @@ _SIGS = {
     "fa_forward_splitkv": (_i, [_vp] * 6 + [_i, _i, _i, _i, _i, _f, _i, _i, _vp, _i]),
     "fa_quantize_fp8": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "fa_forward_fp8": (_i, [_vp] * 7 + [_i, _i, _i, _i, _f, _i, _vp]),
+    "fa_probe_mfma_rate": (_i, [_vp, _vp, _i, _i, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
     "fa_version": (ctypes.c_char_p, []),
 }
@@ -457,6 +458,21 @@ def dropout_mask(seed, b, h, H, dropout_p, row0, col0, rows, cols, device="cuda"
     st = lib().fa_dropout_mask(int(seed), b, h, H, float(dropout_p), row0, col0, rows, cols,
                                out.data_ptr(), _stream(out))
     _check(st, "fa_dropout_mask")
+    return out
+
+
+def probe_mfma_rate(operands, blocks, iters, out=None):
+    """Runs the matrix-core rate probe (fa_probe_mfma_rate) on `operands`, a
+    contiguous bf16 CUDA tensor of 16 * 64 * 8 elements (16 fragments of 64
+    lanes x 8 values). Returns the per-lane sums, float32 [blocks * 256]."""
+    torch = _torch()
+    if (operands.dtype != torch.bfloat16 or operands.numel() != 16 * 64 * 8
+            or operands.device.type != "cuda" or not operands.is_contiguous()):
+        raise ValueError("operands must be a contiguous CUDA bfloat16 tensor of 8192 elements")
+    out = _out(out, (blocks * 256,), torch.float32, operands, "out")
+    st = lib().fa_probe_mfma_rate(operands.data_ptr(), out.data_ptr(), int(blocks), int(iters),
+                                  _stream(operands))
+    _check(st, "fa_probe_mfma_rate")
     return out
 
 

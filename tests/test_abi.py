@@ -250,3 +250,15 @@ def test_fp8_rejects():
     assert L.fa_forward_fp8(*a) == ARG          # scale
     a = list(args); a[0] = 0
     assert L.fa_forward_fp8(*a) == NULL
+
+
+def test_probe_rejects():
+    L = fa.lib()
+    assert L.fa_probe_mfma_rate(0, P, 1, 1, None) == NULL
+    assert L.fa_probe_mfma_rate(P, 0, 1, 1, None) == NULL
+    assert L.fa_probe_mfma_rate(P + 4, P, 1, 1, None) == ALIGN
+    assert L.fa_probe_mfma_rate(P, P + 8, 1, 1, None) == ALIGN
+    assert L.fa_probe_mfma_rate(P, P, 0, 1, None) == ARG
+    assert L.fa_probe_mfma_rate(P, P, 65537, 1, None) == ARG
+    assert L.fa_probe_mfma_rate(P, P, 1, 0, None) == ARG
+    assert L.fa_probe_mfma_rate(P, P, 1, (1 << 24) + 1, None) == ARG
