@@ -41,11 +41,22 @@ PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector peak (published; counts pa
 METRIC = "attention fwd+bwd TFLOP/s & % of bf16 MFMA peak, causal, N=8K/32K"
 
 
+# --fill: every input element set to this value instead of the seeded draws
+# (same shapes and work; used to show how much of the kernel time depends on
+# the data the matrix cores multiply). None = the workload's own inputs.
+FILL = None
+
+
 def _device_inputs(w, torch):
     inp = make_inputs(w, with_grad=True)
     if w.dtype == "f32":
-        return {k: torch.from_numpy(v[0]).cuda() for k, v in inp.items()}
-    return {k: torch.from_numpy(v[0].view(np.int16)).view(torch.bfloat16).cuda() for k, v in inp.items()}
+        dev = {k: torch.from_numpy(v[0]).cuda() for k, v in inp.items()}
+    else:
+        dev = {k: torch.from_numpy(v[0].view(np.int16)).view(torch.bfloat16).cuda() for k, v in inp.items()}
+    if FILL is not None:
+        for t in dev.values():
+            t.fill_(FILL)
+    return dev
 
 
 def kernel_units(w):
@@ -469,10 +480,15 @@ def main():
     ap.add_argument("--also-fp8", type=int, nargs="*", default=[3])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fill", type=float, default=None, metavar="VALUE",
+                    help="set every input element to VALUE instead of the seeded N(0,1) draws "
+                         "(power analysis only; the line's data field says so)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes (three times), "
                          "the reference kernel for scaling HBM traffic counters, and exit")
     a = ap.parse_args()
+    global FILL
+    FILL = a.fill
     if a.gpus != 1:
         print("bench.py measures one GPU: the attention kernels run on a single device and this build "
               "has no multi-GPU path (heads or sequence chunks would be sharded across GPUs); "
@@ -511,7 +527,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32" if w.dtype == "f32" else "bf16",
-        "data": "synthetic",
+        "data": "synthetic" if a.fill is None else f"synthetic, every input element {a.fill}",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "dropout_p": w.dropout_p, "global_batch": w.B, "seq_len": w.N,
                    "parallelism": "single-gpu"},
