@@ -34,8 +34,12 @@ int check_problem(int B, int H, int N, int d, int dtype) {
   // Element count must fit comfortably in 64-bit byte offsets, and grids
   // (at most one work-group per 16 rows, or per 32-row block per head) in
   // 32 bits.
-  const int64_t rows = (int64_t)B * N * H;
-  if (rows > (int64_t)1 << 36) return FA_ERR_SHAPE;
+  // B * N fits in 64 bits; comparing it with 2^36 / H decides
+  // B * N * H > 2^36 without forming a product that could overflow. Every
+  // product below is then bounded by the row count.
+  const int64_t bn = (int64_t)B * N;
+  if (bn > ((int64_t)1 << 36) / H) return FA_ERR_SHAPE;
+  const int64_t rows = bn * H;
   if ((rows + 15) / 16 > (int64_t)INT32_MAX) return FA_ERR_SHAPE;
   if ((int64_t)((N + 31) / 32) * B * H > (int64_t)INT32_MAX) return FA_ERR_SHAPE;
   // The kernels address one batch item's rows with 32-bit byte offsets.

@@ -262,3 +262,13 @@ def test_probe_rejects():
     assert L.fa_probe_mfma_rate(P, P, 65537, 1, None) == ARG
     assert L.fa_probe_mfma_rate(P, P, 1, 0, None) == ARG
     assert L.fa_probe_mfma_rate(P, P, 1, (1 << 24) + 1, None) == ARG
+
+
+def test_shape_products_that_overflow_64_bits_are_rejected():
+    # B * N * H of three 2^31 - 1 values exceeds 2^63: rejected before any
+    # product is formed.
+    L = fa.lib()
+    big = 2147483647
+    assert L.fa_forward(P, P, P, P, P, big, big, big, 128, 0.1, 0, 0.0, 0, None, 1) == SHAPE
+    assert L.fa_backward_workspace_bytes(big, big, big, 128) == 0
+    assert L.fa_forward_splitkv_workspace_bytes(big, big, big, 128, 8) == 0
