@@ -19,6 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB_PATH = os.path.join(HERE, "libfa.so")
+POISON_LIB_PATH = os.path.join(HERE, "libfa_poison.so")  # race-detection build, tests only
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_probe.hip"]
 ARCH = "gfx950"
 
@@ -63,10 +64,8 @@ def _run(cmd, verbose):
     return out
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compiles every source and links libfa.so; returns its path."""
+def _build_lib(out_path: str, flags, verbose: bool) -> None:
     cc = hipcc()
-    flags = COMMON_FLAGS + list(extra_flags or [])
     tmp = tempfile.mkdtemp(prefix="fa_build_")
     try:
         objs = []
@@ -79,11 +78,24 @@ def build(verbose: bool = False, extra_flags=None) -> str:
                 jobs.append(ex.submit(_run, cmd, verbose))
             for j in jobs:
                 j.result()
-        out_tmp = LIB_PATH + ".tmp"
+        out_tmp = out_path + ".tmp"
         _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp] + objs, verbose)
-        os.replace(out_tmp, LIB_PATH)
+        os.replace(out_tmp, out_path)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compiles every source and links libfa.so, and the race-detection
+    build libfa_poison.so (the same sources with -DFA_LDS_POISON: LDS stages
+    are filled with NaN bytes between their last read and the next tile's
+    loads); returns the path of libfa.so."""
+    flags = COMMON_FLAGS + list(extra_flags or [])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=2) as ex:
+        jobs = [ex.submit(_build_lib, LIB_PATH, flags, verbose),
+                ex.submit(_build_lib, POISON_LIB_PATH, flags + ["-DFA_LDS_POISON"], verbose)]
+        for j in jobs:
+            j.result()
     return LIB_PATH
 
 

@@ -383,6 +383,7 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdP
                   char* nxt, float* lsn, float* ddn, uint32_t* arn, int t) {
     wait_vmem();
     __syncthreads();
+    if constexpr (kLdsPoison) poison_stage(nxt, C::STAGE, gt, C::NT);
     const bool valid = QG == 1 || t < ntiles;  // one group: every step has a tile
     const int qt0 = valid ? tile_start(t) : 0;
     const bool more = t + QG < ntiles;
@@ -467,6 +468,7 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdP
   };
 
   const int nsteps = (ntiles + QG - 1) / QG;  // the same count for every group
+  if constexpr (kLdsPoison) poison_stage(st0[qg], C::STAGE, gt, C::NT);
   if (qg < ntiles) {
     stat_load(tile_start(qg));
     issue(st0[qg], tile_start(qg));
@@ -661,6 +663,7 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
   auto step = [&](const char* cur, const uint32_t* bcc, char* nxt, uint32_t* bcn, int t) {
     wait_vmem();
     __syncthreads();
+    if constexpr (kLdsPoison) poison_stage(nxt, C::STAGE, tid, C::NT);
     const int k0 = tile_start(t);
     if (t + 1 < ntiles) issue(nxt, bcn, tile_start(t + 1));
     if (CAUSAL && k0 > qw0 + 31) return;
@@ -714,6 +717,7 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
     sched_lds_ahead<2 * C::NDB, 2, 1, DROP ? 4 : 0>();
   };
 
+  if constexpr (kLdsPoison) poison_stage(st0, C::STAGE, tid, C::NT);
   if (ntiles > 0) issue(st0, bc0, tile_start(0));
   for (int t = 0; t < ntiles; t += 2) {
     step(st0, bc0, st1, bc1, t);

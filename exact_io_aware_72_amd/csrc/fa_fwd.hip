@@ -293,6 +293,7 @@ __attribute__((amdgpu_waves_per_eu(1, (D == 64 && !FP8) ? 4 : 2))) void fwd_bf16
     // barrier nobody reads `nxt` any more, so the next tile can go there.
     wait_vmem();
     __syncthreads();
+    if constexpr (kLdsPoison) poison_stage(nxt, C::STAGE, tid, C::NT);
     const int k0 = tile_start(t);
     // Exponent coefficient of this tile (FP8: times the two block scales).
     const float c2t = FP8 ? c2 * qsc * ksn : c2;
@@ -427,6 +428,7 @@ __attribute__((amdgpu_waves_per_eu(1, (D == 64 && !FP8) ? 4 : 2))) void fwd_bf16
     }
   };
 
+  if constexpr (kLdsPoison) poison_stage(st0, C::STAGE, tid, C::NT);
   if (ntiles > 0) issue(st0, ck0, tile_start(0));
   for (int t = 0; t < ntiles; t += 2) {
     step(st0, ck0, st1, ck1, t);

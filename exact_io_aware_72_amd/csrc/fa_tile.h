@@ -122,6 +122,27 @@ __device__ __forceinline__ u32x2 ld_lds_tr16(const char* base, int off) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Race-detection builds (-DFA_LDS_POISON): once every wave is past the
+// barrier after its last read of an LDS stage, and before the next tile's
+// loads into that stage are issued, the stage is filled with all-ones bytes
+// (NaN as bf16 and as fp32). A read that runs ahead of those loads, or a
+// stage reused too early, then shows up as NaN outputs instead of stale but
+// plausible values. Regular builds compile this to nothing.
+#ifdef FA_LDS_POISON
+constexpr bool kLdsPoison = true;
+#else
+constexpr bool kLdsPoison = false;
+#endif
+// Every thread of the work-group must call this (it ends with a barrier);
+// threads tid = 0 .. nt-1 fill `bytes` bytes (a multiple of 16) at `stage`.
+__device__ __forceinline__ void poison_stage(char* stage, int bytes, int tid, int nt) {
+  if constexpr (kLdsPoison) {
+    for (int i = tid; i < bytes / 16; i += nt)
+      reinterpret_cast<u32x4*>(stage)[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+    __syncthreads();  // stored before any wave issues its loads into the stage
+  }
+}
+
 // Waits for this wave's outstanding global loads (direct-to-LDS included)
 // and nothing else: s_waitcnt vmcnt(0) with expcnt and lgkmcnt at maximum.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
