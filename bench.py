@@ -78,7 +78,7 @@ def kernel_units(w):
     }
 
 
-def run_gpu(w, steps, warmup, torch, fa):
+def run_gpu(w, steps, warmup, torch, fa, keep_outputs=False):
     """One step = fa_forward, then (for workloads with a backward pass) the
     D preprocess, dK/dV and dQ kernels; HIP events between the calls time
     each kernel."""
@@ -133,6 +133,8 @@ def run_gpu(w, steps, warmup, torch, fa):
         "fwd_tflops": fwd_f / (fwd_ms * 1e-3) / 1e12,
         "bwd_tflops": bwd_f / (bwd_ms * 1e-3) / 1e12 if w.backward else None,
         "kernel_ms": per,
+        "outputs": ({"O": o, "LSE": lse, "dQ": dq, "dK": dk, "dV": dv} if w.backward else
+                    {"O": o, "LSE": lse}) if keep_outputs else None,
     }
 
 
@@ -440,9 +442,13 @@ def roofline(w, kernel_ms):
             "traffic_detail": rec}
 
 
-def cpu_baseline(w, seconds):
+def cpu_baseline(w, seconds, gpu_out=None):
     """The fp64 oracle (as it stands) on whole heads of the same workload,
-    one head at a time until about `seconds` have passed."""
+    one head at a time until about `seconds` have passed. With `gpu_out`
+    (the timed run's output tensors), each head the oracle computed is also
+    compared with the GPU's, element by element, outside the timed region:
+    max and mean absolute error per tensor against the bar (bf16: 2e-2 and
+    1e-3; fp32: 1e-5)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -452,22 +458,41 @@ def cpu_baseline(w, seconds):
     inp = make_inputs(w, with_grad=True)
     vals = {k: v[1] for k, v in inp.items()}
     fwd_f, bwd_f = counted_flops(1, 1, w.N, w.d, w.causal, True)
-    done, t0 = 0, time.perf_counter()
+    done, el = 0, 0.0
+    err = {}  # name -> [max abs, sum abs, count]
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    for bh in heads:
-        oracle.forward(vals["q"], vals["k"], vals["v"], w.scale, w.causal, w.dropout_p, w.dropout_seed,
-                       heads=[bh])
-        oracle.backward(vals["q"], vals["k"], vals["v"], vals["do"], w.scale, w.causal, w.dropout_p,
-                        w.dropout_seed, heads=[bh], check_d=False)
+    for b, h in heads:
+        t0 = time.perf_counter()
+        o, lse = oracle.forward(vals["q"], vals["k"], vals["v"], w.scale, w.causal, w.dropout_p,
+                                w.dropout_seed, heads=[(b, h)])
+        dq, dk, dv, _ = oracle.backward(vals["q"], vals["k"], vals["v"], vals["do"], w.scale, w.causal,
+                                        w.dropout_p, w.dropout_seed, heads=[(b, h)], check_d=False)
+        el += time.perf_counter() - t0
         done += 1
-        if time.perf_counter() - t0 >= seconds:
+        if gpu_out is not None:
+            ref = {"O": o[b, :, h], "LSE": lse[b, h], "dQ": dq[b, :, h], "dK": dk[b, :, h], "dV": dv[b, :, h]}
+            for name, t in gpu_out.items():
+                g = (t[b, h] if name == "LSE" else t[b, :, h]).float().cpu().numpy().astype(np.float64)
+                e = np.abs(g - ref[name])
+                acc = err.setdefault(name, [0.0, 0.0, 0])
+                acc[0] = max(acc[0], float(e.max()))
+                acc[1] += float(e.sum())
+                acc[2] += e.size
+        if el >= seconds:
             break
-    el = time.perf_counter() - t0
-    return {"value": done * (fwd_f + bwd_f) / el / 1e12, "unit": "TFLOP/s",
-            "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {len(heads)} heads (full N={w.N}, fwd+bwd, fp64 numpy) in {el:.1f} s",
-            "host_cpus": len(os.sched_getaffinity(0))}
-
+    res = {"value": done * (fwd_f + bwd_f) / el / 1e12, "unit": "TFLOP/s",
+           "cores": threads, "kind": "oracle",
+           "sample": f"{done} of {len(heads)} heads (full N={w.N}, fwd+bwd, fp64 numpy) in {el:.1f} s",
+           "host_cpus": len(os.sched_getaffinity(0))}
+    if gpu_out is not None:
+        max_tol, mean_tol = (1e-5, None) if w.dtype == "f32" else (2e-2, 1e-3)
+        per = {n: {"max_abs": a[0], "mean_abs": a[1] / a[2]} for n, a in err.items()}
+        res["parity"] = {
+            "heads": done, "tensors": per, "max_abs_bar": max_tol, "mean_abs_bar": mean_tol,
+            "within": all(v["max_abs"] <= max_tol and (mean_tol is None or v["mean_abs"] <= mean_tol)
+                          for v in per.values()),
+        }
+    return res
 
 def main():
     ap = argparse.ArgumentParser()
@@ -516,7 +541,7 @@ def main():
         return
 
     w = WORKLOADS[a.workload]
-    r = run_gpu(w, a.steps, a.warmup, torch, fa)
+    r = run_gpu(w, a.steps, a.warmup, torch, fa, keep_outputs=not a.no_cpu_baseline and a.fill is None)
     line = {
         "metric": METRIC,
         "value": r["tflops"],
@@ -568,7 +593,7 @@ def main():
         # against the fastest timed launch: the highest rate the matrix cores
         # sustained on this data in the run
         _add_ceiling_frac(entry, line["mfma_ceiling"]["random_operands_tflops_best"])
-    line["cpu_baseline"] = None if a.no_cpu_baseline else cpu_baseline(w, a.cpu_seconds)
+    line["cpu_baseline"] = None if a.no_cpu_baseline else cpu_baseline(w, a.cpu_seconds, r["outputs"])
     print(json.dumps(line), flush=True)
 
 
