@@ -442,6 +442,17 @@ def roofline(w, kernel_ms):
             "traffic_detail": rec}
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, seconds, gpu_out=None):
     """The fp64 oracle (as it stands) on whole heads of the same workload,
     one head at a time until about `seconds` have passed. With `gpu_out`
@@ -483,7 +494,7 @@ def cpu_baseline(w, seconds, gpu_out=None):
     res = {"value": done * (fwd_f + bwd_f) / el / 1e12, "unit": "TFLOP/s",
            "cores": threads, "kind": "oracle",
            "sample": f"{done} of {len(heads)} heads (full N={w.N}, fwd+bwd, fp64 numpy) in {el:.1f} s",
-           "host_cpus": len(os.sched_getaffinity(0))}
+           "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model()}
     if gpu_out is not None:
         max_tol, mean_tol = (1e-5, None) if w.dtype == "f32" else (2e-2, 1e-3)
         per = {n: {"max_abs": a[0], "mean_abs": a[1] / a[2]} for n, a in err.items()}
