@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB_PATH = os.path.join(HERE, "libfa.so")
 POISON_LIB_PATH = os.path.join(HERE, "libfa_poison.so")  # race-detection build, tests only
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_probe.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

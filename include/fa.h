@@ -30,7 +30,9 @@
  *     dtype FA_BF16 (bf16 storage, fp32 accumulation, bf16 matrix cores) or
  *     FA_F32 (fp32 throughout). Causal masking keeps key j for query i iff
  *     j <= i (queries and keys share positions 0..N-1).
- *   - Dropout: 0 <= dropout_p < 1. Probabilities are dropped after the
+ *   - Dropout: dropout_p = 0 or 2^-16 <= dropout_p < 1 (the draws have 16
+ *     bits, so a smaller nonzero p could drop nothing; it is rejected with
+ *     FA_ERR_DROPOUT). Probabilities are dropped after the
  *     softmax normalisation with the keep mask of a counter hash of
  *     (seed, b, h, row, col) and kept ones are scaled by 1/(1 - dropout_p);
  *     the logsumexp is that of the undropped probabilities. `seed` is used
@@ -57,7 +59,7 @@ typedef enum {
                               a size that overflows                             */
   FA_ERR_HEADDIM = -3,     /* d not in {64, 80, 128}                             */
   FA_ERR_DTYPE = -4,       /* dtype not FA_F32 / FA_BF16                         */
-  FA_ERR_DROPOUT = -5,     /* dropout_p outside [0, 1) or NaN                    */
+  FA_ERR_DROPOUT = -5,     /* dropout_p NaN, outside [0, 1) or in (0, 2^-16)     */
   FA_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned                   */
   FA_ERR_UNSUPPORTED = -7, /* valid request this build does not implement       */
   FA_ERR_HIP = -8,         /* a HIP runtime call failed; see fa_status_string    */
@@ -272,30 +274,6 @@ const char* fa_status_string(int status);
 /* Library version string, e.g. "fa-mi355x 0.1.0 gfx950". */
 const char* fa_version(void);
 
-/*
- * Measurement aid, not part of the attention path: the sustained rate of the
- * bf16 matrix cores (v_mfma_f32_32x32x16_bf16) on given operand data, with no
- * memory, LDS or vector work in the timed loop. The published dense peak is
- * reached only on low-toggle data; timed on the workload's own value
- * distribution, this gives the matrix-core rate the attention kernels can
- * reach on that data.
- *   operands  device, 16 fragments x 64 lanes x 16 bytes = 16 KiB of bf16
- *             (8 bf16 per 16-byte entry); lane L of every wave reads entry
- *             f*64 + L of fragment f. Fragments 0..7 are A_0..A_7, 8..15 are
- *             B_0..B_7.
- *   out       device float[blocks * 256]: per lane, the sum of its
- *             accumulator registers. Summed over the 64 lanes of a wave this
- *             is iters * sum_i (sum of all elements of A_i B_i and of
- *             B_i A_{(i+1) mod 8}), with fragments laid out as the matrix-core
- *             A operand (lane L: row L%32, columns 8*(L/32)..+7) and B operand
- *             (lane L: column L%32, rows 8*(L/32)..+7).
- *   blocks    work-groups of 4 waves, 1 <= blocks <= 65536
- *   iters     loop trips of 16 products each, 1 <= iters <= 2^24
- * Work: blocks * 4 * iters * 16 * 32768 floating-point operations.
- * Errors: FA_ERR_NULL, FA_ERR_ALIGN (16 bytes), FA_ERR_ARG (blocks or iters
- * out of range), FA_ERR_HIP.
- */
-int fa_probe_mfma_rate(const void* operands, float* out, int blocks, int iters, void* stream);
 
 #ifdef __cplusplus
 }

@@ -68,6 +68,8 @@ def _fwd(**kw):
     (dict(d=32), HEADDIM), (dict(d=96), HEADDIM), (dict(d=256), HEADDIM),
     (dict(dtype=2), DTYPE), (dict(dtype=-1), DTYPE),
     (dict(p=1.0), DROPOUT), (dict(p=-0.1), DROPOUT), (dict(p=float("nan")), DROPOUT), (dict(p=1.5), DROPOUT),
+    # below the 16-bit draws' resolution: nothing would be dropped, yet O rescaled
+    (dict(p=1e-6), DROPOUT), (dict(p=2.0 ** -16 * 0.999), DROPOUT), (dict(p=1e-45), DROPOUT),
     (dict(scale=float("inf")), ARG), (dict(scale=float("nan")), ARG), (dict(scale=0.0), ARG),
     (dict(scale=-0.125), ARG),
 ])
@@ -106,6 +108,7 @@ def test_backward_rejects():
 @pytest.mark.parametrize("args,status", [
     ((1, 0, 0, 1, 0.1, 0, 0, 4, 4, 0, None), NULL),
     ((1, 0, 0, 1, 1.0, 0, 0, 4, 4, P, None), DROPOUT),
+    ((1, 0, 0, 1, 1e-6, 0, 0, 4, 4, P, None), DROPOUT),  # in (0, 2^-16)
     ((1, 0, 1, 1, 0.1, 0, 0, 4, 4, P, None), ARG),      # h >= H
     ((1, -1, 0, 1, 0.1, 0, 0, 4, 4, P, None), ARG),     # b < 0
     ((1, 0, 0, 1, 0.1, -1, 0, 4, 4, P, None), ARG),     # row0 < 0
@@ -250,18 +253,6 @@ def test_fp8_rejects():
     assert L.fa_forward_fp8(*a) == ARG          # scale
     a = list(args); a[0] = 0
     assert L.fa_forward_fp8(*a) == NULL
-
-
-def test_probe_rejects():
-    L = fa.lib()
-    assert L.fa_probe_mfma_rate(0, P, 1, 1, None) == NULL
-    assert L.fa_probe_mfma_rate(P, 0, 1, 1, None) == NULL
-    assert L.fa_probe_mfma_rate(P + 4, P, 1, 1, None) == ALIGN
-    assert L.fa_probe_mfma_rate(P, P + 8, 1, 1, None) == ALIGN
-    assert L.fa_probe_mfma_rate(P, P, 0, 1, None) == ARG
-    assert L.fa_probe_mfma_rate(P, P, 65537, 1, None) == ARG
-    assert L.fa_probe_mfma_rate(P, P, 1, 0, None) == ARG
-    assert L.fa_probe_mfma_rate(P, P, 1, (1 << 24) + 1, None) == ARG
 
 
 def test_shape_products_that_overflow_64_bits_are_rejected():
