@@ -19,10 +19,10 @@ import os
 __all__ = [
     "FAError", "lib", "lib_path", "version", "forward", "backward", "backward_preprocess",
     "backward_dkdv", "backward_dq", "workspace_bytes", "dropout_mask", "FlashAttnFunction",
-    "flash_attention", "forward_varlen", "backward_varlen", "varlen_workspace_bytes",
+    "flash_attention", "draw_seed", "forward_varlen", "backward_varlen", "varlen_workspace_bytes",
     "forward_blocksparse", "backward_blocksparse", "BLOCK",
     "forward_splitkv", "splitkv_num_splits", "splitkv_workspace_bytes",
-    "quantize_fp8", "forward_fp8", "forward_fp8_quantized", "probe_mfma_rate",
+    "quantize_fp8", "forward_fp8", "forward_fp8_quantized",
     "EXPORTED_SYMBOLS", "STATUS",
 ]
 
@@ -38,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "fa_forward_varlen", "fa_backward_varlen", "fa_backward_varlen_workspace_bytes",
     "fa_forward_blocksparse", "fa_backward_blocksparse",
     "fa_splitkv_num_splits", "fa_forward_splitkv_workspace_bytes", "fa_forward_splitkv",
-    "fa_quantize_fp8", "fa_forward_fp8", "fa_probe_mfma_rate",
+    "fa_quantize_fp8", "fa_forward_fp8",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -76,7 +76,6 @@ _SIGS = {
     "fa_forward_splitkv": (_i, [_vp] * 6 + [_i, _i, _i, _i, _i, _f, _i, _i, _vp, _i]),
     "fa_quantize_fp8": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "fa_forward_fp8": (_i, [_vp] * 7 + [_i, _i, _i, _i, _f, _i, _vp]),
-    "fa_probe_mfma_rate": (_i, [_vp, _vp, _i, _i, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
     "fa_version": (ctypes.c_char_p, []),
 }
@@ -461,34 +460,26 @@ def dropout_mask(seed, b, h, H, dropout_p, row0, col0, rows, cols, device="cuda"
     return out
 
 
-def probe_mfma_rate(operands, blocks, iters, out=None):
-    """Runs the matrix-core rate probe (fa_probe_mfma_rate) on `operands`, a
-    contiguous bf16 CUDA tensor of 16 * 64 * 8 elements (16 fragments of 64
-    lanes x 8 values). Returns the per-lane sums, float32 [blocks * 256]."""
-    torch = _torch()
-    if (operands.dtype != torch.bfloat16 or operands.numel() != 16 * 64 * 8
-            or operands.device.type != "cuda" or not operands.is_contiguous()):
-        raise ValueError("operands must be a contiguous CUDA bfloat16 tensor of 8192 elements")
-    out = _out(out, (blocks * 256,), torch.float32, operands, "out")
-    st = lib().fa_probe_mfma_rate(operands.data_ptr(), out.data_ptr(), int(blocks), int(iters),
-                                  _stream(operands))
-    _check(st, "fa_probe_mfma_rate")
-    return out
-
-
 def _autograd_function():
     torch = _torch()
 
     class FlashAttnFunction(torch.autograd.Function):
         """Autograd wrapper: forward saves (q, k, v, o, lse); backward
-        recomputes the attention probabilities from them."""
+        recomputes the attention probabilities from them. With dropout and
+        seed=None, each forward call draws a fresh seed (draw_seed), so
+        every call gets a new keep mask; the seed is kept on the autograd
+        node (its `seed` attribute) and the backward pass regenerates the
+        same mask from it."""
 
         @staticmethod
-        def forward(ctx, q, k, v, causal=False, dropout_p=0.0, seed=0, scale=None):
+        def forward(ctx, q, k, v, causal=False, dropout_p=0.0, seed=None, scale=None):
             q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+            if seed is None:
+                seed = draw_seed() if dropout_p > 0 else 0
             o, lse = forward(q, k, v, causal, dropout_p, seed, scale)
             ctx.save_for_backward(q, k, v, o, lse)
             ctx.args = (causal, dropout_p, seed, scale)
+            ctx.seed = seed
             return o
 
         @staticmethod
@@ -520,7 +511,16 @@ def __getattr__(name):
     raise AttributeError(name)
 
 
-def flash_attention(q, k, v, causal=False, dropout_p=0.0, seed=0, scale=None):
+def draw_seed():
+    """A dropout seed in [0, 2^63) drawn from torch's default CPU generator
+    (reproducible under torch.manual_seed)."""
+    torch = _torch()
+    return int(torch.randint(0, 2 ** 63 - 1, (1,), dtype=torch.int64).item())
+
+
+def flash_attention(q, k, v, causal=False, dropout_p=0.0, seed=None, scale=None):
     """O = softmax(q k^T * scale) v over (batch, seq_len, num_heads, head_dim)
-    tensors, differentiable through FlashAttnFunction."""
+    tensors, differentiable through FlashAttnFunction. With dropout and
+    seed=None every call draws a fresh seed (see FlashAttnFunction); pass a
+    seed to fix the keep mask."""
     return _Namespace.FlashAttnFunction.apply(q, k, v, causal, dropout_p, seed, scale)

@@ -48,8 +48,11 @@ int check_problem(int B, int H, int N, int d, int dtype) {
   return FA_OK;
 }
 
+// The keep decision compares 16-bit draws with floor(p * 2^16): a p in
+// (0, 2^-16) would drop nothing yet still rescale, so it is rejected.
 int check_dropout(float p) {
   if (!(p >= 0.0f && p < 1.0f)) return FA_ERR_DROPOUT;  // also rejects NaN
+  if (p > 0.0f && p < 1.0f / 65536.0f) return FA_ERR_DROPOUT;
   return FA_OK;
 }
 

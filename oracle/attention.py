@@ -16,10 +16,10 @@ Definitions followed ("FlashAttention for Efficient Training" unless noted):
     contribute nothing (the -inf masking of section 5.2 "Handling Variable
     Sequence Lengths"; causal use in section 5.1 "Memory-Efficient Backward
     Pass"). Queries and keys share positions 0..N-1 (top-left aligned).
-  * block-sparse: with a mask over 128 x 128 blocks of S, scores in zero
-    blocks are -inf ("Only non-zero blocks ... are computed", section 3.2
-    "Block-Sparse Attention Support"); a row left with no finite score gets
-    P = 0, O = 0 and LSE = -inf
+  * block-sparse: with a mask over 128 x 128 blocks of S, the scores of a
+    zero block are -inf and take no part in the softmax; the page computes
+    only the nonzero blocks (section 3.2 "Block-Sparse Attention Support").
+    A row left with no finite score gets P = 0, O = 0 and LSE = -inf
   * queries against a longer key sequence (forward_cross): under the causal
     mask the Nq queries are the last Nq of the Nk positions (a reading; the
     pages only use queries and keys of one length)

@@ -90,10 +90,13 @@ def pair_keys(key: int, pairs):
 
 
 def keep_threshold(p: float) -> int:
-    """T = floor(p_f32 * 2^16), exact in float64."""
+    """T = floor(p_f32 * 2^16), exact in float64. A p in (0, 2^-16) would
+    give T = 0 (nothing dropped, yet kept values rescaled) and is rejected."""
     pf = float(np.float32(p))
     if not (0.0 <= pf < 1.0):
         raise ValueError("dropout probability must lie in [0, 1)")
+    if 0.0 < pf < 2.0 ** -16:
+        raise ValueError("dropout probability below 2^-16, the draws' resolution")
     return int(np.floor(pf * 65536.0))
 
 

@@ -65,8 +65,73 @@ def test_threshold_for_p_0_1():
     assert DH.keep_threshold(0.0) == 0
     assert DH.keep_threshold(0.5) == 32768
     assert DH.keep_threshold(float(np.float32(1.0) - np.float32(2.0 ** -24))) == 65535
+    assert DH.keep_threshold(2.0 ** -16) == 1
     with pytest.raises(ValueError):
         DH.keep_threshold(1.0)
+    # below the draws' resolution a nonzero p would drop nothing: rejected
+    for p in (1e-6, 2.0 ** -17, 2.0 ** -16 * 0.999):
+        with pytest.raises(ValueError):
+            DH.keep_threshold(p)
+
+
+@pytest.mark.parametrize("p", [2.0 ** -16, 0.001, 0.1, 0.25, 0.5, 0.9])
+def test_keep_rate_times_rescale(p):
+    """Kept values are scaled by 1/(1 - p) (the float32 value the kernels
+    use), the keep probability is 1 - T/2^16 with T = floor(p 2^16), so the
+    expected dropped probability is (keep rate) * (rescale) times P. That
+    factor is within 2^-16 / (1 - p) of 1 (the 16-bit draws' resolution; at
+    p = 0.1 it is 1.0000102), and an empirical keep rate over 4M draws
+    matches 1 - T/2^16."""
+    pf = float(np.float32(p))
+    t = DH.keep_threshold(p)
+    keep = 1.0 - t / 65536.0
+    rescale = float(np.float32(1.0 / (1.0 - pf)))
+    # lower end: the float32 rounding of 1/(1 - p) (at most 2^-24 relative)
+    assert -2.0 ** -23 <= keep * rescale - 1.0 <= 2.0 ** -16 / (1.0 - pf) + 1e-7
+    m = DH.keep_mask(31, 0, 0, 1, p, np.arange(2048), np.arange(2048))
+    sigma = np.sqrt(max(keep * (1 - keep), 1e-12) / m.size)
+    assert abs(m.mean() - keep) <= 6 * sigma + 2.0 ** -22
+    if p == 0.1:
+        assert abs(keep * rescale - 1.0000102) < 1e-7
+
+
+def test_row_and_pair_keys_do_not_coincide():
+    """Row keys A_i and pair keys B_c come from disjoint counters (odd and
+    even multiples of G past the head key). Over the N = 65536 dropout
+    workload's index ranges (seed 2026, 8 heads, rows < 65536, pairs <
+    32768) the two key sets share only the chance coincidences of 32-bit
+    values (about 0.5 per head expected), and no row key equals the pair
+    key of the same index or its neighbours. A derivation slip that aligned
+    the counters (say A_i from 2i + 2) would make A_i = B_i for every i and
+    zero the draws fmix32(0) = 0 of a whole diagonal."""
+    rows, pairs = np.arange(65536), np.arange(32768)
+    for h in range(8):
+        key = DH.head_key(2026, 0, h, 8)
+        a, bk = DH.row_keys(key, rows), DH.pair_keys(key, pairs)
+        assert len(np.intersect1d(a, bk)) <= 8  # Poisson(0.5): P(> 8) < 1e-9
+        for shift in (-1, 0, 1):
+            i = np.arange(max(0, -shift), 32768 - max(0, shift))
+            assert not np.any(a[i] == bk[i + shift])
+
+
+@pytest.mark.parametrize("diag", ["c = i", "c = i // 2 (query's own pair)", "c = 2i"])
+def test_keep_rate_on_diagonals(diag):
+    """The keep rate along systematic diagonals of (row, key pair) equals the
+    rate elsewhere: 65536 decisions per head and diagonal of the N = 65536
+    dropout workload (seed 2026, heads 0 and 5)."""
+    keep = 1.0 - DH.keep_threshold(0.1) / 65536.0
+    for h in (0, 5):
+        key = DH.head_key(2026, 0, h, 8)
+        i = np.arange(32768) if diag != "c = 2i" else np.arange(16384)
+        c = {"c = i": i, "c = i // 2 (query's own pair)": i // 2, "c = 2i": 2 * i}[diag]
+        if diag == "c = i // 2 (query's own pair)":
+            i = np.arange(65536)
+            c = i // 2
+        w = DH.fmix32(DH.row_keys(key, i) ^ DH.pair_keys(key, c))
+        u = np.concatenate([w & np.uint32(0xFFFF), w >> np.uint32(16)])
+        rate = float(np.mean(u >= DH.keep_threshold(0.1)))
+        sigma = np.sqrt(keep * (1 - keep) / u.size)
+        assert abs(rate - keep) <= 6 * sigma, (h, diag, rate)
 
 
 def test_keep_rate_and_independence():

@@ -245,6 +245,38 @@ def test_autograd_function_matches_backward():
     assert torch.equal(q.grad, dq) and torch.equal(k.grad, dk) and torch.equal(v.grad, dv)
 
 
+def test_autograd_dropout_draws_a_fresh_seed_per_call():
+    """flash_attention with dropout and no seed: two calls draw different
+    seeds (different keep masks, so different outputs), each seed is kept on
+    the autograd node, and the gradients equal fa.backward run with that
+    seed; under torch.manual_seed the draws repeat."""
+    w = _case(5, B=1, H=2, N=200)
+    inp = make_inputs(w, with_grad=True)
+    dev, _ = device_inputs(inp, w.dtype)
+    runs = []
+    for _ in range(2):
+        q, k, v = (dev[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
+        o = fa.flash_attention(q, k, v, causal=True, dropout_p=0.1)
+        o.backward(dev["do"])
+        runs.append((o.grad_fn.seed, o.detach(), q.grad, k.grad, v.grad))
+    (s1, o1, *g1), (s2, o2, *_) = runs
+    assert s1 != s2
+    assert not torch.equal(o1, o2)
+    m1 = fa.dropout_mask(s1, 0, 0, 2, 0.1, 0, 0, 200, 200)
+    m2 = fa.dropout_mask(s2, 0, 0, 2, 0.1, 0, 0, 200, 200)
+    assert not torch.equal(m1, m2)
+    o_ref, lse = fa.forward(dev["q"], dev["k"], dev["v"], True, 0.1, s1)
+    g_ref = fa.backward(dev["q"], dev["k"], dev["v"], o_ref, dev["do"], lse, True, 0.1, s1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o_ref)
+    for a, b in zip(g1, g_ref):
+        assert torch.equal(a, b)
+    torch.manual_seed(7)
+    a = fa.draw_seed()
+    torch.manual_seed(7)
+    assert fa.draw_seed() == a
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_zero_query_closed_form(causal):
     """Q = 0 gives uniform attention: O_i is the mean of the visible V rows and
