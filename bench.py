@@ -41,21 +41,12 @@ PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector peak (published; counts pa
 METRIC = "attention fwd+bwd TFLOP/s & % of bf16 MFMA peak, causal, N=8K/32K"
 
 
-# --fill: every input element set to this value instead of the seeded draws
-# (same shapes and work; used to show how much of the kernel time depends on
-# the data the matrix cores multiply). None = the workload's own inputs.
-FILL = None
-
-
 def _device_inputs(w, torch):
     inp = make_inputs(w, with_grad=True)
     if w.dtype == "f32":
         dev = {k: torch.from_numpy(v[0]).cuda() for k, v in inp.items()}
     else:
         dev = {k: torch.from_numpy(v[0].view(np.int16)).view(torch.bfloat16).cuda() for k, v in inp.items()}
-    if FILL is not None:
-        for t in dev.values():
-            t.fill_(FILL)
     return dev
 
 
@@ -78,10 +69,83 @@ def kernel_units(w):
     }
 
 
-def run_gpu(w, steps, warmup, torch, fa, keep_outputs=False):
+class ClockSampler:
+    """Graphics clock of the benchmarked GPU while the timed steps run: a host
+    thread reads the power-management firmware's metrics table through
+    amdsmi every `period` seconds (per-XCD current clocks and the firmware's
+    running average) and reports the medians over the samples. The device is
+    matched to torch's current device by PCI address. Reports None with a
+    reason when amdsmi or the metrics table is unavailable."""
+
+    def __init__(self, torch, period=0.002):
+        import threading
+        self.period = period
+        self.samples, self.avg = [], []
+        self.error = None
+        self.handle = None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            prop = torch.cuda.get_device_properties(torch.cuda.current_device())
+            bdf = f"{prop.pci_domain_id:04x}:{prop.pci_bus_id:02x}:{prop.pci_device_id:02x}.0"
+            self.handle = amdsmi.amdsmi_get_processor_handle_from_bdf(bdf)
+            self.bdf = bdf
+            self._smi = amdsmi
+            self._read()  # fails here, not in the thread, if the table is unreadable
+            self.samples, self.avg = [], []
+        except Exception as e:  # amdsmi missing, no permission, unknown device
+            self.error = f"{type(e).__name__}: {e}"
+            self.handle = None
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self.handle)
+        per_xcd = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        if not per_xcd and isinstance(m.get("current_gfxclk"), (int, float)):
+            per_xcd = [m["current_gfxclk"]]
+        if per_xcd:
+            self.samples.append(float(np.mean(per_xcd)))
+        a = m.get("average_gfxclk_frequency")
+        if isinstance(a, (int, float)) and 0 < a < 10000:
+            self.avg.append(float(a))
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self._read()
+            except Exception as e:  # pragma: no cover
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+        if self.handle is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        if not self.samples:
+            return {"mhz": None, "source": "amdsmi gpu metrics", "error": self.error or "no samples"}
+        return {"mhz": float(np.median(self.samples)), "source": "amdsmi gpu metrics: median over "
+                "samples of the mean per-XCD current graphics clock, sampled every "
+                f"{self.period * 1e3:.0f} ms during the timed steps",
+                "samples": len(self.samples), "min_mhz": float(np.min(self.samples)),
+                "max_mhz": float(np.max(self.samples)),
+                "firmware_average_mhz": float(np.median(self.avg)) if self.avg else None,
+                "device_bdf": self.bdf}
+
+
+def run_gpu(w, steps, warmup, torch, fa, keep_outputs=False, sample_clock=False):
     """One step = fa_forward, then (for workloads with a backward pass) the
     D preprocess, dK/dV and dQ kernels; HIP events between the calls time
-    each kernel."""
+    each kernel. Step and pass times are medians over the timed steps;
+    kernel_ms holds each kernel's mean launch time (the roofline's average
+    launch duration) and kernel_ms_median the medians."""
     dev = _device_inputs(w, torch)
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
     o = torch.empty_like(q)
@@ -114,25 +178,40 @@ def run_gpu(w, steps, warmup, torch, fa, keep_outputs=False):
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+    clock = ClockSampler(torch) if sample_clock else None
+    if clock:
+        clock.start()
     t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = evs[0][0].elapsed_time(evs[-1][-1]) / steps
-    per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    clock_info = clock.stop() if clock else None
+    # Per step: first to last event of that step; the line reports the median
+    # step and keeps the mean (first event of the first step to the last of
+    # the last, over the step count) beside it.
+    step_ms = [e[0].elapsed_time(e[-1]) for e in evs]
+    ms_step = float(np.median(step_ms))
+    ms_step_mean = evs[0][0].elapsed_time(evs[-1][-1]) / steps
+    launch = {n: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, n in enumerate(names)}
+    per = {n: float(np.mean(t)) for n, t in launch.items()}
+    per_median = {n: float(np.median(t)) for n, t in launch.items()}
     fwd_f, bwd_f = counted_flops(w.B, w.H, w.N, w.d, w.causal, w.backward)
-    fwd_ms = per["forward"]
-    bwd_ms = per["bwd_preprocess"] + per["bwd_dkdv"] + per["bwd_dq"] if w.backward else None
+    fwd_ms = per_median["forward"]
+    bwd_ms = (per_median["bwd_preprocess"] + per_median["bwd_dkdv"] + per_median["bwd_dq"]
+              if w.backward else None)
     return {
         "ms_per_step": ms_step,
+        "ms_per_step_mean": ms_step_mean,
         "wall_s": wall,
+        "clock": clock_info,
         "tflops": (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12,
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
         "fwd_tflops": fwd_f / (fwd_ms * 1e-3) / 1e12,
         "bwd_tflops": bwd_f / (bwd_ms * 1e-3) / 1e12 if w.backward else None,
         "kernel_ms": per,
+        "kernel_ms_median": per_median,
         "outputs": ({"O": o, "LSE": lse, "dQ": dq, "dK": dk, "dV": dv} if w.backward else
                     {"O": o, "LSE": lse}) if keep_outputs else None,
     }
@@ -345,44 +424,6 @@ def run_gpu_fp8(cfg, steps, warmup, torch, fa):
             "forward_bf16_ms": ms_bf16, "forward_bf16_tflops": fwd_f / (ms_bf16 * 1e-3) / 1e12}
 
 
-def mfma_ceiling(torch, fa, blocks=512, iters=20000, reps=5):
-    """Sustained bf16 matrix-core rate of the probe kernel (fa_probe_mfma_rate:
-    32x32x16 products on register-resident operands, nothing else in the
-    loop) on operands drawn like the workload's inputs (iid N(0,1) rounded to
-    bf16) and on constant operands (all 1.0). 512 work-groups of four waves
-    give two waves per SIMD, the occupancy of the attention kernels. The
-    random-operand rate is what the matrix cores sustain on this data at the
-    chip's power limit; the constant-operand rate shows the instruction stream
-    itself is not the limit. Reports the rate of the median and of the
-    fastest of `reps` timed launches."""
-    rng = np.random.default_rng(2026)
-    res = {"blocks": blocks, "iters": iters,
-           "operands": "16 fragments of 64 lanes x 8 bf16: iid N(0,1) rounded to bf16, or all 1.0"}
-    flops = float(blocks) * 4 * iters * 16 * 32768
-    for label, x in (("random", rng.standard_normal(16 * 64 * 8).astype(np.float32)),
-                     ("constant", np.ones(16 * 64 * 8, np.float32))):
-        ops = torch.from_numpy(x).cuda().to(torch.bfloat16)
-        out = fa.probe_mfma_rate(ops, blocks, 16)  # warm-up
-        torch.cuda.synchronize()
-        times = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fa.probe_mfma_rate(ops, blocks, iters, out=out)
-            e1.record()
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        res[f"{label}_operands_tflops"] = flops / (float(np.median(times)) * 1e-3) / 1e12
-        res[f"{label}_operands_tflops_best"] = flops / (float(np.min(times)) * 1e-3) / 1e12
-    return res
-
-
-def _add_ceiling_frac(entry, ceiling):
-    rl = entry.get("roofline") if isinstance(entry, dict) else None
-    if rl and rl.get("bound") == "mfma" and rl.get("unit") == "TFLOP/s" and rl.get("peak") == PEAK_BF16_TFLOPS:
-        rl["frac_of_data_ceiling"] = rl["achieved"] / ceiling
-
-
 def kernel_source_digest():
     """SHA-256 over the kernel sources (comments and blank lines removed, so
     that only code counts) and the build flags: HBM traffic figures recorded
@@ -392,8 +433,6 @@ def kernel_source_digest():
     from exact_io_aware_72_amd import build as fa_build
     h = hashlib.sha256()
     for name in sorted(os.listdir(fa_build.CSRC)):
-        if name == "fa_probe.hip":  # the matrix-core rate probe, not an attention kernel
-            continue
         with open(os.path.join(fa_build.CSRC, name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -518,15 +557,10 @@ def main():
     ap.add_argument("--also-fp8", type=int, nargs="*", default=[3])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--fill", type=float, default=None, metavar="VALUE",
-                    help="set every input element to VALUE instead of the seeded N(0,1) draws "
-                         "(power analysis only; the line's data field says so)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes (three times), "
                          "the reference kernel for scaling HBM traffic counters, and exit")
     a = ap.parse_args()
-    global FILL
-    FILL = a.fill
     if a.gpus != 1:
         print("bench.py measures one GPU: the attention kernels run on a single device and this build "
               "has no multi-GPU path (heads or sequence chunks would be sharded across GPUs); "
@@ -552,7 +586,7 @@ def main():
         return
 
     w = WORKLOADS[a.workload]
-    r = run_gpu(w, a.steps, a.warmup, torch, fa, keep_outputs=not a.no_cpu_baseline and a.fill is None)
+    r = run_gpu(w, a.steps, a.warmup, torch, fa, keep_outputs=not a.no_cpu_baseline, sample_clock=True)
     line = {
         "metric": METRIC,
         "value": r["tflops"],
@@ -561,11 +595,12 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": r["ms_per_step"],
+        "ms_per_step_mean": r["ms_per_step_mean"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32" if w.dtype == "f32" else "bf16",
-        "data": "synthetic" if a.fill is None else f"synthetic, every input element {a.fill}",
+        "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "dropout_p": w.dropout_p, "global_batch": w.B, "seq_len": w.N,
                    "parallelism": "single-gpu"},
@@ -573,9 +608,10 @@ def main():
         "fwd_ms": r["fwd_ms"], "bwd_ms": r["bwd_ms"],
         "fwd_tflops": r["fwd_tflops"], "bwd_tflops": r["bwd_tflops"],
         "kernel_ms": r["kernel_ms"],
+        "kernel_ms_median": r["kernel_ms_median"],
+        "clock": r["clock"],
         "roofline": roofline(w, r["kernel_ms"]),
     }
-    line["mfma_ceiling"] = mfma_ceiling(torch, fa)
     also = []
     for cfg in a.also:
         wa = WORKLOADS[cfg]
@@ -600,10 +636,6 @@ def main():
         also.append(run_gpu_fp8(cfg, max(5, a.steps // 2), 2, torch, fa))
         torch.cuda.empty_cache()
     line["also"] = also
-    for entry in [line] + also:
-        # against the fastest timed launch: the highest rate the matrix cores
-        # sustained on this data in the run
-        _add_ceiling_frac(entry, line["mfma_ceiling"]["random_operands_tflops_best"])
     line["cpu_baseline"] = None if a.no_cpu_baseline else cpu_baseline(w, a.cpu_seconds, r["outputs"])
     print(json.dumps(line), flush=True)
 
