@@ -69,75 +69,58 @@ def kernel_units(w):
     }
 
 
-class ClockSampler:
-    """Graphics clock of the benchmarked GPU while the timed steps run: a host
-    thread reads the power-management firmware's metrics table through
-    amdsmi every `period` seconds (per-XCD current clocks and the firmware's
-    running average) and reports the medians over the samples. The device is
-    matched to torch's current device by PCI address. Reports None with a
-    reason when amdsmi or the metrics table is unavailable."""
+class ClockStamps:
+    """Mean shader clock of each XCD over the timed steps: clock-stamp
+    kernels (libfa_clock.so, fa_clock_stamp) enqueued on the benchmark's
+    stream right before the first timed step and right after the last one
+    read each XCD's shader-cycle counter (s_memtime) and the fixed 100 MHz
+    real-time counter (s_memrealtime). Per XCD, clock = 100 MHz * cycles /
+    real-time ticks between the two stamps (work-groups matched by the XCD id
+    they read). The stamps lie outside the HIP-event brackets of the steps.
+    Reports None with the reason if the library is missing."""
 
-    def __init__(self, torch, period=0.002):
-        import threading
-        self.period = period
-        self.samples, self.avg = [], []
+    def __init__(self, torch, blocks=8):
+        import ctypes
+        self.torch = torch
+        self.blocks = blocks
         self.error = None
-        self.handle = None
-        self._stop = threading.Event()
-        self._thread = None
+        path = os.path.join(ROOT, "exact_io_aware_72_amd", "libfa_clock.so")
         try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            prop = torch.cuda.get_device_properties(torch.cuda.current_device())
-            bdf = f"{prop.pci_domain_id:04x}:{prop.pci_bus_id:02x}:{prop.pci_device_id:02x}.0"
-            self.handle = amdsmi.amdsmi_get_processor_handle_from_bdf(bdf)
-            self.bdf = bdf
-            self._smi = amdsmi
-            self._read()  # fails here, not in the thread, if the table is unreadable
-            self.samples, self.avg = [], []
-        except Exception as e:  # amdsmi missing, no permission, unknown device
-            self.error = f"{type(e).__name__}: {e}"
-            self.handle = None
+            self.lib = ctypes.CDLL(path)
+            self.lib.fa_clock_stamp.restype = ctypes.c_int
+            self.lib.fa_clock_stamp.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        except OSError as e:
+            self.lib, self.error = None, f"{path}: {e}"
+        self.bufs = [torch.zeros(3 * blocks, dtype=torch.int64, device="cuda") for _ in range(2)]
+        self._ctypes = ctypes
 
-    def _read(self):
-        m = self._smi.amdsmi_get_gpu_metrics_info(self.handle)
-        per_xcd = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
-        if not per_xcd and isinstance(m.get("current_gfxclk"), (int, float)):
-            per_xcd = [m["current_gfxclk"]]
-        if per_xcd:
-            self.samples.append(float(np.mean(per_xcd)))
-        a = m.get("average_gfxclk_frequency")
-        if isinstance(a, (int, float)) and 0 < a < 10000:
-            self.avg.append(float(a))
+    def stamp(self, i):
+        if self.lib is None:
+            return
+        stream = self._ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+        if self.lib.fa_clock_stamp(self.bufs[i].data_ptr(), self.blocks, stream) != 0:
+            self.error = "fa_clock_stamp failed"
 
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                self._read()
-            except Exception as e:  # pragma: no cover
-                self.error = f"{type(e).__name__}: {e}"
-                return
-            self._stop.wait(self.period)
-
-    def start(self):
-        import threading
-        if self.handle is not None:
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
-
-    def stop(self):
-        if self._thread is not None:
-            self._stop.set()
-            self._thread.join()
-        if not self.samples:
-            return {"mhz": None, "source": "amdsmi gpu metrics", "error": self.error or "no samples"}
-        return {"mhz": float(np.median(self.samples)), "source": "amdsmi gpu metrics: median over "
-                "samples of the mean per-XCD current graphics clock, sampled every "
-                f"{self.period * 1e3:.0f} ms during the timed steps",
-                "samples": len(self.samples), "min_mhz": float(np.min(self.samples)),
-                "max_mhz": float(np.max(self.samples)),
-                "firmware_average_mhz": float(np.median(self.avg)) if self.avg else None,
-                "device_bdf": self.bdf}
+    def result(self):
+        """Call after synchronising."""
+        if self.lib is None or self.error:
+            return {"mhz": None, "error": self.error}
+        a, b = (x.cpu().numpy().reshape(-1, 3).astype(np.int64) for x in self.bufs)
+        per = {}
+        for r0 in a:
+            for r1 in b:
+                if r1[0] == r0[0] and int(r0[0]) not in per and r1[2] > r0[2]:
+                    per[int(r0[0])] = 100.0 * float(r1[1] - r0[1]) / float(r1[2] - r0[2])
+        # An XCD that idles between the stamps can stop or reset its cycle
+        # counter (seen on sub-millisecond regions); such readings fall
+        # outside any real clock and are left out of the median.
+        ok = [v for v in per.values() if 100.0 < v < 3000.0]
+        if not ok:
+            return {"mhz": None, "per_xcd_mhz": per, "error": "no plausible per-XCD reading"}
+        return {"mhz": float(np.median(ok)), "per_xcd_mhz": per, "xcds_used": len(ok),
+                "source": "s_memtime cycles / s_memrealtime (100 MHz) ticks per XCD between "
+                          "stamps enqueued before the first and after the last timed step",
+                "region_ms": float(np.median([(r1[2] - r0[2]) / 1e5 for r0, r1 in zip(a, b)]))}
 
 
 def run_gpu(w, steps, warmup, torch, fa, keep_outputs=False, sample_clock=False):
@@ -178,15 +161,17 @@ def run_gpu(w, steps, warmup, torch, fa, keep_outputs=False, sample_clock=False)
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
-    clock = ClockSampler(torch) if sample_clock else None
-    if clock:
-        clock.start()
+    clock = ClockStamps(torch) if sample_clock else None
     t0 = time.perf_counter()
+    if clock:
+        clock.stamp(0)
     for i in range(steps):
         step(evs[i])
+    if clock:
+        clock.stamp(1)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    clock_info = clock.stop() if clock else None
+    clock_info = clock.result() if clock else None
     # Per step: first to last event of that step; the line reports the median
     # step and keeps the mean (first event of the first step to the last of
     # the last, over the step count) beside it.
@@ -615,13 +600,14 @@ def main():
     also = []
     for cfg in a.also:
         wa = WORKLOADS[cfg]
-        ra = run_gpu(wa, max(3, a.steps // 4) if wa.backward else a.steps, 2, torch, fa)
+        ra = run_gpu(wa, max(3, a.steps // 4) if wa.backward else a.steps, 2, torch, fa, sample_clock=True)
         peak = PEAK_FP32_VECTOR_TFLOPS if wa.dtype == "f32" else PEAK_BF16_TFLOPS
         also.append({"workload": wa.name, "dtype": wa.dtype, "passes": "fwd+bwd" if wa.backward else "fwd",
                      "tflops": ra["tflops"], "ms_per_step": ra["ms_per_step"],
                      "pct_of_peak": 100.0 * ra["tflops"] / peak,
                      "fwd_tflops": ra["fwd_tflops"], "bwd_tflops": ra["bwd_tflops"],
-                     "kernel_ms": ra["kernel_ms"], "roofline": roofline(wa, ra["kernel_ms"])})
+                     "kernel_ms": ra["kernel_ms"], "clock": ra["clock"],
+                     "roofline": roofline(wa, ra["kernel_ms"])})
         torch.cuda.empty_cache()
     for name in a.also_varlen:
         also.append(run_gpu_varlen(VARLEN_WORKLOADS[name], max(3, a.steps // 4), 2, torch, fa))

@@ -20,7 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB_PATH = os.path.join(HERE, "libfa.so")
 POISON_LIB_PATH = os.path.join(HERE, "libfa_poison.so")  # race-detection build, tests only
+CLOCK_LIB_PATH = os.path.join(HERE, "libfa_clock.so")    # benchmark clock stamps, not attention
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
+CLOCK_SOURCES = ["clock_stamp.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -64,14 +66,15 @@ def _run(cmd, verbose):
     return out
 
 
-def _build_lib(out_path: str, flags, verbose: bool) -> None:
+def _build_lib(out_path: str, flags, verbose: bool, sources=None) -> None:
     cc = hipcc()
+    sources = SOURCES if sources is None else sources
     tmp = tempfile.mkdtemp(prefix="fa_build_")
     try:
         objs = []
         jobs = []
-        with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-            for src in SOURCES:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(sources)) as ex:
+            for src in sources:
                 obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
                 objs.append(obj)
                 cmd = [cc] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -86,14 +89,16 @@ def _build_lib(out_path: str, flags, verbose: bool) -> None:
 
 
 def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compiles every source and links libfa.so, and the race-detection
-    build libfa_poison.so (the same sources with -DFA_LDS_POISON: LDS stages
-    are filled with NaN bytes between their last read and the next tile's
-    loads); returns the path of libfa.so."""
+    """Compiles every source and links libfa.so, the race-detection build
+    libfa_poison.so (the same sources with -DFA_LDS_POISON: LDS stages are
+    filled with NaN bytes between their last read and the next tile's
+    loads) and the benchmark's clock-stamp library libfa_clock.so; returns
+    the path of libfa.so."""
     flags = COMMON_FLAGS + list(extra_flags or [])
-    with concurrent.futures.ThreadPoolExecutor(max_workers=2) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=3) as ex:
         jobs = [ex.submit(_build_lib, LIB_PATH, flags, verbose),
-                ex.submit(_build_lib, POISON_LIB_PATH, flags + ["-DFA_LDS_POISON"], verbose)]
+                ex.submit(_build_lib, POISON_LIB_PATH, flags + ["-DFA_LDS_POISON"], verbose),
+                ex.submit(_build_lib, CLOCK_LIB_PATH, flags, verbose, CLOCK_SOURCES)]
         for j in jobs:
             j.result()
     return LIB_PATH

@@ -38,6 +38,25 @@ def test_library_exports_every_declared_symbol():
     assert {n for n in exported if n.startswith("fa")} == set(_declared())
 
 
+def test_clock_library_exports_its_header():
+    """libfa_clock.so (benchmark clock stamps) exports what include/fa_clock.h
+    declares, and rejects bad arguments before any HIP call."""
+    import ctypes
+    path = os.path.join(os.path.dirname(fa.lib_path()), "libfa_clock.so")
+    text = open(os.path.join(os.path.dirname(HEADER), "fa_clock.h")).read()
+    declared = set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text))
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert declared == {"fa_clock_stamp"} and declared <= exported
+    L = ctypes.CDLL(path)
+    L.fa_clock_stamp.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert L.fa_clock_stamp(None, 8, None) == -1
+    assert L.fa_clock_stamp(P + 4, 8, None) == -1
+    assert L.fa_clock_stamp(P, 0, None) == -1
+    assert L.fa_clock_stamp(P, 1025, None) == -1
+
+
 def test_version_and_status_strings():
     assert "gfx950" in fa.version()
     L = fa.lib()
