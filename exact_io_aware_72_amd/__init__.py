@@ -22,7 +22,7 @@ __all__ = [
     "flash_attention", "draw_seed", "forward_varlen", "backward_varlen", "varlen_workspace_bytes",
     "forward_blocksparse", "backward_blocksparse", "BLOCK",
     "forward_splitkv", "splitkv_num_splits", "splitkv_workspace_bytes",
-    "quantize_fp8", "forward_fp8", "forward_fp8_quantized",
+    "quantize_fp8", "forward_fp8", "forward_fp8_quantized", "backward_noalloc", "NOALLOC_MAX_ROWS",
     "EXPORTED_SYMBOLS", "STATUS",
 ]
 
@@ -38,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "fa_forward_varlen", "fa_backward_varlen", "fa_backward_varlen_workspace_bytes",
     "fa_forward_blocksparse", "fa_backward_blocksparse",
     "fa_splitkv_num_splits", "fa_forward_splitkv_workspace_bytes", "fa_forward_splitkv",
-    "fa_quantize_fp8", "fa_forward_fp8",
+    "fa_quantize_fp8", "fa_forward_fp8", "fa_backward_noalloc",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +62,7 @@ _SIGS = {
     "fa_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
     "fa_backward_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "fa_backward": (_i, [_vp] * 10 + [_i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
+    "fa_backward_noalloc": (_i, [_vp] * 9 + [_i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
     "fa_backward_preprocess": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _i]),
     "fa_backward_dkdv": (_i, [_vp] * 8 + [_i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
     "fa_backward_dq": (_i, [_vp] * 7 + [_i, _i, _i, _i, _f, _i, _f, _u64, _vp, _i]),
@@ -197,6 +198,28 @@ def backward(q, k, v, o, dout, lse, causal=False, dropout_p=0.0, seed=0, scale=N
                            ws.data_ptr(), B, H, N, d, _scale(scale, d), int(bool(causal)),
                            float(dropout_p), int(seed), _stream(q), _code(q))
     _check(st, "fa_backward")
+    return dq, dk, dv
+
+
+NOALLOC_MAX_ROWS = 1 << 22  # FA_NOALLOC_MAX_ROWS: B * H * N limit of backward_noalloc
+
+
+def backward_noalloc(q, k, v, o, dout, lse, dq, dk, dv, causal=False, dropout_p=0.0, seed=0,
+                     scale=None):
+    """fa_backward_noalloc: the backward pass with D in the library's fixed
+    device array (no workspace, nothing allocated by the library). The
+    caller passes the output buffers; B * H * N <= NOALLOC_MAX_ROWS. Calls
+    that overlap on one GPU race on that array."""
+    torch = _torch()
+    B, N, H, d = _shape(q, k, v, o, dout)
+    _buf(lse, (B, H, N), torch.float32, q, "lse")
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _buf(t, q.shape, q.dtype, q, name)
+    st = lib().fa_backward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), B, H, N, d, _scale(scale, d), int(bool(causal)),
+                                   float(dropout_p), int(seed), _stream(q), _code(q))
+    _check(st, "fa_backward_noalloc")
     return dq, dk, dv
 
 

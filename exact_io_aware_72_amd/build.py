@@ -21,7 +21,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB_PATH = os.path.join(HERE, "libfa.so")
 POISON_LIB_PATH = os.path.join(HERE, "libfa_poison.so")  # race-detection build, tests only
 CLOCK_LIB_PATH = os.path.join(HERE, "libfa_clock.so")    # benchmark clock stamps, not attention
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_noalloc.hip"]
 CLOCK_SOURCES = ["clock_stamp.hip"]
 ARCH = "gfx950"
 

@@ -205,6 +205,22 @@ FA_EXPORT int fa_backward(const void* q, const void* k, const void* v, const voi
   return hip_status(bf16 ? fa::launch_bwd_dq_bf16(a, s) : fa::launch_bwd_dq_f32(a, s));
 }
 
+namespace fa {
+int record_hip_error(hipError_t e) { return hip_status(e); }
+
+// Every check fa_backward makes except the workspace pointer's, for entry
+// points that supply the workspace themselves; no HIP call.
+int check_backward_args(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                        int H, int N, int d, float scale, int causal, float dropout_p,
+                        uint64_t seed, int dtype) {
+  fa::AttnArgs a;
+  FA_TRY(fill_bwd(a, q, k, v, dout, lse, nullptr, B, H, N, d, scale, causal, dropout_p, seed,
+                  dtype));
+  return check_ptrs({q, k, v, o, dout, lse, dq, dk, dv});
+}
+}  // namespace fa
+
 // ---------------------------------------------------------------------------
 // Packed variable-length batches.
 namespace {

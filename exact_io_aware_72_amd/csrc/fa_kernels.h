@@ -70,6 +70,16 @@ hipError_t launch_bwd_dkdv_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkdv_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq_f32(const AttnArgs& a, hipStream_t s);
+// Status code for a failed HIP call, recording its text for fa_status_string
+// (fa_api.cpp).
+int record_hip_error(hipError_t e);
+
+// Argument checks of fa_backward without the workspace (fa_api.cpp).
+int check_backward_args(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                        int H, int N, int d, float scale, int causal, float dropout_p,
+                        uint64_t seed, int dtype);
+
 hipError_t launch_dropout_mask(uint64_t seed, int b, int h, int H, uint32_t threshold, int row0,
                                int col0, int rows, int cols, uint8_t* out, hipStream_t s);
 

@@ -108,6 +108,26 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 float* workspace, int B, int H, int N, int d, float scale,
                 int causal, float dropout_p, uint64_t seed, void* stream, int dtype);
 
+/*
+ * Backward pass without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, results and error codes
+ * as fa_backward, minus `workspace`: D goes to a fixed device array inside
+ * the library, FA_NOALLOC_MAX_ROWS floats (16 MiB) per GPU, held until the
+ * process ends. Requires B*H*N <= FA_NOALLOC_MAX_ROWS (else FA_ERR_SHAPE,
+ * nothing launched). The library allocates nothing. All calls on one GPU
+ * share that GPU's array, which keeps the last call's contents: calls that
+ * overlap on one GPU (different streams, or threads without ordering) race
+ * and must be serialised by the caller. The first call on a device looks up
+ * the array's device address (hipGetSymbolAddress); a failure there returns
+ * FA_ERR_HIP with nothing launched.
+ */
+#define FA_NOALLOC_MAX_ROWS (1 << 22)
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        int B, int H, int N, int d, float scale, int causal,
+                        float dropout_p, uint64_t seed, void* stream, int dtype);
+
 /* Step B1 alone: workspace[b][h][i] = sum_c dout[b][i][h][c] * o[b][i][h][c]
  * in fp32. Same argument rules as fa_backward. */
 int fa_backward_preprocess(const void* o, const void* dout, float* workspace,

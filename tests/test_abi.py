@@ -274,6 +274,23 @@ def test_fp8_rejects():
     assert L.fa_forward_fp8(*a) == NULL
 
 
+def test_backward_noalloc_rejects_before_any_hip_call():
+    L = fa.lib()
+    ok = [P] * 9 + [1, 64, 1 << 16, 128, 0.1, 1, 0.0, 0, None, 1]
+    big = list(ok); big[11] = (1 << 16) + 1  # B * H * N = 2^22 + 64 > FA_NOALLOC_MAX_ROWS
+    assert L.fa_backward_noalloc(*big) == SHAPE
+    a = list(ok); a[0] = 0
+    assert L.fa_backward_noalloc(*a) == NULL
+    a = list(ok); a[8] = P + 2
+    assert L.fa_backward_noalloc(*a) == ALIGN
+    a = list(ok); a[12] = 96
+    assert L.fa_backward_noalloc(*a) == HEADDIM
+    a = list(ok); a[15] = 1e-6
+    assert L.fa_backward_noalloc(*a) == DROPOUT
+    a = list(ok); a[13] = 0.0
+    assert L.fa_backward_noalloc(*a) == ARG
+
+
 def test_shape_products_that_overflow_64_bits_are_rejected():
     # B * N * H of three 2^31 - 1 values exceeds 2^63: rejected before any
     # product is formed.
