@@ -37,7 +37,7 @@ from workloads import (SPARSE_WORKLOADS, SPLITKV_WORKLOADS, VARLEN_WORKLOADS, WO
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 matrix-core peak (published)
-PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector peak (published; counts packed fp32)
+PEAK_FP32_MFMA_TFLOPS = 157.3    # MI355X dense fp32 matrix-core peak (published)
 METRIC = "attention fwd+bwd TFLOP/s & % of bf16 MFMA peak, causal, N=8K/32K"
 
 
@@ -59,8 +59,8 @@ def kernel_units(w):
     elems = w.B * w.H * float(w.N) * w.N / (2.0 if w.causal else 1.0)
     tensor_bytes = w.B * w.N * w.H * w.d * 2
     if w.dtype == "f32":
-        # fp32 runs on the vector ALUs (fused multiply-adds), not the matrix cores
-        return {"forward": ("alu", 2 * 2 * w.d * elems)}
+        # fp32 runs on the fp32 matrix cores (v_mfma_f32_32x32x2_f32)
+        return {"forward": ("mfma_f32", 2 * 2 * w.d * elems)}
     return {
         "forward": ("mfma", 2 * 2 * w.d * elems),
         "bwd_preprocess": ("hbm", 2 * tensor_bytes + 4 * w.B * w.H * w.N),
@@ -455,8 +455,9 @@ def roofline(w, kernel_ms):
     sec = kernel_ms[name] * 1e-3
     if bound == "mfma":
         achieved, peak, unit = work / sec / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
-    elif bound == "alu":
-        achieved, peak, unit = work / sec / 1e12, PEAK_FP32_VECTOR_TFLOPS, "TFLOP/s"
+    elif bound == "mfma_f32":
+        bound = "mfma"
+        achieved, peak, unit = work / sec / 1e12, PEAK_FP32_MFMA_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = work / sec / 1e9, PEAK_HBM_GBS, "GB/s"
     rec = recorded_traffic(w.name, name)
@@ -601,7 +602,7 @@ def main():
     for cfg in a.also:
         wa = WORKLOADS[cfg]
         ra = run_gpu(wa, max(3, a.steps // 4) if wa.backward else a.steps, 2, torch, fa, sample_clock=True)
-        peak = PEAK_FP32_VECTOR_TFLOPS if wa.dtype == "f32" else PEAK_BF16_TFLOPS
+        peak = PEAK_FP32_MFMA_TFLOPS if wa.dtype == "f32" else PEAK_BF16_TFLOPS
         also.append({"workload": wa.name, "dtype": wa.dtype, "passes": "fwd+bwd" if wa.backward else "fwd",
                      "tflops": ra["tflops"], "ms_per_step": ra["ms_per_step"],
                      "pct_of_peak": 100.0 * ra["tflops"] / peak,

@@ -480,13 +480,20 @@ __attribute__((amdgpu_waves_per_eu(1, (D == 64 && !FP8) ? 4 : 2))) void fwd_bf16
 }
 
 // ---------------------------------------------------------------------------
-// fp32 path: the same tiled online softmax on the vector ALUs, sixteen
-// threads per query row (each owns d/16 of the head dimension; a score is
-// summed over the sixteen by four lane exchanges), 8 rows per work-group.
-// Used for fp32 inputs, where the bf16 matrix cores do not apply. Spreading a
-// row over more threads shortens each thread's dependent chain, which is what
-// the small fp32 problems wait on: at B=1 H=1 N=256 d=64 the forward takes
-// 173 us with two threads per row, 75 us with eight and 51 us with sixteen.
+// fp32 path on the fp32 matrix cores (v_mfma_f32_32x32x2_f32). A work-group
+// of eight waves owns 32 query rows of one (batch, head); wave w takes the
+// 32-key tiles w, w + 8, w + 16, ... of the key range, so that even a short
+// sequence spreads over eight waves. Each wave keeps its own running max,
+// sum and output (the online softmax of the bf16 path, rescaled on every
+// tile) and reads its K and V rows from global memory straight into
+// registers. At the end the eight partial results are merged through LDS in
+// a fixed order: M = max_w m_w, O = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w.
+// Lanes as in the bf16 kernel: S^T = K Q^T with lane = query (both lane
+// halves) and register r -> key c_row(r, half). Step c of the contraction
+// takes dimension half * D/2 + c (relabelling the contraction index on both
+// operands leaves the product unchanged), so a lane reads D/2 consecutive
+// floats of its Q and K rows. P^T feeds O^T += V^T P^T directly: step c
+// takes key c_row(c, half), whose probability is the lane's own register c.
 struct FwdParamsF {
   const float* q;
   const float* k;
@@ -504,18 +511,24 @@ struct FwdParamsF {
   uint64_t seed;
 };
 
-constexpr int kF32Tpr = 16;            // threads per query row (each owns d/16 columns)
-constexpr int kF32Bm = 128 / kF32Tpr;  // query rows per work-group
+constexpr int kF32Waves = 8;  // waves per work-group (key tiles dealt round-robin)
+constexpr int kF32Bm = 32;    // query rows per work-group
+
+__device__ __forceinline__ f32x16 mfma32x32x2_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
 
 template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
-  constexpr int BM = kF32Bm, BN = 16, DH = D / kF32Tpr;
-  __shared__ __align__(16) float ks[BN][D];
-  __shared__ __align__(16) float vs[BN][D];
-  __shared__ uint32_t bk[BN / 2];  // dropout keys of the tile's key pairs
+__global__ __launch_bounds__(64 * kF32Waves) void fwd_f32_kernel(FwdParamsF p) {
+  constexpr int NW = kF32Waves, BM = kF32Bm, BN = 32, DH = D / 2;
+  constexpr int NDB = (D + 31) / 32;
+  __shared__ float red_m[NW][BM];
+  __shared__ float red_l[NW][BM];
+  __shared__ __align__(16) float red_o[NW][16][64];
 
-  const int tid = threadIdx.x;
-  const int qi = tid / kF32Tpr, part = tid % kF32Tpr;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
   const int H = p.H;
   const int nqb = (p.N + BM - 1) / BM;
   const BlockMap bm = map_block(blockIdx.x, nqb, p.B * H);
@@ -524,19 +537,22 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
   const SeqRows sr = seq_rows(p.cu, p.total, b, h, H, D, p.N);
   const int N = sr.n;
   const int q0 = qb * BM;
-  if (q0 >= N) return;  // block past the end of a shorter sequence
-  const int myq = q0 + qi;
+  if (q0 >= N) return;  // block past the end of a shorter sequence (whole work-group)
+  const int myq = q0 + l32;
   const int64_t rs = (int64_t)H * D;
-  const int64_t base = sr.base;
+  const float* Qg = p.q + sr.base;
+  const float* Kg = p.k + sr.base;
+  const float* Vg = p.v + sr.base;
 
-  float qv[DH], ov[DH];
+  // This lane's query row, dimensions hf * DH .. hf * DH + DH - 1 (zeros past N).
+  float qf[DH];
   {
     const bool ok = myq < N;
-    const float* qrow = p.q + base + (int64_t)(ok ? myq : 0) * rs + part * DH;
+    const float* row = Qg + (int64_t)(ok ? myq : 0) * rs + hf * DH;
 #pragma unroll
-    for (int c = 0; c < DH; ++c) {
-      qv[c] = ok ? qrow[c] : 0.f;
-      ov[c] = 0.f;
+    for (int c = 0; c < DH; c += 4) {
+      const f32x4 x = ok ? *reinterpret_cast<const f32x4*>(row + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+      qf[c] = x[0], qf[c + 1] = x[1], qf[c + 2] = x[2], qf[c + 3] = x[3];
     }
   }
   uint64_t kbh = 0;
@@ -546,75 +562,117 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(FwdParamsF p) {
     arow = row_key(kbh, myq);
   }
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  const int ntiles = (kend + BN - 1) / BN;
   const uint8_t* mrow = nullptr;  // this query block's row of the block mask
   if (p.bmask != nullptr)
     mrow = p.bmask + b * p.msb + h * p.msh +
            (int64_t)(q0 / kSparseBlock) * ((N + kSparseBlock - 1) / kSparseBlock);
+
   float m = -INFINITY, l = 0.f;
-  for (int k0 = 0; k0 < kend; k0 += BN) {
-    if (mrow != nullptr && mrow[k0 / kSparseBlock] == 0) continue;  // uniform over the block
-    __syncthreads();
-    for (int i = tid; i < BN * D / 4; i += 128) {
-      const int r = i / (D / 4), c = (i - r * (D / 4)) * 4;
-      const int key = k0 + r;
-      f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-      if (key < N) {
-        kx = *reinterpret_cast<const f32x4*>(p.k + base + (int64_t)key * rs + c);
-        vx = *reinterpret_cast<const f32x4*>(p.v + base + (int64_t)key * rs + c);
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+  for (int t = wave; t < ntiles; t += NW) {
+    const int k0 = t * BN;
+    if (mrow != nullptr && mrow[k0 / kSparseBlock] == 0) continue;  // uniform over the wave
+    // S^T = K Q^T: register r -> key k0 + c_row(r, hf), lane -> query myq.
+    float kf[DH];
+    {
+      const bool ok = k0 + l32 < N;
+      const float* row = Kg + (int64_t)(ok ? k0 + l32 : 0) * rs + hf * DH;
+#pragma unroll
+      for (int c = 0; c < DH; c += 4) {
+        const f32x4 x = ok ? *reinterpret_cast<const f32x4*>(row + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        kf[c] = x[0], kf[c + 1] = x[1], kf[c + 2] = x[2], kf[c + 3] = x[3];
       }
-      *reinterpret_cast<f32x4*>(&ks[r][c]) = kx;
-      *reinterpret_cast<f32x4*>(&vs[r][c]) = vx;
     }
-    if constexpr (DROP) {
-      if (tid < BN / 2) bk[tid] = pair_key(kbh, (k0 >> 1) + tid);
-    }
-    __syncthreads();
-    float s[BN];
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int c = 0; c < DH; ++c) s = mfma32x32x2_f32(kf[c], qf[c], s);
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < BN; ++j) {
-      float acc = 0.f;
-#pragma unroll
-      for (int c = 0; c < DH; ++c) acc = fmaf(qv[c], ks[j][part * DH + c], acc);
-#pragma unroll
-      for (int x = 1; x < kF32Tpr; x <<= 1) acc += __shfl_xor(acc, x, kF32Tpr);
-      float x = acc * p.c2;
-      const int key = k0 + j;
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + c_row(r, hf);
+      float x = s[r] * p.c2;
       if (key >= N || (CAUSAL && key > myq)) x = -INFINITY;
-      s[j] = x;
+      s[r] = x;
       mx = fmaxf(mx, x);
     }
+    mx = xor32_max(mx);
     const float mnew = fmaxf(m, mx);
     const float mref = (mnew == -INFINITY) ? 0.f : mnew;
     const float alpha = exp2_hw(m - mref);
     m = mnew;
-    float psum = 0.f;
+    float ps = 0.f;
 #pragma unroll
-    for (int j = 0; j < BN; ++j) {
-      const float pv = exp2_hw(s[j] - mref);
-      psum += pv;
-      s[j] = pv;
-      if constexpr (DROP) {
-        if (!keep_key(pair_mix(arow, bk[j >> 1]), j, p.drop_t)) s[j] = 0.f;
+    for (int r = 0; r < 16; ++r) {
+      const float pv = exp2_hw(s[r] - mref);
+      ps += pv;
+      s[r] = pv;
+    }
+    l = l * alpha + ps;  // this lane half's keys; the halves are added at the end
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+    if constexpr (DROP) {
+      // Lane j (j < 16) hashes the tile's key pair j; register r reads the
+      // pair of its key (c_row(r, hf) >> 1) from that lane.
+      const uint32_t pk = pair_key(kbh, (k0 >> 1) + (lane & 15));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ko = c_row(r, hf);
+        const uint32_t y = pair_mix(arow, (uint32_t)__shfl((int)pk, ko >> 1));
+        if (!keep_key(y, ko, p.drop_t)) s[r] = 0.f;
       }
     }
-    l = l * alpha + psum;
+    // O^T += V^T P^T: step c takes key k0 + c_row(c, hf), column 32 db + l32.
 #pragma unroll
-    for (int c = 0; c < DH; ++c) {
-      float acc = ov[c] * alpha;
+    for (int db = 0; db < NDB; ++db) {
+      const int col = 32 * db + l32;
 #pragma unroll
-      for (int j = 0; j < BN; ++j) acc = fmaf(s[j], vs[j][part * DH + c], acc);
-      ov[c] = acc;
+      for (int c = 0; c < 16; ++c) {
+        const int key = k0 + c_row(c, hf);
+        const float a = (col < D && key < N) ? Vg[(int64_t)key * rs + col] : 0.f;
+        o[db] = mfma32x32x2_f32(a, s[c], o[db]);
+      }
     }
   }
-  if (myq < N) {
-    // A row whose blocks are all masked has no keys: O = 0, LSE = -inf.
-    const float inv = l == 0.f ? 0.f : (DROP ? p.drop_r : 1.f) / l;
-    float* orow = p.o + base + (int64_t)myq * rs + part * DH;
-#pragma unroll
-    for (int c = 0; c < DH; ++c) orow[c] = ov[c] * inv;
-    if (part == 0) p.lse[sr.stat + myq] = (m + log2_hw(l)) * kLn2;
+
+  // Merge the eight waves' partial results in wave order.
+  const float lw = xor32_sum(l);
+  if (hf == 0) {
+    red_m[wave][l32] = m;
+    red_l[wave][l32] = lw;
   }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w][l32]);
+  const float mref = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) L += red_l[w][l32] * exp2_hw(red_m[w][l32] - mref);
+  const float sc = exp2_hw(m - mref);
+  // A row whose blocks are all masked has no keys: O = 0, LSE = -inf.
+  const float inv = L == 0.f ? 0.f : (DROP ? p.drop_r : 1.f) / L;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    if (db > 0) __syncthreads();  // the previous block's sums are read
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red_o[wave][r][lane] = o[db][r] * sc;
+    __syncthreads();
+    if (wave < 4) {
+      // wave g sums registers 4g .. 4g + 3: dimensions 32 db + 8g + 4hf + 0..3
+      const int g = wave, d0 = 32 * db + 8 * g + 4 * hf;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += red_o[w][4 * g + e][lane];
+      if (myq < N && d0 < D)
+        *reinterpret_cast<f32x4*>(p.o + sr.base + (int64_t)myq * rs + d0) = acc * inv;
+    }
+  }
+  if (wave == 0 && hf == 0 && myq < N) p.lse[sr.stat + myq] = (M + log2_hw(L)) * kLn2;
 }
 
 // Eight waves (256 query rows) per work-group share each K/V tile, which
@@ -710,7 +768,8 @@ hipError_t launch_fwd_bf16_d(const FwdParams& prm, bool causal, bool drop,
 
 template <int D, bool CAUSAL, bool DROP>
 hipError_t launch_fwd_f32_t(const FwdParamsF& prm, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, DROP>), dim3(nblocks), dim3(128), 0, s, prm);
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, DROP>), dim3(nblocks), dim3(64 * kF32Waves), 0, s,
+                     prm);
   return hipGetLastError();
 }
 
