@@ -178,6 +178,49 @@ struct Both32 {
   }
 };
 
+// Instruction order of the dQ step after the score products: the NKC dP^T
+// products, each followed by V2 vector instructions (exponentials, dropout
+// hashes) and one V-row LDS read two steps ahead; the dS work of the first
+// 16-key step (V3a instructions); then the NDB dQ products of that step,
+// each followed by V3b vector instructions of the second step's dS and two
+// transposing reads; then the second step's NDB products.
+template <int NKC, int NDB, int PRE, int V2, int V3a, int V3b>
+__device__ __forceinline__ void sched_dq_order() {
+  constexpr int kValu = 0x002, kMfma = 0x008, kDs = 0x080;
+  __builtin_amdgcn_sched_group_barrier(kDs, PRE + 2, 0);
+#pragma unroll
+  for (int i = 0; i < NKC; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kValu, V2, 0);
+    if (i + 2 < NKC)
+      __builtin_amdgcn_sched_group_barrier(kDs, 1, 0);
+    else
+      __builtin_amdgcn_sched_group_barrier(kDs, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kValu, V3a, 0);
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kValu, V3b, 0);
+    __builtin_amdgcn_sched_group_barrier(kDs, 2, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    if (i + 1 < NDB) __builtin_amdgcn_sched_group_barrier(kDs, 2, 0);
+  }
+}
+// Vector work per dQ step: 16 FMAs and 16 exponentials (with dropout also
+// 8 hashes, about 40 instructions), then per 16-key step 8 multiplies and
+// 4 packs (with dropout 8 keep tests and selects more).
+template <int NKC, int NDB, bool DROP>
+__device__ __forceinline__ void sched_dq_phases() {
+  if constexpr (DROP)
+    sched_dq_order<NKC, NDB, 4, (72 + NKC - 1) / NKC, 36, (36 + NDB - 1) / NDB>();
+  else
+    sched_dq_order<NKC, NDB, 0, (32 + NKC - 1) / NKC, 12, (12 + NDB - 1) / NDB>();
+}
+
 // ---------------------------------------------------------------------------
 // B2 (bf16): one work-group of NW waves per (block of 32 NW keys, b, h); each
 // wave owns 32 keys (lane = key) with their K rows in registers, the block's
@@ -349,9 +392,9 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdP
   };
   auto stat_store = [&](float* ls, float* dd, uint32_t* ar) {
     if (gt < 32) {
-      ls[gt] = sx * kLog2e;
+      ls[gt] = DROP ? sx * kLog2e : -sx / p.scale;  // without dropout: start of the S accumulator
     } else if (gt < 64) {
-      dd[gt - 32] = sx;
+      dd[gt - 32] = DROP ? sx : -sx;  // without dropout the dP accumulator starts at -D
     } else if (DROP && gt < 96) {
       ar[gt - 64] = __float_as_uint(sx);
     }
@@ -377,6 +420,98 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdP
     dvacc[db] = f32x16{};
   }
 
+  // One query tile without dropout, in issue order: each group of
+  // instructions below is kept in place by a scheduling barrier, so the
+  // matrix products and the vector work of the same tile alternate within
+  // the wave. The S accumulator starts at -lse/scale and the dP accumulator
+  // at -D (both from the per-stage arrays), so P = exp2(S * scale log2 e)
+  // and dS = P * dP need one multiply each per element.
+  auto dkdv_tile_nodrop = [&](const char* cur, const float* lsc, const float* ddc, int qt0) {
+    constexpr int NKC = C::NKC, NT = 2 * C::NDB;
+    constexpr int EP = (16 + NKC - 1) / NKC;  // probabilities per dP product
+    constexpr int EQ = (16 + NT - 1) / NT;    // dS values per dV product
+    // Phase 1: S = Q K^T (K in registers, Q rows from LDS).
+    f32x16 s;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(lsc + 8 * g + 4 * hf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[4 * g + e] = x[e];
+    }
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) s = mfma32x32x16(ld_lds_128(cur, ofs.row_off(c)), kreg[c], s);
+    sched_lds_ahead<NKC, 1, 1, 4>();
+    __builtin_amdgcn_sched_barrier(0);
+    if (CAUSAL && qt0 < kw0 + 31) {
+      // diagonal tile: keys after the query get probability exp2(-inf) = 0
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = mykey > qt0 + c_row(r, hf) ? -INFINITY : s[r];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase 2: dP = dO V^T (dO rows and the block's V rows from LDS), two
+    // steps of operands ahead; after each product EP probabilities.
+    f32x16 dp;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(ddc + 8 * g + 4 * hf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[4 * g + e] = x[e];
+    }
+    u32x4 xa[NKC], xb[NKC];
+    auto dp_ops = [&](int c) {
+      const int o = ofs.row_off(c);
+      const int vo = (2 * c < 8 * VB::NG) ? (c >> 2) * VB::GBYTES + vrow[c & 3] : vrow_tail;
+      xa[c] = ld_lds_128(cur, QT::BYTES + o);
+      xb[c] = ld_lds_128(vblk, vo);
+    };
+    dp_ops(0);
+    if (NKC > 1) dp_ops(1);
+    float pv[16];
+    u32x4 pop[2], sop[2];
+    u32x4 ta[NT + 2], tb[NT];  // transposing-read operands of the dV and dK products
+    auto tr_v = [&](int j) { ta[j] = ofs.tr_frag(cur + QT::BYTES, j % C::NDB, j / C::NDB); };
+    auto tr_k = [&](int j) { tb[j] = ofs.tr_frag(cur, j % C::NDB, j / C::NDB); };
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      dp = mfma32x32x16(xa[c], xb[c], dp);
+      if (c + 2 < NKC) dp_ops(c + 2);
+      else tr_v(c + 2 - NKC);
+#pragma unroll
+      for (int e = c * EP; e < (c + 1) * EP && e < 16; ++e) pv[e] = exp2_hw(s[e] * p.c2);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        if (c * EP < 8 * kt + 8 && (c + 1) * EP >= 8 * kt + 8)
+          pop[kt] = u32x4{pack_bf16x2(pv[8 * kt + 0], pv[8 * kt + 1]), pack_bf16x2(pv[8 * kt + 2], pv[8 * kt + 3]),
+                          pack_bf16x2(pv[8 * kt + 4], pv[8 * kt + 5]), pack_bf16x2(pv[8 * kt + 6], pv[8 * kt + 7])};
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Phase 3: dV^T += dO^T P (transposing reads of dO), two products of
+    // operands ahead; after each product EQ values of dS = P (dP - D).
+    float dsv[16];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      dvacc[j % C::NDB] = mfma32x32x16(ta[j], pop[j / C::NDB], dvacc[j % C::NDB]);
+      if (j + 2 < NT) tr_v(j + 2);
+      else tr_k(j + 2 - NT);
+#pragma unroll
+      for (int e = j * EQ; e < (j + 1) * EQ && e < 16; ++e) dsv[e] = pv[e] * dp[e];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        if (j * EQ < 8 * kt + 8 && (j + 1) * EQ >= 8 * kt + 8)
+          sop[kt] = u32x4{pack_bf16x2(dsv[8 * kt + 0], dsv[8 * kt + 1]), pack_bf16x2(dsv[8 * kt + 2], dsv[8 * kt + 3]),
+                          pack_bf16x2(dsv[8 * kt + 4], dsv[8 * kt + 5]), pack_bf16x2(dsv[8 * kt + 6], dsv[8 * kt + 7])};
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Phase 4: dK^T += Q^T dS (transposing reads of Q).
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      dkacc[j % C::NDB] = mfma32x32x16(tb[j], sop[j / C::NDB], dkacc[j % C::NDB]);
+      if (j + 2 < NT) tr_k(j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   // Step of this group over kept query tile t (t >= ntiles: the group has
   // no tile in this step and only takes part in the barrier).
   auto step = [&](const char* cur, const float* lsc, const float* ddc, const uint32_t* arc,
@@ -393,6 +528,9 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdP
       issue(nxt, qn);
     }
     if (valid && (!CAUSAL || qt0 + C::BQ - 1 >= kw0)) {
+      if constexpr (!DROP) {
+        dkdv_tile_nodrop(cur, lsc, ddc, qt0);
+      } else {
       // S = Q K^T and dP = dO V^T : lane = key, register r -> query qt0 + c_row(r, hf)
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -463,6 +601,7 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdP
       // Statistics reads first, then the four transposing reads of step i + 1
       // ahead of the two products of step i.
       sched_lds_ahead<2 * C::NDB, 4, 2, DROP ? 12 : 8, 1>();
+      }
     }
     if (more) stat_store(lsn, ddn, arn);
   };
@@ -659,6 +798,9 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
   f32x16 dqacc[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) dqacc[db] = f32x16{};
+  f32x16 negd;  // -D of this lane's query: start of the dP^T accumulator (no dropout)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negd[r] = -dq_d;
 
   auto step = [&](const char* cur, const uint32_t* bcc, char* nxt, uint32_t* bcn, int t) {
     wait_vmem();
@@ -667,54 +809,64 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
     const int k0 = tile_start(t);
     if (t + 1 < ntiles) issue(nxt, bcn, tile_start(t + 1));
     if (CAUSAL && k0 > qw0 + 31) return;
-    // S^T = K Q^T and dP^T = V dO^T : lane = query, register r -> key k0 + c_row(r, hf)
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // Phase 1. S^T = K Q^T : lane = query, register r -> key k0 + c_row(r, hf).
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int c = 0; c < C::NKC; ++c) s = mfma32x32x16(ld_lds_128(cur, ofs.row_off(c)), qreg[c], s);
+    sched_lds_ahead<C::NKC, 1, 1>();
+    __builtin_amdgcn_sched_barrier(0);  // the later phases are ordered on their own
+    if ((k0 + C::BK > N) || (CAUSAL && k0 + C::BK - 1 > qw0)) {
+      // tail or diagonal tile: keys past N or after the query get exp2(-inf) = 0
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + c_row(r, hf);
+        s[r] = (key >= N || (CAUSAL && key > myq)) ? -INFINITY : s[r];
+      }
+    }
+    // Phase 2. dP^T = V dO^T on the matrix cores while the vector ALUs form
+    // P^T; without dropout the accumulator starts at -D of this lane's query.
+    f32x16 dp = DROP ? f32x16{} : negd;
 #pragma unroll
     for (int c = 0; c < C::NKC; ++c) {
       const int vo = (2 * c < 8 * VT::NG) ? (c >> 2) * VT::GBYTES + vrow[c & 3] : vrow_tail;
-      s = mfma32x32x16(ld_lds_128(cur, ofs.row_off(c)), qreg[c], s);
       dp = mfma32x32x16(ld_lds_128(cur, vo), doreg[c], dp);
     }
-    sched_lds_ahead<C::NKC, 2, 2>();
-    const bool need_mask = (k0 + C::BK > N) || (CAUSAL && k0 + C::BK - 1 > qw0);
+    float pv[16];
+    // Registers 4g + e hold keys 8g + 4hf + e; keys (e, e + 1), e = 0, 2, are
+    // a pair and share one dropout hash.
+    uint32_t yd[DROP ? 4 : 1][2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if constexpr (DROP) {
+        const u32x2 bc = *reinterpret_cast<const u32x2*>(bcc + 4 * g + 2 * hf);
+        yd[g][0] = pair_mix(arow, bc[0]);
+        yd[g][1] = pair_mix(arow, bc[1]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[4 * g + e] = exp2_hw(fmaf(s[4 * g + e], p.c2, -lse2));
+    }
+    // Phase 3. dS^T = P^T (dP^T - D) per 16-key step, and dQ^T += K^T dS^T.
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       float dsv[8];
 #pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const int g = 2 * kt + gg;
-        // Registers 4g + e hold keys 8g + 4hf + e; keys (e, e + 1), e = 0, 2,
-        // are a pair and share one dropout hash.
-        uint32_t yd[2] = {0, 0};
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * kt + i, g = r >> 2, e = r & 3;
         if constexpr (DROP) {
-          const u32x2 bc = *reinterpret_cast<const u32x2*>(bcc + 4 * g + 2 * hf);
-          yd[0] = pair_mix(arow, bc[0]);
-          yd[1] = pair_mix(arow, bc[1]);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float pv = exp2_hw(fmaf(s[r], p.c2, -lse2));
-          if (need_mask) {
-            const int key = k0 + c_row(r, hf);
-            if (key >= N || (CAUSAL && key > myq)) pv = 0.f;
-          }
-          float dpv = dp[r];
-          if constexpr (DROP) {
-            const bool kp = (e & 1) ? keep_odd(yd[e >> 1], p.drop_t) : keep_even(yd[e >> 1], p.drop_t);
-            dpv = kp ? dpv * p.drop_r : 0.f;
-          }
-          dsv[4 * gg + e] = pv * (dpv - dq_d);
+          const uint32_t y = yd[DROP ? g : 0][e >> 1];
+          const bool kp = (e & 1) ? keep_odd(y, p.drop_t) : keep_even(y, p.drop_t);
+          dsv[i] = pv[r] * ((kp ? dp[r] * p.drop_r : 0.f) - dq_d);
+        } else {
+          dsv[i] = pv[r] * dp[r];
         }
       }
       const u32x4 sop = {pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3]),
                          pack_bf16x2(dsv[4], dsv[5]), pack_bf16x2(dsv[6], dsv[7])};
-      // dQ^T += K^T dS^T over the 16 keys of step kt.
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
         dqacc[db] = mfma32x32x16(ofs.tr_frag(cur, db, kt), sop, dqacc[db]);
     }
-    sched_lds_ahead<2 * C::NDB, 2, 1, DROP ? 4 : 0>();
+    sched_dq_phases<C::NKC, C::NDB, DROP>();
   };
 
   if constexpr (kLdsPoison) poison_stage(st0, C::STAGE, tid, C::NT);
