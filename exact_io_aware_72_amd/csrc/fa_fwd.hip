@@ -544,16 +544,19 @@ __global__ __launch_bounds__(64 * kF32Waves) void fwd_f32_kernel(FwdParamsF p) {
   const float* Kg = p.k + sr.base;
   const float* Vg = p.v + sr.base;
 
-  // This lane's query row, dimensions hf * DH .. hf * DH + DH - 1 (zeros past N).
+  // Buffer resources over the (batch, head) rows: reads of rows at or past N
+  // return zeros (hardware range check), so no load needs a branch.
+  const uint32_t rs4 = (uint32_t)rs * 4u;
+  const BufRes rq = make_bufres(Qg, (uint32_t)N * rs4);
+  const BufRes rk = make_bufres(Kg, (uint32_t)N * rs4);
+  const BufRes rv = make_bufres(Vg, (uint32_t)N * rs4);
+  // This lane's query row, dimensions hf * DH .. hf * DH + DH - 1.
   float qf[DH];
-  {
-    const bool ok = myq < N;
-    const float* row = Qg + (int64_t)(ok ? myq : 0) * rs + hf * DH;
 #pragma unroll
-    for (int c = 0; c < DH; c += 4) {
-      const f32x4 x = ok ? *reinterpret_cast<const f32x4*>(row + c) : f32x4{0.f, 0.f, 0.f, 0.f};
-      qf[c] = x[0], qf[c + 1] = x[1], qf[c + 2] = x[2], qf[c + 3] = x[3];
-    }
+  for (int c = 0; c < DH; c += 4) {
+    const u32x4 x = buf_load_128(rq, (uint32_t)myq * rs4 + (uint32_t)(hf * DH + c) * 4u);
+    qf[c] = __uint_as_float(x[0]), qf[c + 1] = __uint_as_float(x[1]);
+    qf[c + 2] = __uint_as_float(x[2]), qf[c + 3] = __uint_as_float(x[3]);
   }
   uint64_t kbh = 0;
   uint32_t arow = 0;
@@ -575,20 +578,39 @@ __global__ __launch_bounds__(64 * kF32Waves) void fwd_f32_kernel(FwdParamsF p) {
   for (int t = wave; t < ntiles; t += NW) {
     const int k0 = t * BN;
     if (mrow != nullptr && mrow[k0 / kSparseBlock] == 0) continue;  // uniform over the wave
-    // S^T = K Q^T: register r -> key k0 + c_row(r, hf), lane -> query myq.
+    // All of this tile's K and V loads are issued before its products, so
+    // their latency is paid once. K: this lane's key row k0 + l32, the same
+    // dimensions as its query row. V: step c of O^T += V^T P^T takes key
+    // k0 + c_row(c, hf), column 32 db + l32 (columns past D, only for
+    // D = 80, read zeros through an offset beyond the range).
     float kf[DH];
-    {
-      const bool ok = k0 + l32 < N;
-      const float* row = Kg + (int64_t)(ok ? k0 + l32 : 0) * rs + hf * DH;
 #pragma unroll
-      for (int c = 0; c < DH; c += 4) {
-        const f32x4 x = ok ? *reinterpret_cast<const f32x4*>(row + c) : f32x4{0.f, 0.f, 0.f, 0.f};
-        kf[c] = x[0], kf[c + 1] = x[1], kf[c + 2] = x[2], kf[c + 3] = x[3];
-      }
+    for (int c = 0; c < DH; c += 4) {
+      const u32x4 x = buf_load_128(rk, (uint32_t)(k0 + l32) * rs4 + (uint32_t)(hf * DH + c) * 4u);
+      kf[c] = __uint_as_float(x[0]), kf[c + 1] = __uint_as_float(x[1]);
+      kf[c + 2] = __uint_as_float(x[2]), kf[c + 3] = __uint_as_float(x[3]);
     }
+    float va[NDB][16];
+    auto load_v = [&](int db) {
+      const int col = 32 * db + l32;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const uint32_t off = (uint32_t)(k0 + c_row(c, hf)) * rs4 + (uint32_t)col * 4u;
+        va[db][c] = buf_load_f32(rv, col < D ? off : 0x80000000u);
+      }
+    };
+    // At D = 128 the V loads are requested after the score products (the
+    // K row's registers are free by then), still ahead of the softmax.
+    constexpr int NEARLY = D == 128 ? 0 : NDB;
+#pragma unroll
+    for (int db = 0; db < NEARLY; ++db) load_v(db);
+    __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of the products
     f32x16 s = f32x16{};
 #pragma unroll
     for (int c = 0; c < DH; ++c) s = mfma32x32x2_f32(kf[c], qf[c], s);
+#pragma unroll
+    for (int db = NEARLY; db < NDB; ++db) load_v(db);
+    __builtin_amdgcn_sched_barrier(0);
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -624,17 +646,11 @@ __global__ __launch_bounds__(64 * kF32Waves) void fwd_f32_kernel(FwdParamsF p) {
         if (!keep_key(y, ko, p.drop_t)) s[r] = 0.f;
       }
     }
-    // O^T += V^T P^T: step c takes key k0 + c_row(c, hf), column 32 db + l32.
+    // O^T += V^T P^T.
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int col = 32 * db + l32;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const int key = k0 + c_row(c, hf);
-        const float a = (col < D && key < N) ? Vg[(int64_t)key * rs + col] : 0.f;
-        o[db] = mfma32x32x2_f32(a, s[c], o[db]);
-      }
-    }
+      for (int c = 0; c < 16; ++c) o[db] = mfma32x32x2_f32(va[db][c], s[c], o[db]);
   }
 
   // Merge the eight waves' partial results in wave order.
