@@ -428,8 +428,6 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdP
   // and dS = P * dP need one multiply each per element.
   auto dkdv_tile_nodrop = [&](const char* cur, const float* lsc, const float* ddc, int qt0) {
     constexpr int NKC = C::NKC, NT = 2 * C::NDB;
-    constexpr int EP = (16 + NKC - 1) / NKC;  // probabilities per dP product
-    constexpr int EQ = (16 + NT - 1) / NT;    // dS values per dV product
     // Phase 1: S = Q K^T (K in registers, Q rows from LDS).
     f32x16 s;
 #pragma unroll
@@ -448,8 +446,7 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdP
       for (int r = 0; r < 16; ++r) s[r] = mykey > qt0 + c_row(r, hf) ? -INFINITY : s[r];
     }
     __builtin_amdgcn_sched_barrier(0);
-    // Phase 2: dP = dO V^T (dO rows and the block's V rows from LDS), two
-    // steps of operands ahead; after each product EP probabilities.
+    // dP = dO V^T (dO rows and the block's V rows from LDS), starting at -D.
     f32x16 dp;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -457,57 +454,67 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdP
 #pragma unroll
       for (int e = 0; e < 4; ++e) dp[4 * g + e] = x[e];
     }
+    // Phases 2-4 as one sequence of NKC + 4 NDB products (dP, then dV,
+    // then dK), each followed by the LDS reads of the product two places
+    // later and by a share of the vector work: probability e (multiply +
+    // exp2) after product (e (NKC + NDB)) / 16, dS value e after product
+    // NKC + (3 NDB e) / 16, and each pack right after its last input. The
+    // shares are spread so that no product carries more than about one and
+    // a half exponentials, and every operand is ready before the product
+    // that takes it (P^T of step kt before the dV products of step kt, dS
+    // of step kt before the dK products of step kt).
+    constexpr int NP = NKC + 4 * C::NDB;   // products after the S phase
+    constexpr int SP = NKC + C::NDB;       // slots that carry probabilities
+    constexpr int SS = 3 * C::NDB;         // slots that carry dS values
     u32x4 xa[NKC], xb[NKC];
-    auto dp_ops = [&](int c) {
-      const int o = ofs.row_off(c);
-      const int vo = (2 * c < 8 * VB::NG) ? (c >> 2) * VB::GBYTES + vrow[c & 3] : vrow_tail;
-      xa[c] = ld_lds_128(cur, QT::BYTES + o);
-      xb[c] = ld_lds_128(vblk, vo);
+    u32x4 ta[NT], tb[NT];  // transposing-read operands of the dV and dK products
+    auto ops = [&](int j) {
+      if (j < NKC) {
+        const int o = ofs.row_off(j);
+        const int vo = (2 * j < 8 * VB::NG) ? (j >> 2) * VB::GBYTES + vrow[j & 3] : vrow_tail;
+        xa[j] = ld_lds_128(cur, QT::BYTES + o);
+        xb[j] = ld_lds_128(vblk, vo);
+      } else if (j < NKC + NT) {
+        const int t = j - NKC;
+        ta[t] = ofs.tr_frag(cur + QT::BYTES, t % C::NDB, t / C::NDB);
+      } else if (j < NP) {
+        const int t = j - NKC - NT;
+        tb[t] = ofs.tr_frag(cur, t % C::NDB, t / C::NDB);
+      }
     };
-    dp_ops(0);
-    if (NKC > 1) dp_ops(1);
-    float pv[16];
+    ops(0);
+    ops(1);
+    float pv[16], dsv[16];
     u32x4 pop[2], sop[2];
-    u32x4 ta[NT + 2], tb[NT];  // transposing-read operands of the dV and dK products
-    auto tr_v = [&](int j) { ta[j] = ofs.tr_frag(cur + QT::BYTES, j % C::NDB, j / C::NDB); };
-    auto tr_k = [&](int j) { tb[j] = ofs.tr_frag(cur, j % C::NDB, j / C::NDB); };
+    auto pack8 = [&](const float* x) {
+      return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                   pack_bf16x2(x[6], x[7])};
+    };
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < NKC; ++c) {
-      dp = mfma32x32x16(xa[c], xb[c], dp);
-      if (c + 2 < NKC) dp_ops(c + 2);
-      else tr_v(c + 2 - NKC);
+    for (int j = 0; j < NP; ++j) {
+      if (j < NKC) {
+        dp = mfma32x32x16(xa[j], xb[j], dp);
+      } else if (j < NKC + NT) {
+        const int t = j - NKC;
+        dvacc[t % C::NDB] = mfma32x32x16(ta[t], pop[t / C::NDB], dvacc[t % C::NDB]);
+      } else {
+        const int t = j - NKC - NT;
+        dkacc[t % C::NDB] = mfma32x32x16(tb[t], sop[t / C::NDB], dkacc[t % C::NDB]);
+      }
+      ops(j + 2);
 #pragma unroll
-      for (int e = c * EP; e < (c + 1) * EP && e < 16; ++e) pv[e] = exp2_hw(s[e] * p.c2);
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-        if (c * EP < 8 * kt + 8 && (c + 1) * EP >= 8 * kt + 8)
-          pop[kt] = u32x4{pack_bf16x2(pv[8 * kt + 0], pv[8 * kt + 1]), pack_bf16x2(pv[8 * kt + 2], pv[8 * kt + 3]),
-                          pack_bf16x2(pv[8 * kt + 4], pv[8 * kt + 5]), pack_bf16x2(pv[8 * kt + 6], pv[8 * kt + 7])};
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Phase 3: dV^T += dO^T P (transposing reads of dO), two products of
-    // operands ahead; after each product EQ values of dS = P (dP - D).
-    float dsv[16];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      dvacc[j % C::NDB] = mfma32x32x16(ta[j], pop[j / C::NDB], dvacc[j % C::NDB]);
-      if (j + 2 < NT) tr_v(j + 2);
-      else tr_k(j + 2 - NT);
-#pragma unroll
-      for (int e = j * EQ; e < (j + 1) * EQ && e < 16; ++e) dsv[e] = pv[e] * dp[e];
+      for (int e = 0; e < 16; ++e)
+        if ((e * SP) / 16 == j) pv[e] = exp2_hw(s[e] * p.c2);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
-        if (j * EQ < 8 * kt + 8 && (j + 1) * EQ >= 8 * kt + 8)
-          sop[kt] = u32x4{pack_bf16x2(dsv[8 * kt + 0], dsv[8 * kt + 1]), pack_bf16x2(dsv[8 * kt + 2], dsv[8 * kt + 3]),
-                          pack_bf16x2(dsv[8 * kt + 4], dsv[8 * kt + 5]), pack_bf16x2(dsv[8 * kt + 6], dsv[8 * kt + 7])};
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Phase 4: dK^T += Q^T dS (transposing reads of Q).
+        if (((8 * kt + 7) * SP) / 16 == j) pop[kt] = pack8(pv + 8 * kt);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      dkacc[j % C::NDB] = mfma32x32x16(tb[j], sop[j / C::NDB], dkacc[j % C::NDB]);
-      if (j + 2 < NT) tr_k(j + 2);
+      for (int e = 0; e < 16; ++e)
+        if (NKC + (e * SS) / 16 == j) dsv[e] = pv[e] * dp[e];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        if (NKC + ((8 * kt + 7) * SS) / 16 == j) sop[kt] = pack8(dsv + 8 * kt);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -671,10 +678,10 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdP
 // stages by direct-to-LDS loads: K row reads (A operand of S^T = K Q^T) and
 // K transposing reads (A operand of dQ^T += K^T dS^T) from one copy, V row
 // reads (A operand of dP^T = V dO^T).
-template <int D>
+template <int D, int NW = 4>
 struct DqCfg {
-  static constexpr int NT = 256;
-  static constexpr int BQ = 128;
+  static constexpr int NT = 64 * NW;  // NW waves of 32 queries
+  static constexpr int BQ = 32 * NW;
   static constexpr int BK = 32;
   static constexpr int NKC = D / 16;
   static constexpr int DP = (D + 31) / 32 * 32;
@@ -683,12 +690,16 @@ struct DqCfg {
   using VT = Tile<BK, D, Swz::kRow>;
   static constexpr int STAGE = KT::BYTES + VT::BYTES;
   static constexpr int NLOAD = KT::NLOAD + VT::NLOAD;
-  static constexpr int LPW = (NLOAD + 3) / 4;
+  static constexpr int LPW = (NLOAD + NW - 1) / NW;
 };
 
-template <int D, bool CAUSAL, bool DROP, bool SPARSE>
-__global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
-  using C = DqCfg<D>;
+// NW = 8 (256 queries per work-group) at long sequences: each K/V tile then
+// serves twice the queries, which halves the K/V bytes streamed from L2 and
+// beyond per query (the key-range prefixes of co-resident work-groups do not
+// share L2 lines at 32K+ keys).
+template <int D, bool CAUSAL, bool DROP, bool SPARSE, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdParams p) {
+  using C = DqCfg<D, NW>;
   using KT = typename C::KT;
   using VT = typename C::VT;
   __shared__ __align__(16) char st0[C::STAGE];
@@ -762,7 +773,7 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
   int dlds[C::LPW];
 #pragma unroll
   for (int m = 0; m < C::LPW; ++m) {
-    const int i = (wave & 3) + 4 * m;
+    const int i = wave + NW * m;
     int off = 0, row = 0, ch = 0;
     if (i < KT::NLOAD) {
       KT::load_slot(i, lane, off, row, ch);
@@ -779,7 +790,7 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdParams p) {
     const BufRes rv = make_bufres(Vg + (int64_t)k0 * rs, left);
 #pragma unroll
     for (int m = 0; m < C::LPW; ++m) {
-      const int i = (wave & 3) + 4 * m;
+      const int i = wave + NW * m;
       if (i < C::NLOAD) lds_dma_16(i < KT::NLOAD ? rk : rv, stage + dlds[m], dsrc[m]);
     }
     if constexpr (DROP) {
@@ -1162,6 +1173,24 @@ hipError_t launch_dkdv_ds(const BwdParams& prm, bool causal, bool drop, dim3 gri
 template <int D, bool SPARSE>
 hipError_t launch_dq_ds(const BwdParams& prm, bool causal, bool drop, dim3 grid, dim3 block,
                         hipStream_t s) {
+  // A block-mask row covers 128 queries: block-sparse runs keep four waves.
+  if constexpr (!SPARSE) {
+    if (prm.N >= 32768) {
+      const dim3 grid8((unsigned)((prm.N + 255) / 256 * prm.B * prm.H)), block8(512);
+      if (causal) {
+        if (drop)
+          hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, true, true, false, 8>), grid8, block8, 0, s, prm);
+        else
+          hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, true, false, false, 8>), grid8, block8, 0, s, prm);
+      } else {
+        if (drop)
+          hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, false, true, false, 8>), grid8, block8, 0, s, prm);
+        else
+          hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, false, false, false, 8>), grid8, block8, 0, s, prm);
+      }
+      return hipGetLastError();
+    }
+  }
   if (causal) {
     if (drop)
       hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, true, true, SPARSE>), grid, block, 0, s, prm);

@@ -95,6 +95,37 @@ def test_full_size_whole_heads(cfg, heads):
         print(f"  head ({b},{h}) ok", flush=True)
 
 
+@pytest.mark.parametrize("d,causal", [(80, False), (64, True)])
+def test_long_sequence_wide_groups(d, causal):
+    """N = 32768 runs the sixteen-wave forward groups (head dims up to 80, no
+    dropout) and the eight-wave dQ groups. Shapes the workloads do not cover
+    (full mask at d = 80, causal at d = 64), at sampled rows and columns of
+    one head against the oracle."""
+    w = WORKLOADS[4].with_(H=2, d=d, causal=causal)
+    inp = make_inputs(w, with_grad=True)
+    dev = {k: to_device(v[0], w.dtype) for k, v in inp.items()}
+    print(f"N=32768 d={d} causal={causal}", flush=True)
+    args = (w.causal, 0.0, 0, w.scale)
+    o, lse = fa.forward(dev["q"], dev["k"], dev["v"], *args)
+    dq, dk, dv = fa.backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, *args)
+    torch.cuda.synchronize()
+    N = w.N
+    rng = np.random.default_rng(77)
+    rows = np.unique(np.concatenate([[0, 255, 256, 511, 512, N // 2, N - 513, N - 512, N - 1],
+                                     rng.choice(N, 7, replace=False)]))
+    cols = np.unique(np.concatenate([[0, 1, 32767 - 300, N - 1], rng.choice(N, 6, replace=False)]))
+    b, h = 0, 1
+    val = {k: v[1] for k, v in inp.items()}
+    ref = oracle.sampled_head(val["q"], val["k"], val["v"], val["do"], w.scale, w.causal, 0.0, 0,
+                              b, h, rows, cols)
+    r_t, c_t = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    assert_close("O", to_host(o[b, r_t, h]), ref["o"], w.dtype)
+    assert_close("LSE", to_host(lse[b, h, r_t]), ref["lse"], w.dtype)
+    assert_close("dQ", to_host(dq[b, r_t, h]), ref["dq"], w.dtype)
+    assert_close("dK", to_host(dk[b, c_t, h]), ref["dk"], w.dtype)
+    assert_close("dV", to_host(dv[b, c_t, h]), ref["dv"], w.dtype)
+
+
 @pytest.mark.parametrize("cfg", [3, 4])
 def test_full_size_gradient_invariants(cfg):
     """Rows of dS sum to zero, so sum_j dK_j = 0; rows of P sum to one, so
