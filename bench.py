@@ -79,6 +79,8 @@ class ClockStamps:
     they read). The stamps lie outside the HIP-event brackets of the steps.
     Reports None with the reason if the library is missing."""
 
+    MIN_REGION_MS = 2.0
+
     def __init__(self, torch, blocks=8):
         import ctypes
         self.torch = torch
@@ -111,16 +113,21 @@ class ClockStamps:
             for r1 in b:
                 if r1[0] == r0[0] and int(r0[0]) not in per and r1[2] > r0[2]:
                     per[int(r0[0])] = 100.0 * float(r1[1] - r0[1]) / float(r1[2] - r0[2])
+        region_ms = float(np.median([(r1[2] - r0[2]) / 1e5 for r0, r1 in zip(a, b)]))
         # An XCD that idles between the stamps can stop or reset its cycle
-        # counter (seen on sub-millisecond regions); such readings fall
-        # outside any real clock and are left out of the median.
-        ok = [v for v in per.values() if 100.0 < v < 3000.0]
+        # counter (seen on sub-millisecond regions), so short regions are not
+        # reported, and readings outside 100 MHz .. the 2.4 GHz peak engine
+        # clock are left out of the median.
+        if region_ms < self.MIN_REGION_MS:
+            return {"mhz": None, "per_xcd_mhz": per, "region_ms": region_ms,
+                    "error": f"timed region shorter than {self.MIN_REGION_MS} ms"}
+        ok = [v for v in per.values() if 100.0 < v < 2450.0]
         if not ok:
             return {"mhz": None, "per_xcd_mhz": per, "error": "no plausible per-XCD reading"}
         return {"mhz": float(np.median(ok)), "per_xcd_mhz": per, "xcds_used": len(ok),
                 "source": "s_memtime cycles / s_memrealtime (100 MHz) ticks per XCD between "
                           "stamps enqueued before the first and after the last timed step",
-                "region_ms": float(np.median([(r1[2] - r0[2]) / 1e5 for r0, r1 in zip(a, b)]))}
+                "region_ms": region_ms}
 
 
 def run_gpu(w, steps, warmup, torch, fa, keep_outputs=False, sample_clock=False):
