@@ -242,4 +242,27 @@ __device__ __forceinline__ BlockMap map_block(int id, int nblk, int BH) {
   return m;
 }
 
+// Causal blocks when the whole grid is resident at once: the grid is
+// 8 XCDs x `cpx` CUs x `slots` work-groups, `slots` even and within the
+// kernel's occupancy. Work-groups are dispatched round-robin over the XCDs
+// and, within an XCD, breadth-first over its CUs, so the `slots` work-groups
+// of one CU are the ids of one XCD whose local index is equal mod `cpx`.
+// Those take slots / 2 complementary rank pairs (r, nblk - 1 - r) of one
+// head each, whose causal work sums to nblk + 1 blocks: every CU gets the
+// same work, where rank-major order leaves up to 1.4x between CUs. Heads are
+// dealt to XCDs as in map_block.
+__device__ __forceinline__ BlockMap map_block_pairs(int id, int nblk, int BH, int slots, int cpx) {
+  BlockMap m;
+  const int xcd = id & 7;
+  const int local = id >> 3;
+  const int hpx = BH >> 3;
+  const int c = local % cpx, j = local / cpx;
+  const int half = slots >> 1;
+  const int pair = (j % half) * cpx + c;  // < half * cpx = hpx * nblk / 2
+  const int r = pair / hpx;
+  m.bh = (pair - r * hpx) * 8 + xcd;
+  m.rank = j < half ? r : nblk - 1 - r;
+  return m;
+}
+
 }  // namespace fa

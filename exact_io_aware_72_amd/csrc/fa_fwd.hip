@@ -25,6 +25,7 @@
 // a wave skips tiles wholly after its own last query; diagonal tiles are
 // masked per element.
 #include "fa_device.h"
+#include <atomic>
 #include <type_traits>
 
 #include "fa_hash.h"
@@ -51,6 +52,9 @@ struct FwdParams {
   int total;
   const uint8_t* bmask;  // block-sparse mask, or nullptr
   int64_t msb, msh;
+  // Causal, whole grid resident: work-groups per CU and CUs per XCD for
+  // map_block_pairs; pair_slots = 0 keeps the rank-major map_block.
+  int pair_slots, cus_per_xcd;
   // Split-KV: Nk key rows per batch item (N query rows), the key range cut
   // into nsplit parts; part s writes O_s (fp32, normalised) and LSE_s.
   int Nk, nsplit;
@@ -123,7 +127,9 @@ __attribute__((amdgpu_waves_per_eu(1, ((D == 64 && !FP8) || NW == 16) ? 4 : 2)))
     split = wgid % p.nsplit;
     wgid /= p.nsplit;
   }
-  const BlockMap bm = map_block(wgid, nqb, p.B * H);
+  const BlockMap bm = (CAUSAL && !SPLIT && !SPARSE && p.pair_slots > 0)
+                          ? map_block_pairs(wgid, nqb, p.B * H, p.pair_slots, p.cus_per_xcd)
+                          : map_block(wgid, nqb, p.B * H);
   const int qb = CAUSAL ? (nqb - 1 - bm.rank) : bm.rank;
   const int b = bm.bh / H, h = bm.bh - b * H;
   const SeqRows sr = seq_rows(p.cu, p.total, b, h, H, D, p.N);
@@ -714,29 +720,73 @@ bool fwd_sixteen_waves(int N) {
   return D <= 80 && !DROP && N >= 32768;
 }
 
+// CUs of the current device (cached per device; 0 if the query fails).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Work-groups of `kernel` that one CU holds at once (cached per instance;
+// the kernels' resources do not depend on the device among gfx950 parts).
+template <auto Kernel>
+int resident_per_cu(int threads) {
+  static std::atomic<int> cache{-1};
+  int n = cache.load(std::memory_order_relaxed);
+  if (n < 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(Kernel), threads, 0) !=
+        hipSuccess)
+      n = 0;
+    cache.store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Launches a fixed-length forward instance. For causal masks whose grid fits
+// the device at once as an even number of work-groups per CU, the blocks are
+// paired so that every CU gets equal work (map_block_pairs); the results do
+// not depend on which work-group computes which block.
+template <auto Kernel>
+hipError_t launch_fwd_grid(int nblocks, int threads, bool causal, const FwdParams& prm, hipStream_t s) {
+  FwdParams p = prm;
+  p.pair_slots = 0;
+  p.cus_per_xcd = 0;
+  const int BH = prm.B * prm.H;
+  if (causal && prm.cu == nullptr && (BH & 7) == 0 && ((nblocks / BH) & 1) == 0) {
+    const int ncu = device_cus();
+    if (ncu > 0 && (ncu & 7) == 0 && nblocks % ncu == 0) {
+      const int slots = nblocks / ncu;
+      if ((slots & 1) == 0 && slots <= resident_per_cu<Kernel>(threads)) {
+        p.pair_slots = slots;
+        p.cus_per_xcd = ncu / 8;
+      }
+    }
+  }
+  hipLaunchKernelGGL(Kernel, dim3(nblocks), dim3(threads), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL, bool DROP, bool SPARSE>
 hipError_t launch_fwd_bf16_t(const FwdParams& prm, hipStream_t s) {
   // A block mask row covers 128 queries: block-sparse runs keep four waves.
   if constexpr (!SPARSE) {
     if constexpr (D <= 80 && !DROP) {  // the only instances built with sixteen waves
-      if (fwd_sixteen_waves<D, DROP>(prm.N)) {
-        const int nblocks = (prm.N + 511) / 512 * prm.B * prm.H;
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROP, SPARSE, false, false, 16>),
-                           dim3(nblocks), dim3(1024), 0, s, prm);
-        return hipGetLastError();
-      }
+      if (fwd_sixteen_waves<D, DROP>(prm.N))
+        return launch_fwd_grid<fwd_bf16_kernel<D, CAUSAL, DROP, SPARSE, false, false, 16>>(
+            (prm.N + 511) / 512 * prm.B * prm.H, 1024, CAUSAL, prm, s);
     }
-    if (fwd_eight_waves<D, DROP>(prm.N)) {
-      const int nblocks = (prm.N + 255) / 256 * prm.B * prm.H;
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROP, SPARSE, false, false, 8>), dim3(nblocks),
-                         dim3(512), 0, s, prm);
-      return hipGetLastError();
-    }
+    if (fwd_eight_waves<D, DROP>(prm.N))
+      return launch_fwd_grid<fwd_bf16_kernel<D, CAUSAL, DROP, SPARSE, false, false, 8>>(
+          (prm.N + 255) / 256 * prm.B * prm.H, 512, CAUSAL, prm, s);
   }
-  const int nblocks = (prm.N + 127) / 128 * prm.B * prm.H;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, DROP, SPARSE, false, false, 4>), dim3(nblocks),
-                     dim3(256), 0, s, prm);
-  return hipGetLastError();
+  return launch_fwd_grid<fwd_bf16_kernel<D, CAUSAL, DROP, SPARSE, false, false, 4>>(
+      (prm.N + 127) / 128 * prm.B * prm.H, 256, CAUSAL && !SPARSE, prm, s);
 }
 
 // Split-KV combine: for each query row, LSE = ln sum_s e^{LSE_s} and

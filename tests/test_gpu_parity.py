@@ -81,6 +81,27 @@ def test_forward_matches_oracle(w):
     assert_close("LSE", lse, lse_ref, w.dtype)
 
 
+# Causal grids that the device holds at once as an even number of work-groups
+# per CU (256 CUs): the launcher pairs the blocks (r, nblk - 1 - r) per CU.
+# Two and four work-groups per CU at d = 64, two at d = 128.
+PAIR_CASES = [
+    _case(2, B=4, H=16, N=1024),
+    _case(2, B=8, H=16, N=1024),
+    _case(3, B=4, H=16, N=1024),
+]
+
+
+@pytest.mark.parametrize("w", PAIR_CASES, ids=_ids(PAIR_CASES))
+def test_forward_resident_grid_pairs(w):
+    inp = make_inputs(w, with_grad=False)
+    dev, val = device_inputs(inp, w.dtype)
+    o, lse = _run_fwd(dev, w)
+    o_ref, lse_ref = oracle.forward(val["q"], val["k"], val["v"], w.scale, w.causal, w.dropout_p,
+                                    w.dropout_seed)
+    assert_close("O", o, o_ref, w.dtype)
+    assert_close("LSE", lse, lse_ref, w.dtype)
+
+
 def test_eight_wave_dropout_forward_rows():
     """Dropout runs from N = 32768 take the eight-wave forward; at N = 32800
     the last 256-row work-group holds 32 rows. Rows at the start, across a
