@@ -242,6 +242,25 @@ __device__ __forceinline__ BlockMap map_block(int id, int nblk, int BH) {
   return m;
 }
 
+// Complementary causal block pairs, one pair per work-group: a linear id
+// maps to (pair index, batch*heads index). Heads are dealt to XCDs as in
+// map_block; within an XCD consecutive ids take consecutive pairs of one
+// head, so the work-groups resident at once share that head's K/V.
+__device__ __forceinline__ BlockMap map_block_pair(int id, int npairs, int BH) {
+  BlockMap m;
+  if ((BH & 7) == 0) {
+    const int xcd = id & 7;
+    const int local = id >> 3;
+    const int hl = local / npairs;
+    m.rank = local - hl * npairs;
+    m.bh = hl * 8 + xcd;
+  } else {
+    m.rank = id / BH;
+    m.bh = id - m.rank * BH;
+  }
+  return m;
+}
+
 // Causal blocks when the whole grid is resident at once: the grid is
 // 8 XCDs x `cpx` CUs x `slots` work-groups, `slots` even and within the
 // kernel's occupancy. Work-groups are dispatched round-robin over the XCDs

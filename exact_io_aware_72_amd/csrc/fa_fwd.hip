@@ -55,6 +55,7 @@ struct FwdParams {
   // Causal, whole grid resident: work-groups per CU and CUs per XCD for
   // map_block_pairs; pair_slots = 0 keeps the rank-major map_block.
   int pair_slots, cus_per_xcd;
+  int pair_blocks;  // causal: complementary block pairs per work-group
   // Split-KV: Nk key rows per batch item (N query rows), the key range cut
   // into nsplit parts; part s writes O_s (fp32, normalised) and LSE_s.
   int Nk, nsplit;
@@ -127,10 +128,22 @@ __attribute__((amdgpu_waves_per_eu(1, ((D == 64 && !FP8) || NW == 16) ? 4 : 2)))
     split = wgid % p.nsplit;
     wgid /= p.nsplit;
   }
-  const BlockMap bm = (CAUSAL && !SPLIT && !SPARSE && p.pair_slots > 0)
-                          ? map_block_pairs(wgid, nqb, p.B * H, p.pair_slots, p.cus_per_xcd)
-                          : map_block(wgid, nqb, p.B * H);
-  const int qb = CAUSAL ? (nqb - 1 - bm.rank) : bm.rank;
+  // Causal blocks: one per work-group (rank-major, or paired across the
+  // work-groups of a CU), or with p.pair_blocks a complementary pair
+  // (nqb - 1 - j, then j) per work-group, so that every work-group has the
+  // same work and co-resident groups sweep the same K/V tiles in step.
+  BlockMap bm;
+  int qb_first, qb_second = -1;
+  if (CAUSAL && !SPLIT && !SPARSE && p.pair_blocks) {
+    bm = map_block_pair(wgid, (nqb + 1) / 2, p.B * H);
+    qb_first = nqb - 1 - bm.rank;
+    if (bm.rank < qb_first) qb_second = bm.rank;
+  } else {
+    bm = (CAUSAL && !SPLIT && !SPARSE && p.pair_slots > 0)
+             ? map_block_pairs(wgid, nqb, p.B * H, p.pair_slots, p.cus_per_xcd)
+             : map_block(wgid, nqb, p.B * H);
+    qb_first = CAUSAL ? (nqb - 1 - bm.rank) : bm.rank;
+  }
   const int b = bm.bh / H, h = bm.bh - b * H;
   const SeqRows sr = seq_rows(p.cu, p.total, b, h, H, D, p.N);
   const int N = sr.n;             // query rows
@@ -138,350 +151,360 @@ __attribute__((amdgpu_waves_per_eu(1, ((D == 64 && !FP8) || NW == 16) ? 4 : 2)))
   // Causal: key j is visible to query i iff j <= i + coff; with Nk > N the
   // queries are the last N positions of the key sequence.
   const int coff = Nk - N;
-  const int q0 = qb * C::BM;
-  if (q0 >= N) return;  // block past the end of a shorter sequence
-  const int qw0 = q0 + wave * 32;
-  const int myq = qw0 + l32;
-  const int64_t rs = (int64_t)H * D;
-  const int64_t base = sr.base;
-  const int64_t kbase = SPLIT ? ((int64_t)b * Nk * H + h) * D : base;
-  const uint16_t* Qg = p.q + base;
-  const uint16_t* Vg = p.v + kbase;
-  const uint32_t rs2 = (uint32_t)(H * D * 2);  // bytes between consecutive rows
-  // K rows: bf16, or FP8 bytes (one byte per element).
-  const char* Kb = FP8 ? reinterpret_cast<const char*>(p.k8 + kbase)
-                       : reinterpret_cast<const char*>(p.k + kbase);
-  const uint32_t rsk = FP8 ? (uint32_t)(H * D) : rs2;
+  // rev: the key tiles in descending order (the second block of a pair).
+  auto run_block = [&](const int qb, const bool rev) {
+    const int q0 = qb * C::BM;
+    if (q0 >= N) return;  // block past the end of a shorter sequence
+    const int qw0 = q0 + wave * 32;
+    const int myq = qw0 + l32;
+    const int64_t rs = (int64_t)H * D;
+    const int64_t base = sr.base;
+    const int64_t kbase = SPLIT ? ((int64_t)b * Nk * H + h) * D : base;
+    const uint16_t* Qg = p.q + base;
+    const uint16_t* Vg = p.v + kbase;
+    const uint32_t rs2 = (uint32_t)(H * D * 2);  // bytes between consecutive rows
+    // K rows: bf16, or FP8 bytes (one byte per element).
+    const char* Kb = FP8 ? reinterpret_cast<const char*>(p.k8 + kbase)
+                         : reinterpret_cast<const char*>(p.k + kbase);
+    const uint32_t rsk = FP8 ? (uint32_t)(H * D) : rs2;
 
-  // Q operand (B of S^T = K Q^T): 8 d-values per lane per 16-wide chunk
-  // (bf16), or 32 bytes per lane per 64-wide chunk (FP8, in qreg[2c],
-  // qreg[2c+1]); rows >= N read as zeros through the buffer range check.
-  u32x4 qreg[C::NKC];
-  float qsc = 1.f;  // FP8: this query block's scale
-  if constexpr (FP8) {
-    const BufRes rq = make_bufres(p.q8 + base, (uint32_t)N * rsk);
-#pragma unroll
-    for (int c = 0; c < NK8; ++c)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        // chunks past D (D = 80) read as zeros through an out-of-range offset
-        const int ch = 4 * c + 2 * hf + u;
-        qreg[2 * c + u] = buf_load_128(rq, ch < KT::VALID ? (uint32_t)myq * rsk + 16 * ch : 0x80000000u);
-      }
-    qsc = p.q_scale[((int64_t)b * H + h) * nqb + qb];
-  } else {
-    const BufRes rq = make_bufres(Qg, (uint32_t)N * rs2);
-#pragma unroll
-    for (int c = 0; c < C::NKC; ++c)
-      qreg[c] = buf_load_128(rq, (uint32_t)myq * rs2 + (16 * c + 8 * hf) * 2);
-  }
-  // FP8: the key tiles' scales, one per 64 keys; the next tile's is loaded
-  // with its tile (and so has arrived when that tile's loads have).
-  const BufRes rks = make_bufres(FP8 ? p.k_scale + ((int64_t)b * H + h) * ((Nk + 63) / 64) : nullptr,
-                                 FP8 ? (uint32_t)((Nk + 63) / 64) * 4 : 0u);
-  float ksn = 1.f;
-
-  uint64_t kbh = 0;
-  uint32_t arow = 0;
-  if constexpr (DROP) {
-    kbh = head_key(p.seed, b, h, H);
-    arow = row_key(kbh, myq);
-  }
-
-  const int kend = CAUSAL ? min(Nk, q0 + C::BM + coff) : Nk;
-  int ntiles, tfirst = 0;
-  if constexpr (SPLIT) {
-    // This part's share of the key tiles: parts of equal tile counts.
-    const int all = (kend + C::BN - 1) / C::BN;
-    const int per = (all + p.nsplit - 1) / p.nsplit;
-    tfirst = min(all, split * per);
-    ntiles = min(all, tfirst + per) - tfirst;
-  } else if constexpr (SPARSE) {
-    // Kept key blocks of this query block, in ascending order.
-    const int nb = (N + kSparseBlock - 1) / kSparseBlock;
-    const uint8_t* mrow = p.bmask + b * p.msb + h * p.msh + (int64_t)qb * nb;
-    const KeptBlocks kb =
-        collect_blocks(mrow, 1, 0, (kend + kSparseBlock - 1) / kSparseBlock, kept, lane, wave == 0);
-    ntiles = kept_tiles<C::BN>(kb, kend);
-    __syncthreads();
-  } else {
-    ntiles = (kend + C::BN - 1) / C::BN;
-  }
-  auto tile_start = [&](int t) {
-    return SPARSE ? kept_tile_start<C::BN>(kept, t) : (tfirst + t) * C::BN;
-  };
-
-  // This wave's share of the tile loads: K instructions first, then V.
-  uint32_t dsrc[C::LPW];
-  int dlds[C::LPW];
-#pragma unroll
-  for (int m = 0; m < C::LPW; ++m) {
-    const int i = (wave % C::NW) + C::NW * m;
-    int off = 0, row = 0, ch = 0;
-    if (i < KT::NLOAD) {
-      KT::load_slot(i, lane, off, row, ch);
-    } else if (i < C::NLOAD) {
-      VT::load_slot(i - KT::NLOAD, lane, off, row, ch);
-      off += KT::BYTES;
-    }
-    dsrc[m] = (uint32_t)row * (i < KT::NLOAD ? rsk : rs2) + 16 * ch;
+    // Q operand (B of S^T = K Q^T): 8 d-values per lane per 16-wide chunk
+    // (bf16), or 32 bytes per lane per 64-wide chunk (FP8, in qreg[2c],
+    // qreg[2c+1]); rows >= N read as zeros through the buffer range check.
+    u32x4 qreg[C::NKC];
+    float qsc = 1.f;  // FP8: this query block's scale
     if constexpr (FP8) {
-      // Chunks past D in a padded FP8 row: an offset beyond every buffer
-      // range makes the load return zeros.
-      if (i < KT::NLOAD && ch >= KT::VALID) dsrc[m] = 0x80000000u;
+      const BufRes rq = make_bufres(p.q8 + base, (uint32_t)N * rsk);
+  #pragma unroll
+      for (int c = 0; c < NK8; ++c)
+  #pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          // chunks past D (D = 80) read as zeros through an out-of-range offset
+          const int ch = 4 * c + 2 * hf + u;
+          qreg[2 * c + u] = buf_load_128(rq, ch < KT::VALID ? (uint32_t)myq * rsk + 16 * ch : 0x80000000u);
+        }
+      qsc = p.q_scale[((int64_t)b * H + h) * nqb + qb];
+    } else {
+      const BufRes rq = make_bufres(Qg, (uint32_t)N * rs2);
+  #pragma unroll
+      for (int c = 0; c < C::NKC; ++c)
+        qreg[c] = buf_load_128(rq, (uint32_t)myq * rs2 + (16 * c + 8 * hf) * 2);
     }
-    dlds[m] = off;
-  }
-  auto issue = [&](char* stage, uint32_t* ck, int k0) {
-    // Resources start at row k0 and end at row N: rows past N arrive as zeros.
-    const BufRes rk = make_bufres(Kb + (int64_t)k0 * rsk, (uint32_t)(Nk - k0) * rsk);
-    const BufRes rv = make_bufres(Vg + (int64_t)k0 * rs, (uint32_t)(Nk - k0) * rs2);
-    if constexpr (FP8) ksn = buf_load_f32(rks, (uint32_t)(k0 >> 6) * 4);
-#pragma unroll
+    // FP8: the key tiles' scales, one per 64 keys; the next tile's is loaded
+    // with its tile (and so has arrived when that tile's loads have).
+    const BufRes rks = make_bufres(FP8 ? p.k_scale + ((int64_t)b * H + h) * ((Nk + 63) / 64) : nullptr,
+                                   FP8 ? (uint32_t)((Nk + 63) / 64) * 4 : 0u);
+    float ksn = 1.f;
+
+    uint64_t kbh = 0;
+    uint32_t arow = 0;
+    if constexpr (DROP) {
+      kbh = head_key(p.seed, b, h, H);
+      arow = row_key(kbh, myq);
+    }
+
+    const int kend = CAUSAL ? min(Nk, q0 + C::BM + coff) : Nk;
+    int ntiles, tfirst = 0;
+    if constexpr (SPLIT) {
+      // This part's share of the key tiles: parts of equal tile counts.
+      const int all = (kend + C::BN - 1) / C::BN;
+      const int per = (all + p.nsplit - 1) / p.nsplit;
+      tfirst = min(all, split * per);
+      ntiles = min(all, tfirst + per) - tfirst;
+    } else if constexpr (SPARSE) {
+      // Kept key blocks of this query block, in ascending order.
+      const int nb = (N + kSparseBlock - 1) / kSparseBlock;
+      const uint8_t* mrow = p.bmask + b * p.msb + h * p.msh + (int64_t)qb * nb;
+      const KeptBlocks kb =
+          collect_blocks(mrow, 1, 0, (kend + kSparseBlock - 1) / kSparseBlock, kept, lane, wave == 0);
+      ntiles = kept_tiles<C::BN>(kb, kend);
+      __syncthreads();
+    } else {
+      ntiles = (kend + C::BN - 1) / C::BN;
+    }
+    auto tile_start = [&](int t) {
+      if (rev) t = ntiles - 1 - t;
+      return SPARSE ? kept_tile_start<C::BN>(kept, t) : (tfirst + t) * C::BN;
+    };
+
+    // This wave's share of the tile loads: K instructions first, then V.
+    uint32_t dsrc[C::LPW];
+    int dlds[C::LPW];
+  #pragma unroll
     for (int m = 0; m < C::LPW; ++m) {
       const int i = (wave % C::NW) + C::NW * m;
-      if (i < C::NLOAD) lds_dma_16(i < KT::NLOAD ? rk : rv, stage + dlds[m], dsrc[m]);
-    }
-    if constexpr (DROP) {
-      if (tid < C::BN / 2) ck[tid] = pair_key(kbh, (k0 >> 1) + tid);
-    }
-  };
-
-  // Per-lane LDS offsets of the matrix-core operands (loop invariant).
-  // K rows l32 (scores s0) and l32 + 32 (s1), chunk 2c + hf: the swizzle of
-  // row l32 + 32 is that of row l32 with bit 2 flipped.
-  const int xk = hf ^ KT::sw(l32);
-  int ka[4] = {0, 0, 0, 0};
-  int ktl = 0;
-  if constexpr (!FP8) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) ka[u] = l32 * 128 + (((2 * u) ^ xk) << 4);
-    ktl = KT::TAIL + l32 * 32 + ((hf ^ KT::swt(l32)) << 4);
-  }
-  // FP8: 64-wide k-step c reads chunks 4c + 2hf + u (u = 0, 1) of rows l32
-  // (fo) and l32 + 32 (fo2).
-  int fo[NK8][2], fo2[NK8][2];
-  if constexpr (FP8) {
-#pragma unroll
-    for (int c = 0; c < NK8; ++c)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        fo[c][u] = KT::off(l32, 4 * c + 2 * hf + u);
-        fo2[c][u] = KT::off(l32 + 32, 4 * c + 2 * hf + u);
+      int off = 0, row = 0, ch = 0;
+      if (i < KT::NLOAD) {
+        KT::load_slot(i, lane, off, row, ch);
+      } else if (i < C::NLOAD) {
+        VT::load_slot(i - KT::NLOAD, lane, off, row, ch);
+        off += KT::BYTES;
       }
-  }
-  // V: 16-lane group g reads rows 4(g/2) + j (+ 8h + 16kt), columns
-  // 16(g%2) + 4a (+ 32db) for lane 4j + a of the group; the uniform part of
-  // the swizzle selects one of four precomputed offsets.
-  const int vg = lane >> 4, vj = (lane >> 2) & 3, va = lane & 3;
-  const int vs = vg >> 1, vgh = vg & 1;
-  const int vlp = (2 * vgh) ^ (va >> 1) ^ (2 * vj) ^ vs;
-  int vaoff[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    vaoff[u] = KT::BYTES + (4 * vs + vj) * 128 + ((vlp ^ (2 * u)) << 4) + 8 * (va & 1);
-  const int vtl = KT::BYTES + VT::TAIL + (4 * vs + vj) * 32 + 8 * va;
+      dsrc[m] = (uint32_t)row * (i < KT::NLOAD ? rsk : rs2) + 16 * ch;
+      if constexpr (FP8) {
+        // Chunks past D in a padded FP8 row: an offset beyond every buffer
+        // range makes the load return zeros.
+        if (i < KT::NLOAD && ch >= KT::VALID) dsrc[m] = 0x80000000u;
+      }
+      dlds[m] = off;
+    }
+    auto issue = [&](char* stage, uint32_t* ck, int k0) {
+      // Resources start at row k0 and end at row N: rows past N arrive as zeros.
+      const BufRes rk = make_bufres(Kb + (int64_t)k0 * rsk, (uint32_t)(Nk - k0) * rsk);
+      const BufRes rv = make_bufres(Vg + (int64_t)k0 * rs, (uint32_t)(Nk - k0) * rs2);
+      if constexpr (FP8) ksn = buf_load_f32(rks, (uint32_t)(k0 >> 6) * 4);
+  #pragma unroll
+      for (int m = 0; m < C::LPW; ++m) {
+        const int i = (wave % C::NW) + C::NW * m;
+        if (i < C::NLOAD) lds_dma_16(i < KT::NLOAD ? rk : rv, stage + dlds[m], dsrc[m]);
+      }
+      if constexpr (DROP) {
+        if (tid < C::BN / 2) ck[tid] = pair_key(kbh, (k0 >> 1) + tid);
+      }
+    };
 
-  // Running statistics in base-2 units of the scaled scores. The reference
-  // max m only moves when a tile's max exceeds it by more than kLazy (then
-  // O and l are rescaled); otherwise probabilities up to 2^kLazy are summed
-  // against the old reference. O and l always share one reference, so the
-  // final O / l and LSE are exact.
-  constexpr float kLazy = 8.0f;
-  const float c2 = p.c2;
-  float m = -INFINITY, l = 0.f;
-  f32x16 oacc[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16{};
-
-  auto step = [&](const char* cur, const uint32_t* ckc, char* nxt, uint32_t* ckn, int t) {
-    // Tile t has landed in `cur` once every wave's loads are done; after the
-    // barrier nobody reads `nxt` any more, so the next tile can go there.
-    wait_vmem();
-    __syncthreads();
-    if constexpr (kLdsPoison) poison_stage(nxt, C::STAGE, tid, C::NT);
-    const int k0 = tile_start(t);
-    // Exponent coefficient of this tile (FP8: times the two block scales).
-    const float c2t = FP8 ? c2 * qsc * ksn : c2;
-    if (t + 1 < ntiles) issue(nxt, ckn, tile_start(t + 1));
-    if (CAUSAL && k0 > qw0 + 31 + coff) return;  // every key is after this wave's queries
-    if (SPLIT && qw0 >= N) return;                // no query rows in this wave
-
-    // S^T = K Q^T: lane = query, registers = keys (c_row layout).
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    // Per-lane LDS offsets of the matrix-core operands (loop invariant).
+    // K rows l32 (scores s0) and l32 + 32 (s1), chunk 2c + hf: the swizzle of
+    // row l32 + 32 is that of row l32 with bit 2 flipped.
+    const int xk = hf ^ KT::sw(l32);
+    int ka[4] = {0, 0, 0, 0};
+    int ktl = 0;
+    if constexpr (!FP8) {
+  #pragma unroll
+      for (int u = 0; u < 4; ++u) ka[u] = l32 * 128 + (((2 * u) ^ xk) << 4);
+      ktl = KT::TAIL + l32 * 32 + ((hf ^ KT::swt(l32)) << 4);
+    }
+    // FP8: 64-wide k-step c reads chunks 4c + 2hf + u (u = 0, 1) of rows l32
+    // (fo) and l32 + 32 (fo2).
+    int fo[NK8][2], fo2[NK8][2];
     if constexpr (FP8) {
-#pragma unroll
-      for (int c = 0; c < NK8; ++c) {
-        const u32x4 x0 = ld_lds_128(cur, fo[c][0]), x1 = ld_lds_128(cur, fo[c][1]);
-        const u32x4 y0 = ld_lds_128(cur, fo2[c][0]), y1 = ld_lds_128(cur, fo2[c][1]);
-        s0 = mfma32x32x64_fp8(x0, x1, qreg[2 * c], qreg[2 * c + 1], s0);
-        s1 = mfma32x32x64_fp8(y0, y1, qreg[2 * c], qreg[2 * c + 1], s1);
-      }
-      sched_lds_ahead<NK8, 4, 2, 0, 1>();
-    } else {
-#pragma unroll
-    for (int c = 0; c < C::NKC; ++c) {
-      int o0, o1;
-      if (2 * c < 8 * KT::NG) {
-        o0 = (c >> 2) * KT::GBYTES + ka[c & 3];
-        o1 = (c >> 2) * KT::GBYTES + 4096 + ka[(c & 3) ^ 2];
+  #pragma unroll
+      for (int c = 0; c < NK8; ++c)
+  #pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          fo[c][u] = KT::off(l32, 4 * c + 2 * hf + u);
+          fo2[c][u] = KT::off(l32 + 32, 4 * c + 2 * hf + u);
+        }
+    }
+    // V: 16-lane group g reads rows 4(g/2) + j (+ 8h + 16kt), columns
+    // 16(g%2) + 4a (+ 32db) for lane 4j + a of the group; the uniform part of
+    // the swizzle selects one of four precomputed offsets.
+    const int vg = lane >> 4, vj = (lane >> 2) & 3, va = lane & 3;
+    const int vs = vg >> 1, vgh = vg & 1;
+    const int vlp = (2 * vgh) ^ (va >> 1) ^ (2 * vj) ^ vs;
+    int vaoff[4];
+  #pragma unroll
+    for (int u = 0; u < 4; ++u)
+      vaoff[u] = KT::BYTES + (4 * vs + vj) * 128 + ((vlp ^ (2 * u)) << 4) + 8 * (va & 1);
+    const int vtl = KT::BYTES + VT::TAIL + (4 * vs + vj) * 32 + 8 * va;
+
+    // Running statistics in base-2 units of the scaled scores. The reference
+    // max m only moves when a tile's max exceeds it by more than kLazy (then
+    // O and l are rescaled); otherwise probabilities up to 2^kLazy are summed
+    // against the old reference. O and l always share one reference, so the
+    // final O / l and LSE are exact.
+    constexpr float kLazy = 8.0f;
+    const float c2 = p.c2;
+    float m = -INFINITY, l = 0.f;
+    f32x16 oacc[C::NDB];
+  #pragma unroll
+    for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16{};
+
+    auto step = [&](const char* cur, const uint32_t* ckc, char* nxt, uint32_t* ckn, int t) {
+      // Tile t has landed in `cur` once every wave's loads are done; after the
+      // barrier nobody reads `nxt` any more, so the next tile can go there.
+      wait_vmem();
+      __syncthreads();
+      if constexpr (kLdsPoison) poison_stage(nxt, C::STAGE, tid, C::NT);
+      const int k0 = tile_start(t);
+      // Exponent coefficient of this tile (FP8: times the two block scales).
+      const float c2t = FP8 ? c2 * qsc * ksn : c2;
+      if (t + 1 < ntiles) issue(nxt, ckn, tile_start(t + 1));
+      if (CAUSAL && k0 > qw0 + 31 + coff) return;  // every key is after this wave's queries
+      if (SPLIT && qw0 >= N) return;                // no query rows in this wave
+
+      // S^T = K Q^T: lane = query, registers = keys (c_row layout).
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
+      if constexpr (FP8) {
+  #pragma unroll
+        for (int c = 0; c < NK8; ++c) {
+          const u32x4 x0 = ld_lds_128(cur, fo[c][0]), x1 = ld_lds_128(cur, fo[c][1]);
+          const u32x4 y0 = ld_lds_128(cur, fo2[c][0]), y1 = ld_lds_128(cur, fo2[c][1]);
+          s0 = mfma32x32x64_fp8(x0, x1, qreg[2 * c], qreg[2 * c + 1], s0);
+          s1 = mfma32x32x64_fp8(y0, y1, qreg[2 * c], qreg[2 * c + 1], s1);
+        }
+        sched_lds_ahead<NK8, 4, 2, 0, 1>();
       } else {
-        o0 = ktl;
-        o1 = ktl + 1024;
-      }
-      s0 = mfma32x32x16(ld_lds_128(cur, o0), qreg[c], s0);
-      s1 = mfma32x32x16(ld_lds_128(cur, o1), qreg[c], s1);
-    }
-    sched_lds_ahead<C::NKC, 2, 2>();
-    }
-    if ((k0 + C::BN > Nk) || (CAUSAL && k0 + C::BN - 1 > qw0 + coff)) {
-      const int lim = CAUSAL ? min(myq + coff, Nk - 1) : Nk - 1;  // last visible key
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + c_row(r, hf);
-        s0[r] = key > lim ? -INFINITY : s0[r];
-        s1[r] = key + 32 > lim ? -INFINITY : s1[r];
-      }
-    }
-    float ma = fmaxf(s0[0], s0[1]), mb = fmaxf(s1[0], s1[1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) {
-      ma = fmaxf(fmaxf(ma, s0[r]), s0[r + 1]);
-      mb = fmaxf(fmaxf(mb, s1[r]), s1[r + 1]);
-    }
-    const float mx = xor32_max(fmaxf(ma, mb)) * c2t;
-    if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
-      const float mnew = fmaxf(m, mx);
-      // Rows without a visible key so far (only in a split key range) have
-      // l = 0 and O = 0: scale 0 instead of exp2(-inf - -inf).
-      const float alpha = (SPLIT && m == -INFINITY) ? 0.f : exp2_hw(m - mnew);
-      m = mnew;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) oacc[db] *= alpha;
-    }
-    // A part of a split key range can start with a tile in which some rows
-    // see no key yet (m = -inf); they take reference 0 so that exp2 gives 0.
-    const float nm = (SPLIT && m == -INFINITY) ? 0.f : -m;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = exp2_hw(fmaf(s0[r], c2t, nm));
-      s1[r] = exp2_hw(fmaf(s1[r], c2t, nm));
-    }
-    if constexpr (DROP) {
-      // l sums the probabilities before dropout.
-      float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        ps0 += s0[r];
-        ps1 += s1[r];
-      }
-      l += ps0 + ps1;
-      // Register 4g + e holds key 8g + 4hf + e: keys (e, e + 1) for e = 0, 2
-      // are a pair and share one hash.
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 c0 = *reinterpret_cast<const u32x2*>(ckc + 4 * g + 2 * hf);
-        const u32x2 c1 = *reinterpret_cast<const u32x2*>(ckc + 16 + 4 * g + 2 * hf);
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          const uint32_t y0 = pair_mix(arow, c0[e >> 1]);
-          const uint32_t y1 = pair_mix(arow, c1[e >> 1]);
-          s0[4 * g + e] = keep_even(y0, p.drop_t) ? s0[4 * g + e] : 0.f;
-          s0[4 * g + e + 1] = keep_odd(y0, p.drop_t) ? s0[4 * g + e + 1] : 0.f;
-          s1[4 * g + e] = keep_even(y1, p.drop_t) ? s1[4 * g + e] : 0.f;
-          s1[4 * g + e + 1] = keep_odd(y1, p.drop_t) ? s1[4 * g + e + 1] : 0.f;
-        }
-      }
-    }
-    // P^T as the B operand, bf16, in 16-key steps; without dropout the row
-    // sum is taken on these rounded values (v_dot2 with ones).
-    u32x4 pop[4];
-    float la = 0.f, lb = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const f32x16& sv = (kt < 2) ? s0 : s1;
-      const int rb = (kt & 1) * 8;
-      pop[kt] = u32x4{pack_bf16x2(sv[rb + 0], sv[rb + 1]), pack_bf16x2(sv[rb + 2], sv[rb + 3]),
-                      pack_bf16x2(sv[rb + 4], sv[rb + 5]), pack_bf16x2(sv[rb + 6], sv[rb + 7])};
-      if constexpr (!DROP) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          float& acc = (w & 1) ? lb : la;
-          acc = add_bf16_pair(pop[kt][w], acc);
-        }
-      }
-    }
-    if constexpr (!DROP) l += la + lb;
-    // O^T += V^T P^T: V fragments by transposing reads (two per operand).
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        u32x2 v0, v1;
-        if (4 * db < 8 * VT::NG) {
-          const int gb = (db >> 1) * VT::GBYTES + 2048 * kt;
-          const int u = 2 * ((db ^ kt) & 1);
-          v0 = ld_lds_tr16(cur, gb + vaoff[u]);
-          v1 = ld_lds_tr16(cur, gb + 1024 + vaoff[u + 1]);
+  #pragma unroll
+      for (int c = 0; c < C::NKC; ++c) {
+        int o0, o1;
+        if (2 * c < 8 * KT::NG) {
+          o0 = (c >> 2) * KT::GBYTES + ka[c & 3];
+          o1 = (c >> 2) * KT::GBYTES + 4096 + ka[(c & 3) ^ 2];
         } else {
-          v0 = ld_lds_tr16(cur, vtl + 512 * kt);
-          v1 = ld_lds_tr16(cur, vtl + 512 * kt + 256);
+          o0 = ktl;
+          o1 = ktl + 1024;
         }
-        const u32x4 aop = {v0[0], v0[1], v1[0], v1[1]};
-        oacc[db] = mfma32x32x16(aop, pop[kt], oacc[db]);
+        s0 = mfma32x32x16(ld_lds_128(cur, o0), qreg[c], s0);
+        s1 = mfma32x32x16(ld_lds_128(cur, o1), qreg[c], s1);
       }
-    }
-  };
-
-  if constexpr (kLdsPoison) poison_stage(st0, C::STAGE, tid, C::NT);
-  if (ntiles > 0) issue(st0, ck0, tile_start(0));
-  for (int t = 0; t < ntiles; t += 2) {
-    step(st0, ck0, st1, ck1, t);
-    if (t + 1 < ntiles) step(st1, ck1, st0, ck0, t + 1);
-  }
-
-  const float ltot = xor32_sum(l);
-  if constexpr (SPLIT) {
-    // Partial result of this key range, normalised by its own sum; a range
-    // with no visible key gives O_s = 0 and LSE_s = -inf.
-    if (myq < N) {
-      const int64_t row = (((int64_t)split * p.B + b) * H + h) * N + myq;
-      const float inv = ltot == 0.f ? 0.f : 1.f / ltot;
-      float* orow = p.ws_o + row * D;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
+      sched_lds_ahead<C::NKC, 2, 2>();
+      }
+      if ((k0 + C::BN > Nk) || (CAUSAL && k0 + C::BN - 1 > qw0 + coff)) {
+        const int lim = CAUSAL ? min(myq + coff, Nk - 1) : Nk - 1;  // last visible key
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + c_row(r, hf);
+          s0[r] = key > lim ? -INFINITY : s0[r];
+          s1[r] = key + 32 > lim ? -INFINITY : s1[r];
+        }
+      }
+      float ma = fmaxf(s0[0], s0[1]), mb = fmaxf(s1[0], s1[1]);
+  #pragma unroll
+      for (int r = 2; r < 16; r += 2) {
+        ma = fmaxf(fmaxf(ma, s0[r]), s0[r + 1]);
+        mb = fmaxf(fmaxf(mb, s1[r]), s1[r + 1]);
+      }
+      const float mx = xor32_max(fmaxf(ma, mb)) * c2t;
+      if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
+        const float mnew = fmaxf(m, mx);
+        // Rows without a visible key so far (only in a split key range) have
+        // l = 0 and O = 0: scale 0 instead of exp2(-inf - -inf).
+        const float alpha = (SPLIT && m == -INFINITY) ? 0.f : exp2_hw(m - mnew);
+        m = mnew;
+        l *= alpha;
+  #pragma unroll
+        for (int db = 0; db < C::NDB; ++db) oacc[db] *= alpha;
+      }
+      // A part of a split key range can start with a tile in which some rows
+      // see no key yet (m = -inf); they take reference 0 so that exp2 gives 0.
+      const float nm = (SPLIT && m == -INFINITY) ? 0.f : -m;
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] = exp2_hw(fmaf(s0[r], c2t, nm));
+        s1[r] = exp2_hw(fmaf(s1[r], c2t, nm));
+      }
+      if constexpr (DROP) {
+        // l sums the probabilities before dropout.
+        float ps0 = 0.f, ps1 = 0.f;
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          ps0 += s0[r];
+          ps1 += s1[r];
+        }
+        l += ps0 + ps1;
+        // Register 4g + e holds key 8g + 4hf + e: keys (e, e + 1) for e = 0, 2
+        // are a pair and share one hash.
+  #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int d0 = db * 32 + 8 * g + 4 * hf;
-          if (d0 < D) {
-            const f32x4 w = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
-                             oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
-            *reinterpret_cast<f32x4*>(orow + d0) = w;
+          const u32x2 c0 = *reinterpret_cast<const u32x2*>(ckc + 4 * g + 2 * hf);
+          const u32x2 c1 = *reinterpret_cast<const u32x2*>(ckc + 16 + 4 * g + 2 * hf);
+  #pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const uint32_t y0 = pair_mix(arow, c0[e >> 1]);
+            const uint32_t y1 = pair_mix(arow, c1[e >> 1]);
+            s0[4 * g + e] = keep_even(y0, p.drop_t) ? s0[4 * g + e] : 0.f;
+            s0[4 * g + e + 1] = keep_odd(y0, p.drop_t) ? s0[4 * g + e + 1] : 0.f;
+            s1[4 * g + e] = keep_even(y1, p.drop_t) ? s1[4 * g + e] : 0.f;
+            s1[4 * g + e + 1] = keep_odd(y1, p.drop_t) ? s1[4 * g + e + 1] : 0.f;
           }
         }
       }
-      if (hf == 0) p.ws_lse[row] = ltot == 0.f ? -INFINITY : (m + log2_hw(ltot)) * kLn2;
-    }
-    return;
-  }
-  if (myq < N) {
-    // A row whose blocks are all masked has no keys: O = 0, LSE = -inf.
-    const float inv = (SPARSE && ltot == 0.f) ? 0.f : (DROP ? p.drop_r : 1.f) / ltot;
-    uint16_t* orow = p.o + base + (int64_t)myq * rs;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = db * 32 + 8 * g + 4 * hf;
-        if (d0 < D) {
-          const u32x2 w = {pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                           pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-          st_global_64(orow + d0, w);
+      // P^T as the B operand, bf16, in 16-key steps; without dropout the row
+      // sum is taken on these rounded values (v_dot2 with ones).
+      u32x4 pop[4];
+      float la = 0.f, lb = 0.f;
+  #pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const f32x16& sv = (kt < 2) ? s0 : s1;
+        const int rb = (kt & 1) * 8;
+        pop[kt] = u32x4{pack_bf16x2(sv[rb + 0], sv[rb + 1]), pack_bf16x2(sv[rb + 2], sv[rb + 3]),
+                        pack_bf16x2(sv[rb + 4], sv[rb + 5]), pack_bf16x2(sv[rb + 6], sv[rb + 7])};
+        if constexpr (!DROP) {
+  #pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            float& acc = (w & 1) ? lb : la;
+            acc = add_bf16_pair(pop[kt][w], acc);
+          }
         }
       }
+      if constexpr (!DROP) l += la + lb;
+      // O^T += V^T P^T: V fragments by transposing reads (two per operand).
+  #pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+  #pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          u32x2 v0, v1;
+          if (4 * db < 8 * VT::NG) {
+            const int gb = (db >> 1) * VT::GBYTES + 2048 * kt;
+            const int u = 2 * ((db ^ kt) & 1);
+            v0 = ld_lds_tr16(cur, gb + vaoff[u]);
+            v1 = ld_lds_tr16(cur, gb + 1024 + vaoff[u + 1]);
+          } else {
+            v0 = ld_lds_tr16(cur, vtl + 512 * kt);
+            v1 = ld_lds_tr16(cur, vtl + 512 * kt + 256);
+          }
+          const u32x4 aop = {v0[0], v0[1], v1[0], v1[1]};
+          oacc[db] = mfma32x32x16(aop, pop[kt], oacc[db]);
+        }
+      }
+    };
+
+    if constexpr (kLdsPoison) poison_stage(st0, C::STAGE, tid, C::NT);
+    if (ntiles > 0) issue(st0, ck0, tile_start(0));
+    for (int t = 0; t < ntiles; t += 2) {
+      step(st0, ck0, st1, ck1, t);
+      if (t + 1 < ntiles) step(st1, ck1, st0, ck0, t + 1);
     }
-    if (hf == 0) p.lse[sr.stat + myq] = (m + log2_hw(ltot)) * kLn2;
+
+    const float ltot = xor32_sum(l);
+    if constexpr (SPLIT) {
+      // Partial result of this key range, normalised by its own sum; a range
+      // with no visible key gives O_s = 0 and LSE_s = -inf.
+      if (myq < N) {
+        const int64_t row = (((int64_t)split * p.B + b) * H + h) * N + myq;
+        const float inv = ltot == 0.f ? 0.f : 1.f / ltot;
+        float* orow = p.ws_o + row * D;
+  #pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+  #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = db * 32 + 8 * g + 4 * hf;
+            if (d0 < D) {
+              const f32x4 w = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
+                               oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
+              *reinterpret_cast<f32x4*>(orow + d0) = w;
+            }
+          }
+        }
+        if (hf == 0) p.ws_lse[row] = ltot == 0.f ? -INFINITY : (m + log2_hw(ltot)) * kLn2;
+      }
+      return;
+    }
+    if (myq < N) {
+      // A row whose blocks are all masked has no keys: O = 0, LSE = -inf.
+      const float inv = (SPARSE && ltot == 0.f) ? 0.f : (DROP ? p.drop_r : 1.f) / ltot;
+      uint16_t* orow = p.o + base + (int64_t)myq * rs;
+  #pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = db * 32 + 8 * g + 4 * hf;
+          if (d0 < D) {
+            const u32x2 w = {pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                             pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+            st_global_64(orow + d0, w);
+          }
+        }
+      }
+      if (hf == 0) p.lse[sr.stat + myq] = (m + log2_hw(ltot)) * kLn2;
+    }
+  };
+  run_block(qb_first, false);
+  if (qb_second >= 0) {
+    // The first block's last tile may still be read from a stage.
+    __syncthreads();
+    run_block(qb_second, true);
   }
 }
 
@@ -748,24 +771,43 @@ int resident_per_cu(int threads) {
   return n;
 }
 
-// Launches a fixed-length forward instance. For causal masks whose grid fits
-// the device at once as an even number of work-groups per CU, the blocks are
-// paired so that every CU gets equal work (map_block_pairs); the results do
-// not depend on which work-group computes which block.
+// Launches a fixed-length forward instance. Causal masks give block j about
+// j + 1 tiles of work, so blocks are paired:
+// - a grid that the device holds at once, as an even number of work-groups
+//   per CU: the work-groups of each CU take complementary blocks
+//   (map_block_pairs), so every CU gets equal work;
+// - a larger grid, when the paired grid still fills the device: each
+//   work-group takes the pair (nqb - 1 - j, j) (map_block_pair), the first
+//   block over ascending key tiles, the second over descending ones. Every
+//   work-group then does the same work, and at any moment the work-groups of
+//   one head read only two key tiles (position t of the first sweep and
+//   position const - t of the second), which the XCD's L2 holds: K and V
+//   are fetched from beyond L2 about once per generation of work-groups
+//   instead of once per block (N = 32768, d = 80: 2.19 to 0.52 GB per
+//   launch; N = 8192, d = 128: 0.82 to 0.25 GB).
+// The descending sweep changes only the order of the online softmax's
+// updates (results equal up to fp32 rounding order); which work-group
+// computes which block does not change any result.
 template <auto Kernel>
 hipError_t launch_fwd_grid(int nblocks, int threads, bool causal, const FwdParams& prm, hipStream_t s) {
   FwdParams p = prm;
   p.pair_slots = 0;
   p.cus_per_xcd = 0;
+  p.pair_blocks = 0;
   const int BH = prm.B * prm.H;
-  if (causal && prm.cu == nullptr && (BH & 7) == 0 && ((nblocks / BH) & 1) == 0) {
+  const int nqb = nblocks / BH;
+  if (causal && prm.cu == nullptr) {
     const int ncu = device_cus();
-    if (ncu > 0 && (ncu & 7) == 0 && nblocks % ncu == 0) {
-      const int slots = nblocks / ncu;
-      if ((slots & 1) == 0 && slots <= resident_per_cu<Kernel>(threads)) {
-        p.pair_slots = slots;
+    const int cap = ncu * resident_per_cu<Kernel>(threads);
+    if (nblocks <= cap) {
+      if ((BH & 7) == 0 && (nqb & 1) == 0 && ncu > 0 && (ncu & 7) == 0 && nblocks % ncu == 0 &&
+          ((nblocks / ncu) & 1) == 0) {
+        p.pair_slots = nblocks / ncu;
         p.cus_per_xcd = ncu / 8;
       }
+    } else if ((nqb + 1) / 2 * BH >= cap) {
+      p.pair_blocks = 1;
+      nblocks = (nqb + 1) / 2 * BH;
     }
   }
   hipLaunchKernelGGL(Kernel, dim3(nblocks), dim3(threads), 0, s, p);

@@ -102,6 +102,47 @@ def test_forward_resident_grid_pairs(w):
     assert_close("LSE", lse, lse_ref, w.dtype)
 
 
+# Causal grids larger than the device holds at once, whose paired grid still
+# fills it: each work-group takes blocks (nqb - 1 - j, j), the second over
+# descending key tiles. Four-wave groups at d = 128 (two per CU), d = 64
+# (four per CU) and d = 80, with dropout, and with an odd block count, a
+# ragged tail and a head count that is not a multiple of 8 (the
+# non-XCD-aware mapping).
+SWEEP_PAIR_CASES = [
+    _case(3, B=2, H=64, N=1024),
+    _case(2, B=4, H=64, N=1024),
+    _case(4, B=2, H=64, N=1024),
+    _case(5, B=1, H=128, N=1024),
+    _case(3, B=1, H=105, N=1100),
+]
+
+
+@pytest.mark.parametrize("w", SWEEP_PAIR_CASES, ids=_ids(SWEEP_PAIR_CASES))
+def test_forward_block_pairs_per_group(w):
+    inp = make_inputs(w, with_grad=False)
+    dev, val = device_inputs(inp, w.dtype)
+    o, lse = _run_fwd(dev, w)
+    o_ref, lse_ref = oracle.forward(val["q"], val["k"], val["v"], w.scale, w.causal, w.dropout_p,
+                                    w.dropout_seed)
+    assert_close("O", o, o_ref, w.dtype)
+    assert_close("LSE", lse, lse_ref, w.dtype)
+
+
+def test_eight_wave_block_pairs_heads():
+    """Eight-wave forward groups (d = 80, N = 8192) over a grid twice the
+    device's: paired blocks per group. Three whole heads, on different XCDs,
+    against the oracle."""
+    w = _case(4, B=1, H=32, N=8192)
+    inp = make_inputs(w, with_grad=False)
+    dev, val = device_inputs(inp, w.dtype)
+    o, lse = _run_fwd(dev, w)
+    heads = [(0, 0), (0, 13), (0, 31)]
+    o_ref, lse_ref = oracle.forward(val["q"], val["k"], val["v"], w.scale, w.causal, heads=heads)
+    for b, h in heads:
+        assert_close(f"O[{b},{h}]", o[b, :, h], o_ref[b, :, h], w.dtype)
+        assert_close(f"LSE[{b},{h}]", lse[b, h], lse_ref[b, h], w.dtype)
+
+
 def test_eight_wave_dropout_forward_rows():
     """Dropout runs from N = 32768 take the eight-wave forward; at N = 32800
     the last 256-row work-group holds 32 rows. Rows at the start, across a
