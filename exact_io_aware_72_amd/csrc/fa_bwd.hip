@@ -22,7 +22,6 @@
 #include "fa_device.h"
 #include "fa_hash.h"
 #include "fa_kernels.h"
-#include "fa_launch.h"
 #include "fa_tile.h"
 
 namespace fa {
@@ -48,7 +47,6 @@ struct BwdParams {
   uint32_t drop_t;
   float drop_r;
   uint64_t seed;
-  int pair_blocks;  // causal: complementary block pairs per work-group
 };
 
 BwdParams make_params(const AttnArgs& a) {
@@ -75,7 +73,6 @@ BwdParams make_params(const AttnArgs& a) {
   p.drop_t = a.drop_threshold;
   p.drop_r = a.drop_rescale;
   p.seed = a.seed;
-  p.pair_blocks = 0;  // set per launch (plan_block_pairs)
   return p;
 }
 
@@ -284,416 +281,393 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdP
   const int l32 = lane & 31, hf = lane >> 5;
   const int H = p.H;
   const int nkb = (p.N + C::BK - 1) / C::BK;
-  // Causal: key block j sees the queries from block j on, so block 0 has the
-  // most work. One block per work-group (heaviest first), or with
-  // p.pair_blocks the pair (j, nkb - 1 - j): block j over descending query
-  // tiles, then block nkb - 1 - j over ascending ones.
-  BlockMap bm;
-  int kb_first, kb_second = -1;
-  const bool paired = CAUSAL && !SPARSE && p.pair_blocks;
-  if (paired) {
-    bm = map_block_pair(blockIdx.x, (nkb + 1) / 2, p.B * H);
-    kb_first = bm.rank;
-    if (nkb - 1 - bm.rank > kb_first) kb_second = nkb - 1 - bm.rank;
-  } else {
-    bm = map_block(blockIdx.x, nkb, p.B * H);
-    kb_first = bm.rank;
-  }
+  const BlockMap bm = map_block(blockIdx.x, nkb, p.B * H);
+  const int kblk = bm.rank;  // causal: key block 0 sees the most queries
   const int b = bm.bh / H, h = bm.bh - b * H;
   const SeqRows sr = seq_rows(p.cu, p.total, b, h, H, D, p.N);
   const int N = sr.n;
-  // rev: the query tiles in descending order.
-  auto run_block = [&](const int kblk, const bool rev) {
-    const int k0 = kblk * C::BK;
-    if (k0 >= N) return;  // block past the end of a shorter sequence
-    const int kw0 = k0 + wv * 32;
-    const int mykey = kw0 + l32;
-    const int64_t rs = (int64_t)H * D;
-    const int64_t base = sr.base;
-    const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + base;
-    const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + base;
-    const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + base;
-    const uint16_t* dOg = static_cast<const uint16_t*>(p.dout) + base;
-    const uint32_t rs2 = (uint32_t)(H * D * 2);
-    const int64_t statoff = sr.stat;
-    const BufRes rl = make_bufres(p.lse + statoff, (uint32_t)N * 4);
-    const BufRes rd = make_bufres(p.dsum + statoff, (uint32_t)N * 4);
+  const int k0 = kblk * C::BK;
+  if (k0 >= N) return;  // block past the end of a shorter sequence
+  const int kw0 = k0 + wv * 32;
+  const int mykey = kw0 + l32;
+  const int64_t rs = (int64_t)H * D;
+  const int64_t base = sr.base;
+  const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + base;
+  const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + base;
+  const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + base;
+  const uint16_t* dOg = static_cast<const uint16_t*>(p.dout) + base;
+  const uint32_t rs2 = (uint32_t)(H * D * 2);
+  const int64_t statoff = sr.stat;
+  const BufRes rl = make_bufres(p.lse + statoff, (uint32_t)N * 4);
+  const BufRes rd = make_bufres(p.dsum + statoff, (uint32_t)N * 4);
 
-    // The block's V rows into LDS (rows >= N arrive as zeros).
-    {
-      const BufRes rvb = make_bufres(Vg + (int64_t)k0 * rs, (uint32_t)(N - k0) * rs2);
-  #pragma unroll
-      for (int m = 0; m < C::VLPW; ++m) {
-        const int i = wv + C::NW * m;
-        if ((QG == 1 || qg == 0) && i < VB::NLOAD) {
-          int off, row, ch;
-          VB::load_slot(i, lane, off, row, ch);
-          lds_dma_16(rvb, vblk + off, (uint32_t)row * rs2 + 16 * ch);
-        }
-      }
-    }
-    // This lane's K row (B operand of S = Q K^T); zeros past N.
-    const BufRes rk = make_bufres(Kg, (uint32_t)N * rs2);
-    u32x4 kreg[C::NKC];
-  #pragma unroll
-    for (int c = 0; c < C::NKC; ++c)
-      kreg[c] = buf_load_128(rk, (uint32_t)mykey * rs2 + (16 * c + 8 * hf) * 2);
-    // This lane's V row in LDS (B operand of dP = dO V^T).
-    const int vr = wv * 32 + l32;
-    const int vx = hf ^ VB::sw(vr);
-    int vrow[4];
-  #pragma unroll
-    for (int u = 0; u < 4; ++u) vrow[u] = vr * 128 + (((2 * u) ^ vx) << 4);
-    const int vrow_tail = VB::TAIL + vr * 32 + ((hf ^ VB::swt(vr)) << 4);
-
-    // Dropout: lanes 2c and 2c + 1 hold the two keys of one pair (mykey is
-    // kw0 + l32 with kw0 even) over the same query rows, so one hash serves
-    // both. Each lane of the two hashes two of every four rows (even lane rows
-    // 0, 1, odd lane rows 2, 3) and passes the 16-bit draws of its partner's
-    // key across; byte selectors pick the halves: own = this key's draws of the
-    // two rows, send = the partner key's.
-    uint64_t kbh = 0;
-    uint32_t bpair = 0, sel_own = 0, sel_send = 0;
-    const bool odd = (lane & 1) != 0;
-    if constexpr (DROP) {
-      kbh = head_key(p.seed, b, h, H);
-      bpair = pair_key(kbh, mykey >> 1);
-      sel_own = odd ? 0x07060302u : 0x05040100u;  // high (odd key) or low (even key) halves
-      sel_send = odd ? 0x05040100u : 0x07060302u;
-    }
-
-    const int qstart = CAUSAL ? k0 : 0;
-    int ntiles;
-    if constexpr (SPARSE) {
-      // Kept query blocks of this key block (a mask column), ascending; under
-      // the causal mask only blocks from the diagonal on.
-      const int nb = (N + kSparseBlock - 1) / kSparseBlock;
-      const uint8_t* mcol = p.bmask + b * p.msb + h * p.msh + kblk;
-      const KeptBlocks kb = collect_blocks(mcol, nb, CAUSAL ? kblk : 0, nb, kept, lane, wave == 0);
-      ntiles = kept_tiles<C::BQ>(kb, N);
-      __syncthreads();
-    } else {
-      ntiles = (N - qstart + C::BQ - 1) / C::BQ;
-    }
-    auto tile_start = [&](int t) {
-      if (rev) t = ntiles - 1 - t;
-      return SPARSE ? kept_tile_start<C::BQ>(kept, t) : qstart + t * C::BQ;
-    };
-
-    // This wave's share of the tile loads: Q instructions, then dO.
-    uint32_t dsrc[C::LPW];
-    int dlds[C::LPW];
-  #pragma unroll
-    for (int m = 0; m < C::LPW; ++m) {
+  // The block's V rows into LDS (rows >= N arrive as zeros).
+  {
+    const BufRes rvb = make_bufres(Vg + (int64_t)k0 * rs, (uint32_t)(N - k0) * rs2);
+#pragma unroll
+    for (int m = 0; m < C::VLPW; ++m) {
       const int i = wv + C::NW * m;
-      int off = 0, row = 0, ch = 0;
-      if (i < QT::NLOAD) {
-        QT::load_slot(i, lane, off, row, ch);
-      } else if (i < C::NLOAD) {
-        QT::load_slot(i - QT::NLOAD, lane, off, row, ch);
-        off += QT::BYTES;
-      }
-      dsrc[m] = (uint32_t)row * rs2 + 16 * ch;
-      dlds[m] = off;
-    }
-    // Statistics of a query tile: threads 0-31 of the group load lse, 32-63
-    // load D, 64-95 hash the row keys; stored after the tile's compute. Rows
-    // past N read zeros (their Q and dO rows are zero too, so they add nothing).
-    float sx = 0.f;
-    auto stat_load = [&](int qt0) {
-      if (gt < 32) {
-        sx = buf_load_f32(rl, (uint32_t)(qt0 + gt) * 4);
-      } else if (gt < 64) {
-        sx = buf_load_f32(rd, (uint32_t)(qt0 + gt - 32) * 4);
-      } else if (DROP && gt < 96) {
-        sx = __uint_as_float(row_key(kbh, qt0 + gt - 64));
-      }
-    };
-    auto stat_store = [&](float* ls, float* dd, uint32_t* ar) {
-      if (gt < 32) {
-        ls[gt] = DROP ? sx * kLog2e : -sx / p.scale;  // without dropout: start of the S accumulator
-      } else if (gt < 64) {
-        dd[gt - 32] = DROP ? sx : -sx;  // without dropout the dP accumulator starts at -D
-      } else if (DROP && gt < 96) {
-        ar[gt - 64] = __float_as_uint(sx);
-      }
-    };
-    auto issue = [&](char* stage, int qt0) {
-      const uint32_t left = (uint32_t)(N - qt0) * rs2;
-      const BufRes rq = make_bufres(Qg + (int64_t)qt0 * rs, left);
-      const BufRes ro = make_bufres(dOg + (int64_t)qt0 * rs, left);
-  #pragma unroll
-      for (int m = 0; m < C::LPW; ++m) {
-        const int i = wv + C::NW * m;
-        if (i < C::NLOAD) lds_dma_16(i < QT::NLOAD ? rq : ro, stage + dlds[m], dsrc[m]);
-      }
-    };
-
-    Both32<D> ofs;
-    ofs.init(lane);
-
-    f32x16 dkacc[C::NDB], dvacc[C::NDB];
-  #pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      dkacc[db] = f32x16{};
-      dvacc[db] = f32x16{};
-    }
-
-    // One query tile without dropout, in issue order: each group of
-    // instructions below is kept in place by a scheduling barrier, so the
-    // matrix products and the vector work of the same tile alternate within
-    // the wave. The S accumulator starts at -lse/scale and the dP accumulator
-    // at -D (both from the per-stage arrays), so P = exp2(S * scale log2 e)
-    // and dS = P * dP need one multiply each per element.
-    auto dkdv_tile_nodrop = [&](const char* cur, const float* lsc, const float* ddc, int qt0) {
-      constexpr int NKC = C::NKC, NT = 2 * C::NDB;
-      // Phase 1: S = Q K^T (K in registers, Q rows from LDS).
-      f32x16 s;
-  #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(lsc + 8 * g + 4 * hf);
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) s[4 * g + e] = x[e];
-      }
-  #pragma unroll
-      for (int c = 0; c < NKC; ++c) s = mfma32x32x16(ld_lds_128(cur, ofs.row_off(c)), kreg[c], s);
-      sched_lds_ahead<NKC, 1, 1, 4>();
-      __builtin_amdgcn_sched_barrier(0);
-      if (CAUSAL && qt0 < kw0 + 31) {
-        // diagonal tile: keys after the query get probability exp2(-inf) = 0
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = mykey > qt0 + c_row(r, hf) ? -INFINITY : s[r];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // dP = dO V^T (dO rows and the block's V rows from LDS), starting at -D.
-      f32x16 dp;
-  #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(ddc + 8 * g + 4 * hf);
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) dp[4 * g + e] = x[e];
-      }
-      // Phases 2-4 as one sequence of NKC + 4 NDB products (dP, then dV,
-      // then dK), each followed by the LDS reads of the product two places
-      // later and by a share of the vector work: probability e (multiply +
-      // exp2) after product (e (NKC + NDB)) / 16, dS value e after product
-      // NKC + (3 NDB e) / 16, and each pack right after its last input. The
-      // shares are spread so that no product carries more than about one and
-      // a half exponentials, and every operand is ready before the product
-      // that takes it (P^T of step kt before the dV products of step kt, dS
-      // of step kt before the dK products of step kt).
-      constexpr int NP = NKC + 4 * C::NDB;   // products after the S phase
-      constexpr int SP = NKC + C::NDB;       // slots that carry probabilities
-      constexpr int SS = 3 * C::NDB;         // slots that carry dS values
-      u32x4 xa[NKC], xb[NKC];
-      u32x4 ta[NT], tb[NT];  // transposing-read operands of the dV and dK products
-      auto ops = [&](int j) {
-        if (j < NKC) {
-          const int o = ofs.row_off(j);
-          const int vo = (2 * j < 8 * VB::NG) ? (j >> 2) * VB::GBYTES + vrow[j & 3] : vrow_tail;
-          xa[j] = ld_lds_128(cur, QT::BYTES + o);
-          xb[j] = ld_lds_128(vblk, vo);
-        } else if (j < NKC + NT) {
-          const int t = j - NKC;
-          ta[t] = ofs.tr_frag(cur + QT::BYTES, t % C::NDB, t / C::NDB);
-        } else if (j < NP) {
-          const int t = j - NKC - NT;
-          tb[t] = ofs.tr_frag(cur, t % C::NDB, t / C::NDB);
-        }
-      };
-      ops(0);
-      ops(1);
-      float pv[16], dsv[16];
-      u32x4 pop[2], sop[2];
-      auto pack8 = [&](const float* x) {
-        return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                     pack_bf16x2(x[6], x[7])};
-      };
-      __builtin_amdgcn_sched_barrier(0);
-  #pragma unroll
-      for (int j = 0; j < NP; ++j) {
-        if (j < NKC) {
-          dp = mfma32x32x16(xa[j], xb[j], dp);
-        } else if (j < NKC + NT) {
-          const int t = j - NKC;
-          dvacc[t % C::NDB] = mfma32x32x16(ta[t], pop[t / C::NDB], dvacc[t % C::NDB]);
-        } else {
-          const int t = j - NKC - NT;
-          dkacc[t % C::NDB] = mfma32x32x16(tb[t], sop[t / C::NDB], dkacc[t % C::NDB]);
-        }
-        ops(j + 2);
-  #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if ((e * SP) / 16 == j) pv[e] = exp2_hw(s[e] * p.c2);
-  #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          if (((8 * kt + 7) * SP) / 16 == j) pop[kt] = pack8(pv + 8 * kt);
-  #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (NKC + (e * SS) / 16 == j) dsv[e] = pv[e] * dp[e];
-  #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          if (NKC + ((8 * kt + 7) * SS) / 16 == j) sop[kt] = pack8(dsv + 8 * kt);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-
-    // Step of this group over kept query tile t (t >= ntiles: the group has
-    // no tile in this step and only takes part in the barrier).
-    auto step = [&](const char* cur, const float* lsc, const float* ddc, const uint32_t* arc,
-                    char* nxt, float* lsn, float* ddn, uint32_t* arn, int t) {
-      wait_vmem();
-      __syncthreads();
-      if constexpr (kLdsPoison) poison_stage(nxt, C::STAGE, gt, C::NT);
-      const bool valid = QG == 1 || t < ntiles;  // one group: every step has a tile
-      const int qt0 = valid ? tile_start(t) : 0;
-      const bool more = t + QG < ntiles;
-      if (more) {
-        const int qn = tile_start(t + QG);
-        stat_load(qn);
-        issue(nxt, qn);
-      }
-      if (valid && (!CAUSAL || qt0 + C::BQ - 1 >= kw0)) {
-        if constexpr (!DROP) {
-          dkdv_tile_nodrop(cur, lsc, ddc, qt0);
-        } else {
-        // S = Q K^T and dP = dO V^T : lane = key, register r -> query qt0 + c_row(r, hf)
-        f32x16 s = f32x16{}, dp = f32x16{};
-  #pragma unroll
-        for (int c = 0; c < C::NKC; ++c) {
-          const int o = ofs.row_off(c);
-          const int vo = (2 * c < 8 * VB::NG) ? (c >> 2) * VB::GBYTES + vrow[c & 3] : vrow_tail;
-          s = mfma32x32x16(ld_lds_128(cur, o), kreg[c], s);
-          dp = mfma32x32x16(ld_lds_128(cur, QT::BYTES + o), ld_lds_128(vblk, vo), dp);
-        }
-        // Issue order: the three LDS reads of step c + 2 go out before the two
-        // products of step c, so read latency overlaps the matrix cores.
-        sched_lds_ahead<C::NKC, 3, 2>();
-        if (CAUSAL && qt0 < kw0 + 31) {
-          // diagonal tile: keys after the query get probability exp2(-inf) = 0
-  #pragma unroll
-          for (int r = 0; r < 16; ++r) s[r] = mykey > qt0 + c_row(r, hf) ? -INFINITY : s[r];
-        }
-  #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          float pt[8], dsv[8];
-  #pragma unroll
-          for (int gg = 0; gg < 2; ++gg) {
-            const int g = 2 * kt + gg;
-            const f32x4 l2 = *reinterpret_cast<const f32x4*>(lsc + 8 * g + 4 * hf);
-            const f32x4 dd = *reinterpret_cast<const f32x4*>(ddc + 8 * g + 4 * hf);
-            // Dropout draws of rows 8g + 4hf + e: e = 0, 1 in dr01, e = 2, 3 in
-            // dr23 (low half, high half).
-            uint32_t dr01 = 0, dr23 = 0;
-            if constexpr (DROP) {
-              const u32x2 ar = *reinterpret_cast<const u32x2*>(arc + 8 * g + 4 * hf + (odd ? 2 : 0));
-              uint32_t fa = pair_mix(ar[0], bpair), fb = pair_mix(ar[1], bpair);
-              fa ^= fa >> 16;  // fmix32: low half the even key's draw, high half the odd key's
-              fb ^= fb >> 16;
-              const uint32_t own = __builtin_amdgcn_perm(fb, fa, sel_own);
-              const uint32_t send = __builtin_amdgcn_perm(fb, fa, sel_send);
-              const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
-              dr01 = odd ? recv : own;
-              dr23 = odd ? own : recv;
-            }
-  #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * g + e;
-              const float pv = exp2_hw(fmaf(s[r], p.c2, -l2[e]));
-              float dpv = dp[r];
-              float ptv = pv;
-              if constexpr (DROP) {
-                const uint32_t dw = e < 2 ? dr01 : dr23;
-                const bool kp = (e & 1) ? dw >= (p.drop_t << 16) : (dw & 0xFFFFu) >= p.drop_t;
-                const float mr = kp ? p.drop_r : 0.f;
-                ptv = pv * mr;
-                dpv *= mr;
-              }
-              pt[4 * gg + e] = ptv;
-              dsv[4 * gg + e] = pv * (dpv - dd[e]);
-            }
-          }
-          const u32x4 pop = {pack_bf16x2(pt[0], pt[1]), pack_bf16x2(pt[2], pt[3]),
-                             pack_bf16x2(pt[4], pt[5]), pack_bf16x2(pt[6], pt[7])};
-          const u32x4 sop = {pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3]),
-                             pack_bf16x2(dsv[4], dsv[5]), pack_bf16x2(dsv[6], dsv[7])};
-          // dV^T += dO^T P~ and dK^T += Q^T dS over the 16 queries of step kt.
-  #pragma unroll
-          for (int db = 0; db < C::NDB; ++db) {
-            dvacc[db] = mfma32x32x16(ofs.tr_frag(cur + QT::BYTES, db, kt), pop, dvacc[db]);
-            dkacc[db] = mfma32x32x16(ofs.tr_frag(cur, db, kt), sop, dkacc[db]);
-          }
-        }
-        // Statistics reads first, then the four transposing reads of step i + 1
-        // ahead of the two products of step i.
-        sched_lds_ahead<2 * C::NDB, 4, 2, DROP ? 12 : 8, 1>();
-        }
-      }
-      if (more) stat_store(lsn, ddn, arn);
-    };
-
-    const int nsteps = (ntiles + QG - 1) / QG;  // the same count for every group
-    if constexpr (kLdsPoison) poison_stage(st0[qg], C::STAGE, gt, C::NT);
-    if (qg < ntiles) {
-      stat_load(tile_start(qg));
-      issue(st0[qg], tile_start(qg));
-      stat_store(ls0[qg], dd0[qg], ar0[qg]);
-    }
-    for (int s = 0; s < nsteps; s += 2) {
-      step(st0[qg], ls0[qg], dd0[qg], ar0[qg], st1[qg], ls1[qg], dd1[qg], ar1[qg], qg + QG * s);
-      if (s + 1 < nsteps)
-        step(st1[qg], ls1[qg], dd1[qg], ar1[qg], st0[qg], ls0[qg], dd0[qg], ar0[qg], qg + QG * (s + 1));
-    }
-
-    if constexpr (QG == 2) {
-      // Group 1's sums into group 0's, one accumulator block at a time through
-      // st0 (free once every wave has passed the barrier): slot (wave, r, lane).
-      float* red = reinterpret_cast<float*>(&st0[0][0]);
-  #pragma unroll
-      for (int tsel = 0; tsel < 2; ++tsel) {
-  #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          f32x16& acc = tsel ? dvacc[db] : dkacc[db];
-          __syncthreads();
-          if (qg == 1) {
-  #pragma unroll
-            for (int r = 0; r < 16; ++r) red[(wv * 16 + r) * 64 + lane] = acc[r];
-          }
-          __syncthreads();
-          if (qg == 0) {
-  #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] += red[(wv * 16 + r) * 64 + lane];
-          }
-        }
+      if ((QG == 1 || qg == 0) && i < VB::NLOAD) {
+        int off, row, ch;
+        VB::load_slot(i, lane, off, row, ch);
+        lds_dma_16(rvb, vblk + off, (uint32_t)row * rs2 + 16 * ch);
       }
     }
+  }
+  // This lane's K row (B operand of S = Q K^T); zeros past N.
+  const BufRes rk = make_bufres(Kg, (uint32_t)N * rs2);
+  u32x4 kreg[C::NKC];
+#pragma unroll
+  for (int c = 0; c < C::NKC; ++c)
+    kreg[c] = buf_load_128(rk, (uint32_t)mykey * rs2 + (16 * c + 8 * hf) * 2);
+  // This lane's V row in LDS (B operand of dP = dO V^T).
+  const int vr = wv * 32 + l32;
+  const int vx = hf ^ VB::sw(vr);
+  int vrow[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) vrow[u] = vr * 128 + (((2 * u) ^ vx) << 4);
+  const int vrow_tail = VB::TAIL + vr * 32 + ((hf ^ VB::swt(vr)) << 4);
 
-    if ((QG == 1 || qg == 0) && mykey < N) {
-      uint16_t* dkrow = static_cast<uint16_t*>(p.dk) + base + (int64_t)mykey * rs;
-      uint16_t* dvrow = static_cast<uint16_t*>(p.dv) + base + (int64_t)mykey * rs;
-      const float sc = p.scale;
-  #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-  #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = db * 32 + 8 * g + 4 * hf;
-          if (d0 < D) {
-            const u32x2 wk = {pack_bf16x2(dkacc[db][4 * g] * sc, dkacc[db][4 * g + 1] * sc),
-                              pack_bf16x2(dkacc[db][4 * g + 2] * sc, dkacc[db][4 * g + 3] * sc)};
-            const u32x2 wv = {pack_bf16x2(dvacc[db][4 * g], dvacc[db][4 * g + 1]),
-                              pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3])};
-            st_global_64(dkrow + d0, wk);
-            st_global_64(dvrow + d0, wv);
-          }
-        }
-      }
+  // Dropout: lanes 2c and 2c + 1 hold the two keys of one pair (mykey is
+  // kw0 + l32 with kw0 even) over the same query rows, so one hash serves
+  // both. Each lane of the two hashes two of every four rows (even lane rows
+  // 0, 1, odd lane rows 2, 3) and passes the 16-bit draws of its partner's
+  // key across; byte selectors pick the halves: own = this key's draws of the
+  // two rows, send = the partner key's.
+  uint64_t kbh = 0;
+  uint32_t bpair = 0, sel_own = 0, sel_send = 0;
+  const bool odd = (lane & 1) != 0;
+  if constexpr (DROP) {
+    kbh = head_key(p.seed, b, h, H);
+    bpair = pair_key(kbh, mykey >> 1);
+    sel_own = odd ? 0x07060302u : 0x05040100u;  // high (odd key) or low (even key) halves
+    sel_send = odd ? 0x05040100u : 0x07060302u;
+  }
+
+  const int qstart = CAUSAL ? k0 : 0;
+  int ntiles;
+  if constexpr (SPARSE) {
+    // Kept query blocks of this key block (a mask column), ascending; under
+    // the causal mask only blocks from the diagonal on.
+    const int nb = (N + kSparseBlock - 1) / kSparseBlock;
+    const uint8_t* mcol = p.bmask + b * p.msb + h * p.msh + kblk;
+    const KeptBlocks kb = collect_blocks(mcol, nb, CAUSAL ? kblk : 0, nb, kept, lane, wave == 0);
+    ntiles = kept_tiles<C::BQ>(kb, N);
+    __syncthreads();
+  } else {
+    ntiles = (N - qstart + C::BQ - 1) / C::BQ;
+  }
+  auto tile_start = [&](int t) {
+    return SPARSE ? kept_tile_start<C::BQ>(kept, t) : qstart + t * C::BQ;
+  };
+
+  // This wave's share of the tile loads: Q instructions, then dO.
+  uint32_t dsrc[C::LPW];
+  int dlds[C::LPW];
+#pragma unroll
+  for (int m = 0; m < C::LPW; ++m) {
+    const int i = wv + C::NW * m;
+    int off = 0, row = 0, ch = 0;
+    if (i < QT::NLOAD) {
+      QT::load_slot(i, lane, off, row, ch);
+    } else if (i < C::NLOAD) {
+      QT::load_slot(i - QT::NLOAD, lane, off, row, ch);
+      off += QT::BYTES;
+    }
+    dsrc[m] = (uint32_t)row * rs2 + 16 * ch;
+    dlds[m] = off;
+  }
+  // Statistics of a query tile: threads 0-31 of the group load lse, 32-63
+  // load D, 64-95 hash the row keys; stored after the tile's compute. Rows
+  // past N read zeros (their Q and dO rows are zero too, so they add nothing).
+  float sx = 0.f;
+  auto stat_load = [&](int qt0) {
+    if (gt < 32) {
+      sx = buf_load_f32(rl, (uint32_t)(qt0 + gt) * 4);
+    } else if (gt < 64) {
+      sx = buf_load_f32(rd, (uint32_t)(qt0 + gt - 32) * 4);
+    } else if (DROP && gt < 96) {
+      sx = __uint_as_float(row_key(kbh, qt0 + gt - 64));
     }
   };
-  run_block(kb_first, paired);
-  if (kb_second >= 0) {
-    // The first block's last tile and its V rows may still be read from LDS.
+  auto stat_store = [&](float* ls, float* dd, uint32_t* ar) {
+    if (gt < 32) {
+      ls[gt] = DROP ? sx * kLog2e : -sx / p.scale;  // without dropout: start of the S accumulator
+    } else if (gt < 64) {
+      dd[gt - 32] = DROP ? sx : -sx;  // without dropout the dP accumulator starts at -D
+    } else if (DROP && gt < 96) {
+      ar[gt - 64] = __float_as_uint(sx);
+    }
+  };
+  auto issue = [&](char* stage, int qt0) {
+    const uint32_t left = (uint32_t)(N - qt0) * rs2;
+    const BufRes rq = make_bufres(Qg + (int64_t)qt0 * rs, left);
+    const BufRes ro = make_bufres(dOg + (int64_t)qt0 * rs, left);
+#pragma unroll
+    for (int m = 0; m < C::LPW; ++m) {
+      const int i = wv + C::NW * m;
+      if (i < C::NLOAD) lds_dma_16(i < QT::NLOAD ? rq : ro, stage + dlds[m], dsrc[m]);
+    }
+  };
+
+  Both32<D> ofs;
+  ofs.init(lane);
+
+  f32x16 dkacc[C::NDB], dvacc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
+  }
+
+  // One query tile without dropout, in issue order: each group of
+  // instructions below is kept in place by a scheduling barrier, so the
+  // matrix products and the vector work of the same tile alternate within
+  // the wave. The S accumulator starts at -lse/scale and the dP accumulator
+  // at -D (both from the per-stage arrays), so P = exp2(S * scale log2 e)
+  // and dS = P * dP need one multiply each per element.
+  auto dkdv_tile_nodrop = [&](const char* cur, const float* lsc, const float* ddc, int qt0) {
+    constexpr int NKC = C::NKC, NT = 2 * C::NDB;
+    // Phase 1: S = Q K^T (K in registers, Q rows from LDS).
+    f32x16 s;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(lsc + 8 * g + 4 * hf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[4 * g + e] = x[e];
+    }
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) s = mfma32x32x16(ld_lds_128(cur, ofs.row_off(c)), kreg[c], s);
+    sched_lds_ahead<NKC, 1, 1, 4>();
+    __builtin_amdgcn_sched_barrier(0);
+    if (CAUSAL && qt0 < kw0 + 31) {
+      // diagonal tile: keys after the query get probability exp2(-inf) = 0
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = mykey > qt0 + c_row(r, hf) ? -INFINITY : s[r];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // dP = dO V^T (dO rows and the block's V rows from LDS), starting at -D.
+    f32x16 dp;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(ddc + 8 * g + 4 * hf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[4 * g + e] = x[e];
+    }
+    // Phases 2-4 as one sequence of NKC + 4 NDB products (dP, then dV,
+    // then dK), each followed by the LDS reads of the product two places
+    // later and by a share of the vector work: probability e (multiply +
+    // exp2) after product (e (NKC + NDB)) / 16, dS value e after product
+    // NKC + (3 NDB e) / 16, and each pack right after its last input. The
+    // shares are spread so that no product carries more than about one and
+    // a half exponentials, and every operand is ready before the product
+    // that takes it (P^T of step kt before the dV products of step kt, dS
+    // of step kt before the dK products of step kt).
+    constexpr int NP = NKC + 4 * C::NDB;   // products after the S phase
+    constexpr int SP = NKC + C::NDB;       // slots that carry probabilities
+    constexpr int SS = 3 * C::NDB;         // slots that carry dS values
+    u32x4 xa[NKC], xb[NKC];
+    u32x4 ta[NT], tb[NT];  // transposing-read operands of the dV and dK products
+    auto ops = [&](int j) {
+      if (j < NKC) {
+        const int o = ofs.row_off(j);
+        const int vo = (2 * j < 8 * VB::NG) ? (j >> 2) * VB::GBYTES + vrow[j & 3] : vrow_tail;
+        xa[j] = ld_lds_128(cur, QT::BYTES + o);
+        xb[j] = ld_lds_128(vblk, vo);
+      } else if (j < NKC + NT) {
+        const int t = j - NKC;
+        ta[t] = ofs.tr_frag(cur + QT::BYTES, t % C::NDB, t / C::NDB);
+      } else if (j < NP) {
+        const int t = j - NKC - NT;
+        tb[t] = ofs.tr_frag(cur, t % C::NDB, t / C::NDB);
+      }
+    };
+    ops(0);
+    ops(1);
+    float pv[16], dsv[16];
+    u32x4 pop[2], sop[2];
+    auto pack8 = [&](const float* x) {
+      return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                   pack_bf16x2(x[6], x[7])};
+    };
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      if (j < NKC) {
+        dp = mfma32x32x16(xa[j], xb[j], dp);
+      } else if (j < NKC + NT) {
+        const int t = j - NKC;
+        dvacc[t % C::NDB] = mfma32x32x16(ta[t], pop[t / C::NDB], dvacc[t % C::NDB]);
+      } else {
+        const int t = j - NKC - NT;
+        dkacc[t % C::NDB] = mfma32x32x16(tb[t], sop[t / C::NDB], dkacc[t % C::NDB]);
+      }
+      ops(j + 2);
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if ((e * SP) / 16 == j) pv[e] = exp2_hw(s[e] * p.c2);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        if (((8 * kt + 7) * SP) / 16 == j) pop[kt] = pack8(pv + 8 * kt);
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (NKC + (e * SS) / 16 == j) dsv[e] = pv[e] * dp[e];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        if (NKC + ((8 * kt + 7) * SS) / 16 == j) sop[kt] = pack8(dsv + 8 * kt);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Step of this group over kept query tile t (t >= ntiles: the group has
+  // no tile in this step and only takes part in the barrier).
+  auto step = [&](const char* cur, const float* lsc, const float* ddc, const uint32_t* arc,
+                  char* nxt, float* lsn, float* ddn, uint32_t* arn, int t) {
+    wait_vmem();
     __syncthreads();
-    run_block(kb_second, false);
+    if constexpr (kLdsPoison) poison_stage(nxt, C::STAGE, gt, C::NT);
+    const bool valid = QG == 1 || t < ntiles;  // one group: every step has a tile
+    const int qt0 = valid ? tile_start(t) : 0;
+    const bool more = t + QG < ntiles;
+    if (more) {
+      const int qn = tile_start(t + QG);
+      stat_load(qn);
+      issue(nxt, qn);
+    }
+    if (valid && (!CAUSAL || qt0 + C::BQ - 1 >= kw0)) {
+      if constexpr (!DROP) {
+        dkdv_tile_nodrop(cur, lsc, ddc, qt0);
+      } else {
+      // S = Q K^T and dP = dO V^T : lane = key, register r -> query qt0 + c_row(r, hf)
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int c = 0; c < C::NKC; ++c) {
+        const int o = ofs.row_off(c);
+        const int vo = (2 * c < 8 * VB::NG) ? (c >> 2) * VB::GBYTES + vrow[c & 3] : vrow_tail;
+        s = mfma32x32x16(ld_lds_128(cur, o), kreg[c], s);
+        dp = mfma32x32x16(ld_lds_128(cur, QT::BYTES + o), ld_lds_128(vblk, vo), dp);
+      }
+      // Issue order: the three LDS reads of step c + 2 go out before the two
+      // products of step c, so read latency overlaps the matrix cores.
+      sched_lds_ahead<C::NKC, 3, 2>();
+      if (CAUSAL && qt0 < kw0 + 31) {
+        // diagonal tile: keys after the query get probability exp2(-inf) = 0
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = mykey > qt0 + c_row(r, hf) ? -INFINITY : s[r];
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        float pt[8], dsv[8];
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const int g = 2 * kt + gg;
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(lsc + 8 * g + 4 * hf);
+          const f32x4 dd = *reinterpret_cast<const f32x4*>(ddc + 8 * g + 4 * hf);
+          // Dropout draws of rows 8g + 4hf + e: e = 0, 1 in dr01, e = 2, 3 in
+          // dr23 (low half, high half).
+          uint32_t dr01 = 0, dr23 = 0;
+          if constexpr (DROP) {
+            const u32x2 ar = *reinterpret_cast<const u32x2*>(arc + 8 * g + 4 * hf + (odd ? 2 : 0));
+            uint32_t fa = pair_mix(ar[0], bpair), fb = pair_mix(ar[1], bpair);
+            fa ^= fa >> 16;  // fmix32: low half the even key's draw, high half the odd key's
+            fb ^= fb >> 16;
+            const uint32_t own = __builtin_amdgcn_perm(fb, fa, sel_own);
+            const uint32_t send = __builtin_amdgcn_perm(fb, fa, sel_send);
+            const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+            dr01 = odd ? recv : own;
+            dr23 = odd ? own : recv;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            const float pv = exp2_hw(fmaf(s[r], p.c2, -l2[e]));
+            float dpv = dp[r];
+            float ptv = pv;
+            if constexpr (DROP) {
+              const uint32_t dw = e < 2 ? dr01 : dr23;
+              const bool kp = (e & 1) ? dw >= (p.drop_t << 16) : (dw & 0xFFFFu) >= p.drop_t;
+              const float mr = kp ? p.drop_r : 0.f;
+              ptv = pv * mr;
+              dpv *= mr;
+            }
+            pt[4 * gg + e] = ptv;
+            dsv[4 * gg + e] = pv * (dpv - dd[e]);
+          }
+        }
+        const u32x4 pop = {pack_bf16x2(pt[0], pt[1]), pack_bf16x2(pt[2], pt[3]),
+                           pack_bf16x2(pt[4], pt[5]), pack_bf16x2(pt[6], pt[7])};
+        const u32x4 sop = {pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3]),
+                           pack_bf16x2(dsv[4], dsv[5]), pack_bf16x2(dsv[6], dsv[7])};
+        // dV^T += dO^T P~ and dK^T += Q^T dS over the 16 queries of step kt.
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          dvacc[db] = mfma32x32x16(ofs.tr_frag(cur + QT::BYTES, db, kt), pop, dvacc[db]);
+          dkacc[db] = mfma32x32x16(ofs.tr_frag(cur, db, kt), sop, dkacc[db]);
+        }
+      }
+      // Statistics reads first, then the four transposing reads of step i + 1
+      // ahead of the two products of step i.
+      sched_lds_ahead<2 * C::NDB, 4, 2, DROP ? 12 : 8, 1>();
+      }
+    }
+    if (more) stat_store(lsn, ddn, arn);
+  };
+
+  const int nsteps = (ntiles + QG - 1) / QG;  // the same count for every group
+  if constexpr (kLdsPoison) poison_stage(st0[qg], C::STAGE, gt, C::NT);
+  if (qg < ntiles) {
+    stat_load(tile_start(qg));
+    issue(st0[qg], tile_start(qg));
+    stat_store(ls0[qg], dd0[qg], ar0[qg]);
+  }
+  for (int s = 0; s < nsteps; s += 2) {
+    step(st0[qg], ls0[qg], dd0[qg], ar0[qg], st1[qg], ls1[qg], dd1[qg], ar1[qg], qg + QG * s);
+    if (s + 1 < nsteps)
+      step(st1[qg], ls1[qg], dd1[qg], ar1[qg], st0[qg], ls0[qg], dd0[qg], ar0[qg], qg + QG * (s + 1));
+  }
+
+  if constexpr (QG == 2) {
+    // Group 1's sums into group 0's, one accumulator block at a time through
+    // st0 (free once every wave has passed the barrier): slot (wave, r, lane).
+    float* red = reinterpret_cast<float*>(&st0[0][0]);
+#pragma unroll
+    for (int tsel = 0; tsel < 2; ++tsel) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        f32x16& acc = tsel ? dvacc[db] : dkacc[db];
+        __syncthreads();
+        if (qg == 1) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[(wv * 16 + r) * 64 + lane] = acc[r];
+        }
+        __syncthreads();
+        if (qg == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] += red[(wv * 16 + r) * 64 + lane];
+        }
+      }
+    }
+  }
+
+  if ((QG == 1 || qg == 0) && mykey < N) {
+    uint16_t* dkrow = static_cast<uint16_t*>(p.dk) + base + (int64_t)mykey * rs;
+    uint16_t* dvrow = static_cast<uint16_t*>(p.dv) + base + (int64_t)mykey * rs;
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * hf;
+        if (d0 < D) {
+          const u32x2 wk = {pack_bf16x2(dkacc[db][4 * g] * sc, dkacc[db][4 * g + 1] * sc),
+                            pack_bf16x2(dkacc[db][4 * g + 2] * sc, dkacc[db][4 * g + 3] * sc)};
+          const u32x2 wv = {pack_bf16x2(dvacc[db][4 * g], dvacc[db][4 * g + 1]),
+                            pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3])};
+          st_global_64(dkrow + d0, wk);
+          st_global_64(dvrow + d0, wv);
+        }
+      }
+    }
   }
 }
 
@@ -741,217 +715,193 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdParams p) {
   const int l32 = lane & 31, hf = lane >> 5;
   const int H = p.H;
   const int nqb = (p.N + C::BQ - 1) / C::BQ;
-  // Causal: query block i sees the keys up to block i. One block per
-  // work-group (heaviest first), or with p.pair_blocks the pair
-  // (nqb - 1 - j, j): the first over ascending key tiles, the second over
-  // descending ones.
-  BlockMap bm;
-  int qb_first, qb_second = -1;
-  if (CAUSAL && !SPARSE && p.pair_blocks) {
-    bm = map_block_pair(blockIdx.x, (nqb + 1) / 2, p.B * H);
-    qb_first = nqb - 1 - bm.rank;
-    if (bm.rank < qb_first) qb_second = bm.rank;
-  } else {
-    bm = map_block(blockIdx.x, nqb, p.B * H);
-    qb_first = CAUSAL ? (nqb - 1 - bm.rank) : bm.rank;
-  }
+  const BlockMap bm = map_block(blockIdx.x, nqb, p.B * H);
+  const int qb = CAUSAL ? (nqb - 1 - bm.rank) : bm.rank;
   const int b = bm.bh / H, h = bm.bh - b * H;
   const SeqRows sr = seq_rows(p.cu, p.total, b, h, H, D, p.N);
   const int N = sr.n;
-  // rev: the key tiles in descending order.
-  auto run_block = [&](const int qb, const bool rev) {
-    const int q0 = qb * C::BQ;
-    if (q0 >= N) return;  // block past the end of a shorter sequence
-    const int qw0 = q0 + wave * 32;
-    const int myq = qw0 + l32;
-    const int64_t rs = (int64_t)H * D;
-    const int64_t base = sr.base;
-    const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + base;
-    const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + base;
-    const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + base;
-    const uint16_t* dOg = static_cast<const uint16_t*>(p.dout) + base;
-    const uint32_t rs2 = (uint32_t)(H * D * 2);
-    const uint32_t nbytes = (uint32_t)N * rs2;
-    const BufRes rq = make_bufres(Qg, nbytes), rdo = make_bufres(dOg, nbytes);
-    const int64_t statoff = sr.stat;
-    const BufRes rl = make_bufres(p.lse + statoff, (uint32_t)N * 4);
-    const BufRes rd = make_bufres(p.dsum + statoff, (uint32_t)N * 4);
+  const int q0 = qb * C::BQ;
+  if (q0 >= N) return;  // block past the end of a shorter sequence
+  const int qw0 = q0 + wave * 32;
+  const int myq = qw0 + l32;
+  const int64_t rs = (int64_t)H * D;
+  const int64_t base = sr.base;
+  const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + base;
+  const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + base;
+  const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + base;
+  const uint16_t* dOg = static_cast<const uint16_t*>(p.dout) + base;
+  const uint32_t rs2 = (uint32_t)(H * D * 2);
+  const uint32_t nbytes = (uint32_t)N * rs2;
+  const BufRes rq = make_bufres(Qg, nbytes), rdo = make_bufres(dOg, nbytes);
+  const int64_t statoff = sr.stat;
+  const BufRes rl = make_bufres(p.lse + statoff, (uint32_t)N * 4);
+  const BufRes rd = make_bufres(p.dsum + statoff, (uint32_t)N * 4);
 
-    // Rows past N: zero Q, dO, LSE and D give dS = 0 (never stored anyway).
-    u32x4 qreg[C::NKC], doreg[C::NKC];
-  #pragma unroll
-    for (int c = 0; c < C::NKC; ++c) {
-      const uint32_t off = (uint32_t)myq * rs2 + (16 * c + 8 * hf) * 2;
-      qreg[c] = buf_load_128(rq, off);
-      doreg[c] = buf_load_128(rdo, off);
-    }
-    const float lse2 = buf_load_f32(rl, (uint32_t)myq * 4) * kLog2e;
-    const float dq_d = buf_load_f32(rd, (uint32_t)myq * 4);
-    uint64_t kbh = 0;
-    uint32_t arow = 0;
-    if constexpr (DROP) {
-      kbh = head_key(p.seed, b, h, H);
-      arow = row_key(kbh, myq);
-    }
+  // Rows past N: zero Q, dO, LSE and D give dS = 0 (never stored anyway).
+  u32x4 qreg[C::NKC], doreg[C::NKC];
+#pragma unroll
+  for (int c = 0; c < C::NKC; ++c) {
+    const uint32_t off = (uint32_t)myq * rs2 + (16 * c + 8 * hf) * 2;
+    qreg[c] = buf_load_128(rq, off);
+    doreg[c] = buf_load_128(rdo, off);
+  }
+  const float lse2 = buf_load_f32(rl, (uint32_t)myq * 4) * kLog2e;
+  const float dq_d = buf_load_f32(rd, (uint32_t)myq * 4);
+  uint64_t kbh = 0;
+  uint32_t arow = 0;
+  if constexpr (DROP) {
+    kbh = head_key(p.seed, b, h, H);
+    arow = row_key(kbh, myq);
+  }
 
-    const int kend = CAUSAL ? min(N, q0 + C::BQ) : N;
-    int ntiles;
-    if constexpr (SPARSE) {
-      const int nb = (N + kSparseBlock - 1) / kSparseBlock;
-      const uint8_t* mrow = p.bmask + b * p.msb + h * p.msh + (int64_t)qb * nb;
-      const KeptBlocks kb =
-          collect_blocks(mrow, 1, 0, (kend + kSparseBlock - 1) / kSparseBlock, kept, lane, wave == 0);
-      ntiles = kept_tiles<C::BK>(kb, kend);
-      __syncthreads();
-    } else {
-      ntiles = (kend + C::BK - 1) / C::BK;
-    }
-    auto tile_start = [&](int t) {
-      if (rev) t = ntiles - 1 - t;
-      return SPARSE ? kept_tile_start<C::BK>(kept, t) : t * C::BK;
-    };
+  const int kend = CAUSAL ? min(N, q0 + C::BQ) : N;
+  int ntiles;
+  if constexpr (SPARSE) {
+    const int nb = (N + kSparseBlock - 1) / kSparseBlock;
+    const uint8_t* mrow = p.bmask + b * p.msb + h * p.msh + (int64_t)qb * nb;
+    const KeptBlocks kb =
+        collect_blocks(mrow, 1, 0, (kend + kSparseBlock - 1) / kSparseBlock, kept, lane, wave == 0);
+    ntiles = kept_tiles<C::BK>(kb, kend);
+    __syncthreads();
+  } else {
+    ntiles = (kend + C::BK - 1) / C::BK;
+  }
+  auto tile_start = [&](int t) { return SPARSE ? kept_tile_start<C::BK>(kept, t) : t * C::BK; };
 
-    // This wave's share of the tile loads: K instructions, then V.
-    uint32_t dsrc[C::LPW];
-    int dlds[C::LPW];
-  #pragma unroll
+  // This wave's share of the tile loads: K instructions, then V.
+  uint32_t dsrc[C::LPW];
+  int dlds[C::LPW];
+#pragma unroll
+  for (int m = 0; m < C::LPW; ++m) {
+    const int i = wave + NW * m;
+    int off = 0, row = 0, ch = 0;
+    if (i < KT::NLOAD) {
+      KT::load_slot(i, lane, off, row, ch);
+    } else if (i < C::NLOAD) {
+      VT::load_slot(i - KT::NLOAD, lane, off, row, ch);
+      off += KT::BYTES;
+    }
+    dsrc[m] = (uint32_t)row * rs2 + 16 * ch;
+    dlds[m] = off;
+  }
+  auto issue = [&](char* stage, uint32_t* bc, int k0) {
+    const uint32_t left = (uint32_t)(N - k0) * rs2;
+    const BufRes rk = make_bufres(Kg + (int64_t)k0 * rs, left);
+    const BufRes rv = make_bufres(Vg + (int64_t)k0 * rs, left);
+#pragma unroll
     for (int m = 0; m < C::LPW; ++m) {
       const int i = wave + NW * m;
-      int off = 0, row = 0, ch = 0;
-      if (i < KT::NLOAD) {
-        KT::load_slot(i, lane, off, row, ch);
-      } else if (i < C::NLOAD) {
-        VT::load_slot(i - KT::NLOAD, lane, off, row, ch);
-        off += KT::BYTES;
-      }
-      dsrc[m] = (uint32_t)row * rs2 + 16 * ch;
-      dlds[m] = off;
+      if (i < C::NLOAD) lds_dma_16(i < KT::NLOAD ? rk : rv, stage + dlds[m], dsrc[m]);
     }
-    auto issue = [&](char* stage, uint32_t* bc, int k0) {
-      const uint32_t left = (uint32_t)(N - k0) * rs2;
-      const BufRes rk = make_bufres(Kg + (int64_t)k0 * rs, left);
-      const BufRes rv = make_bufres(Vg + (int64_t)k0 * rs, left);
-  #pragma unroll
-      for (int m = 0; m < C::LPW; ++m) {
-        const int i = wave + NW * m;
-        if (i < C::NLOAD) lds_dma_16(i < KT::NLOAD ? rk : rv, stage + dlds[m], dsrc[m]);
-      }
-      if constexpr (DROP) {
-        if (tid < C::BK / 2) bc[tid] = pair_key(kbh, (k0 >> 1) + tid);
-      }
-    };
-
-    Both32<D> ofs;
-    ofs.init(lane);
-    const int vx = hf ^ VT::sw(l32);
-    int vrow[4];
-  #pragma unroll
-    for (int u = 0; u < 4; ++u) vrow[u] = KT::BYTES + l32 * 128 + (((2 * u) ^ vx) << 4);
-    const int vrow_tail = KT::BYTES + VT::TAIL + l32 * 32 + ((hf ^ VT::swt(l32)) << 4);
-
-    f32x16 dqacc[C::NDB];
-  #pragma unroll
-    for (int db = 0; db < C::NDB; ++db) dqacc[db] = f32x16{};
-    f32x16 negd;  // -D of this lane's query: start of the dP^T accumulator (no dropout)
-  #pragma unroll
-    for (int r = 0; r < 16; ++r) negd[r] = -dq_d;
-
-    auto step = [&](const char* cur, const uint32_t* bcc, char* nxt, uint32_t* bcn, int t) {
-      wait_vmem();
-      __syncthreads();
-      if constexpr (kLdsPoison) poison_stage(nxt, C::STAGE, tid, C::NT);
-      const int k0 = tile_start(t);
-      if (t + 1 < ntiles) issue(nxt, bcn, tile_start(t + 1));
-      if (CAUSAL && k0 > qw0 + 31) return;
-      // Phase 1. S^T = K Q^T : lane = query, register r -> key k0 + c_row(r, hf).
-      f32x16 s = f32x16{};
-  #pragma unroll
-      for (int c = 0; c < C::NKC; ++c) s = mfma32x32x16(ld_lds_128(cur, ofs.row_off(c)), qreg[c], s);
-      sched_lds_ahead<C::NKC, 1, 1>();
-      __builtin_amdgcn_sched_barrier(0);  // the later phases are ordered on their own
-      if ((k0 + C::BK > N) || (CAUSAL && k0 + C::BK - 1 > qw0)) {
-        // tail or diagonal tile: keys past N or after the query get exp2(-inf) = 0
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + c_row(r, hf);
-          s[r] = (key >= N || (CAUSAL && key > myq)) ? -INFINITY : s[r];
-        }
-      }
-      // Phase 2. dP^T = V dO^T on the matrix cores while the vector ALUs form
-      // P^T; without dropout the accumulator starts at -D of this lane's query.
-      f32x16 dp = DROP ? f32x16{} : negd;
-  #pragma unroll
-      for (int c = 0; c < C::NKC; ++c) {
-        const int vo = (2 * c < 8 * VT::NG) ? (c >> 2) * VT::GBYTES + vrow[c & 3] : vrow_tail;
-        dp = mfma32x32x16(ld_lds_128(cur, vo), doreg[c], dp);
-      }
-      float pv[16];
-      // Registers 4g + e hold keys 8g + 4hf + e; keys (e, e + 1), e = 0, 2, are
-      // a pair and share one dropout hash.
-      uint32_t yd[DROP ? 4 : 1][2];
-  #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if constexpr (DROP) {
-          const u32x2 bc = *reinterpret_cast<const u32x2*>(bcc + 4 * g + 2 * hf);
-          yd[g][0] = pair_mix(arow, bc[0]);
-          yd[g][1] = pair_mix(arow, bc[1]);
-        }
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) pv[4 * g + e] = exp2_hw(fmaf(s[4 * g + e], p.c2, -lse2));
-      }
-      // Phase 3. dS^T = P^T (dP^T - D) per 16-key step, and dQ^T += K^T dS^T.
-  #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        float dsv[8];
-  #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int r = 8 * kt + i, g = r >> 2, e = r & 3;
-          if constexpr (DROP) {
-            const uint32_t y = yd[DROP ? g : 0][e >> 1];
-            const bool kp = (e & 1) ? keep_odd(y, p.drop_t) : keep_even(y, p.drop_t);
-            dsv[i] = pv[r] * ((kp ? dp[r] * p.drop_r : 0.f) - dq_d);
-          } else {
-            dsv[i] = pv[r] * dp[r];
-          }
-        }
-        const u32x4 sop = {pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3]),
-                           pack_bf16x2(dsv[4], dsv[5]), pack_bf16x2(dsv[6], dsv[7])};
-  #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-          dqacc[db] = mfma32x32x16(ofs.tr_frag(cur, db, kt), sop, dqacc[db]);
-      }
-      sched_dq_phases<C::NKC, C::NDB, DROP>();
-    };
-
-    if constexpr (kLdsPoison) poison_stage(st0, C::STAGE, tid, C::NT);
-    if (ntiles > 0) issue(st0, bc0, tile_start(0));
-    for (int t = 0; t < ntiles; t += 2) {
-      step(st0, bc0, st1, bc1, t);
-      if (t + 1 < ntiles) step(st1, bc1, st0, bc0, t + 1);
-    }
-
-    if (myq < N) {
-      uint16_t* dqrow = static_cast<uint16_t*>(p.dq) + base + (int64_t)myq * rs;
-      const float sc = p.scale;
-  #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-  #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = db * 32 + 8 * g + 4 * hf;
-          if (d0 < D) {
-            const u32x2 w = {pack_bf16x2(dqacc[db][4 * g] * sc, dqacc[db][4 * g + 1] * sc),
-                             pack_bf16x2(dqacc[db][4 * g + 2] * sc, dqacc[db][4 * g + 3] * sc)};
-            st_global_64(dqrow + d0, w);
-          }
-        }
-      }
+    if constexpr (DROP) {
+      if (tid < C::BK / 2) bc[tid] = pair_key(kbh, (k0 >> 1) + tid);
     }
   };
-  run_block(qb_first, false);
-  if (qb_second >= 0) {
-    // The first block's last tile may still be read from a stage.
+
+  Both32<D> ofs;
+  ofs.init(lane);
+  const int vx = hf ^ VT::sw(l32);
+  int vrow[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) vrow[u] = KT::BYTES + l32 * 128 + (((2 * u) ^ vx) << 4);
+  const int vrow_tail = KT::BYTES + VT::TAIL + l32 * 32 + ((hf ^ VT::swt(l32)) << 4);
+
+  f32x16 dqacc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) dqacc[db] = f32x16{};
+  f32x16 negd;  // -D of this lane's query: start of the dP^T accumulator (no dropout)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negd[r] = -dq_d;
+
+  auto step = [&](const char* cur, const uint32_t* bcc, char* nxt, uint32_t* bcn, int t) {
+    wait_vmem();
     __syncthreads();
-    run_block(qb_second, true);
+    if constexpr (kLdsPoison) poison_stage(nxt, C::STAGE, tid, C::NT);
+    const int k0 = tile_start(t);
+    if (t + 1 < ntiles) issue(nxt, bcn, tile_start(t + 1));
+    if (CAUSAL && k0 > qw0 + 31) return;
+    // Phase 1. S^T = K Q^T : lane = query, register r -> key k0 + c_row(r, hf).
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int c = 0; c < C::NKC; ++c) s = mfma32x32x16(ld_lds_128(cur, ofs.row_off(c)), qreg[c], s);
+    sched_lds_ahead<C::NKC, 1, 1>();
+    __builtin_amdgcn_sched_barrier(0);  // the later phases are ordered on their own
+    if ((k0 + C::BK > N) || (CAUSAL && k0 + C::BK - 1 > qw0)) {
+      // tail or diagonal tile: keys past N or after the query get exp2(-inf) = 0
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + c_row(r, hf);
+        s[r] = (key >= N || (CAUSAL && key > myq)) ? -INFINITY : s[r];
+      }
+    }
+    // Phase 2. dP^T = V dO^T on the matrix cores while the vector ALUs form
+    // P^T; without dropout the accumulator starts at -D of this lane's query.
+    f32x16 dp = DROP ? f32x16{} : negd;
+#pragma unroll
+    for (int c = 0; c < C::NKC; ++c) {
+      const int vo = (2 * c < 8 * VT::NG) ? (c >> 2) * VT::GBYTES + vrow[c & 3] : vrow_tail;
+      dp = mfma32x32x16(ld_lds_128(cur, vo), doreg[c], dp);
+    }
+    float pv[16];
+    // Registers 4g + e hold keys 8g + 4hf + e; keys (e, e + 1), e = 0, 2, are
+    // a pair and share one dropout hash.
+    uint32_t yd[DROP ? 4 : 1][2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if constexpr (DROP) {
+        const u32x2 bc = *reinterpret_cast<const u32x2*>(bcc + 4 * g + 2 * hf);
+        yd[g][0] = pair_mix(arow, bc[0]);
+        yd[g][1] = pair_mix(arow, bc[1]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[4 * g + e] = exp2_hw(fmaf(s[4 * g + e], p.c2, -lse2));
+    }
+    // Phase 3. dS^T = P^T (dP^T - D) per 16-key step, and dQ^T += K^T dS^T.
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      float dsv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * kt + i, g = r >> 2, e = r & 3;
+        if constexpr (DROP) {
+          const uint32_t y = yd[DROP ? g : 0][e >> 1];
+          const bool kp = (e & 1) ? keep_odd(y, p.drop_t) : keep_even(y, p.drop_t);
+          dsv[i] = pv[r] * ((kp ? dp[r] * p.drop_r : 0.f) - dq_d);
+        } else {
+          dsv[i] = pv[r] * dp[r];
+        }
+      }
+      const u32x4 sop = {pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3]),
+                         pack_bf16x2(dsv[4], dsv[5]), pack_bf16x2(dsv[6], dsv[7])};
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+        dqacc[db] = mfma32x32x16(ofs.tr_frag(cur, db, kt), sop, dqacc[db]);
+    }
+    sched_dq_phases<C::NKC, C::NDB, DROP>();
+  };
+
+  if constexpr (kLdsPoison) poison_stage(st0, C::STAGE, tid, C::NT);
+  if (ntiles > 0) issue(st0, bc0, tile_start(0));
+  for (int t = 0; t < ntiles; t += 2) {
+    step(st0, bc0, st1, bc1, t);
+    if (t + 1 < ntiles) step(st1, bc1, st0, bc0, t + 1);
+  }
+
+  if (myq < N) {
+    uint16_t* dqrow = static_cast<uint16_t*>(p.dq) + base + (int64_t)myq * rs;
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * hf;
+        if (d0 < D) {
+          const u32x2 w = {pack_bf16x2(dqacc[db][4 * g] * sc, dqacc[db][4 * g + 1] * sc),
+                           pack_bf16x2(dqacc[db][4 * g + 2] * sc, dqacc[db][4 * g + 3] * sc)};
+          st_global_64(dqrow + d0, w);
+        }
+      }
+    }
   }
 }
 
@@ -1199,42 +1149,25 @@ __global__ __launch_bounds__(256) void dropout_mask_kernel(uint64_t seed, int b,
     }                                                                              \
   } while (0)
 
-// Launches a fixed-length backward instance; causal grids without a packed
-// batch below N = 32768 get the block pairing of plan_block_pairs
-// (fa_launch.h). A pair's descending sweep changes only the order in which
-// the dK/dV or dQ sums are accumulated (results equal up to fp32 rounding
-// order, and still the same on every run). Measured at N = 8192, d = 128:
-// dK/dV 3-4% faster, dQ unchanged, and 0.60 to 0.33 GB (dK/dV) and 0.88 to
-// 0.32 GB (dQ) fetched from beyond L2 per launch. From N = 32768 the
-// paired sweeps were slower (d = 80: dK/dV 5.59 to 6.51 ms, dQ 3.78 to
-// 3.95 ms, with the clock higher: the work-groups of a head then wait
-// together on the same L2 misses of their short 32-row tiles), so long
-// sequences keep one block per work-group.
-template <auto Kernel>
-hipError_t launch_bwd_grid(int nblk, int threads, bool pairable, const BwdParams& prm, hipStream_t s) {
-  const int BH = prm.B * prm.H;
-  const BlockPairing bp =
-      plan_block_pairs<Kernel>(nblk, BH, threads, pairable && prm.cu == nullptr && prm.N < 32768, false);
-  BwdParams p = prm;
-  p.pair_blocks = bp.pair_blocks;
-  hipLaunchKernelGGL(Kernel, dim3(bp.grid), dim3(threads), 0, s, p);
-  return hipGetLastError();
-}
-
 // bf16 matrix-core kernels: (d, causal, dropout, block-sparse) instances.
 template <int D, bool SPARSE>
 hipError_t launch_dkdv_ds(const BwdParams& prm, bool causal, bool drop, dim3 grid, dim3 block,
                           hipStream_t s) {
   // Block-sparse: two query groups per work-group (see the kernel).
   constexpr int QG = SPARSE ? 2 : 1;
-  const int nkb = (int)grid.x / (prm.B * prm.H);
-  const int nt = (int)block.x * QG;
+  block.x *= QG;
   if (causal) {
-    if (drop) return launch_bwd_grid<bwd_dkdv_bf16_kernel<D, true, true, SPARSE, QG>>(nkb, nt, !SPARSE, prm, s);
-    return launch_bwd_grid<bwd_dkdv_bf16_kernel<D, true, false, SPARSE, QG>>(nkb, nt, !SPARSE, prm, s);
+    if (drop)
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, true, true, SPARSE, QG>), grid, block, 0, s, prm);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, true, false, SPARSE, QG>), grid, block, 0, s, prm);
+  } else {
+    if (drop)
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, false, true, SPARSE, QG>), grid, block, 0, s, prm);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, false, false, SPARSE, QG>), grid, block, 0, s, prm);
   }
-  if (drop) return launch_bwd_grid<bwd_dkdv_bf16_kernel<D, false, true, SPARSE, QG>>(nkb, nt, false, prm, s);
-  return launch_bwd_grid<bwd_dkdv_bf16_kernel<D, false, false, SPARSE, QG>>(nkb, nt, false, prm, s);
+  return hipGetLastError();
 }
 
 template <int D, bool SPARSE>
@@ -1243,23 +1176,33 @@ hipError_t launch_dq_ds(const BwdParams& prm, bool causal, bool drop, dim3 grid,
   // A block-mask row covers 128 queries: block-sparse runs keep four waves.
   if constexpr (!SPARSE) {
     if (prm.N >= 32768) {
-      const int nqb = (prm.N + 255) / 256;
+      const dim3 grid8((unsigned)((prm.N + 255) / 256 * prm.B * prm.H)), block8(512);
       if (causal) {
-        if (drop) return launch_bwd_grid<bwd_dq_bf16_kernel<D, true, true, false, 8>>(nqb, 512, true, prm, s);
-        return launch_bwd_grid<bwd_dq_bf16_kernel<D, true, false, false, 8>>(nqb, 512, true, prm, s);
+        if (drop)
+          hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, true, true, false, 8>), grid8, block8, 0, s, prm);
+        else
+          hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, true, false, false, 8>), grid8, block8, 0, s, prm);
+      } else {
+        if (drop)
+          hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, false, true, false, 8>), grid8, block8, 0, s, prm);
+        else
+          hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, false, false, false, 8>), grid8, block8, 0, s, prm);
       }
-      if (drop) return launch_bwd_grid<bwd_dq_bf16_kernel<D, false, true, false, 8>>(nqb, 512, false, prm, s);
-      return launch_bwd_grid<bwd_dq_bf16_kernel<D, false, false, false, 8>>(nqb, 512, false, prm, s);
+      return hipGetLastError();
     }
   }
-  const int nqb = (int)grid.x / (prm.B * prm.H);
-  const int nt = (int)block.x;
   if (causal) {
-    if (drop) return launch_bwd_grid<bwd_dq_bf16_kernel<D, true, true, SPARSE>>(nqb, nt, !SPARSE, prm, s);
-    return launch_bwd_grid<bwd_dq_bf16_kernel<D, true, false, SPARSE>>(nqb, nt, !SPARSE, prm, s);
+    if (drop)
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, true, true, SPARSE>), grid, block, 0, s, prm);
+    else
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, true, false, SPARSE>), grid, block, 0, s, prm);
+  } else {
+    if (drop)
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, false, true, SPARSE>), grid, block, 0, s, prm);
+    else
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, false, false, SPARSE>), grid, block, 0, s, prm);
   }
-  if (drop) return launch_bwd_grid<bwd_dq_bf16_kernel<D, false, true, SPARSE>>(nqb, nt, false, prm, s);
-  return launch_bwd_grid<bwd_dq_bf16_kernel<D, false, false, SPARSE>>(nqb, nt, false, prm, s);
+  return hipGetLastError();
 }
 
 template <int D>

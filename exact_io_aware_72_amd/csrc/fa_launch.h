@@ -1,6 +1,6 @@
-// Host-side launch helpers shared by the forward and backward launchers:
-// device and occupancy queries, and the choice of causal block pairing
-// (map_block_pairs / map_block_pair in fa_device.h).
+// Host-side launch helpers of the forward launchers: device and occupancy
+// queries, and the choice of causal block pairing (map_block_pairs /
+// map_block_pair in fa_device.h).
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -190,37 +190,6 @@ def test_backward_matches_oracle(w):
     assert_close("dV", dv, dv_r, w.dtype)
 
 
-# Causal backward grids larger than the device holds at once (below
-# N = 32768): each dK/dV work-group takes key blocks (j, nkb - 1 - j), the
-# first over descending query tiles, and each dQ work-group query blocks
-# (nqb - 1 - j, j), the second over descending key tiles.
-BWD_PAIR_CASES = [
-    _case(3, B=2, H=64, N=1024),
-    _case(2, B=4, H=64, N=1024, backward=True),
-    _case(4, B=2, H=64, N=1024),
-    _case(5, B=1, H=128, N=1024),
-    _case(3, B=1, H=105, N=1100),
-]
-
-
-@pytest.mark.parametrize("w", BWD_PAIR_CASES, ids=_ids(BWD_PAIR_CASES))
-def test_backward_block_pairs_per_group(w):
-    inp = make_inputs(w, with_grad=True)
-    dev, val = device_inputs(inp, w.dtype)
-    o, lse = fa.forward(dev["q"], dev["k"], dev["v"], w.causal, w.dropout_p, w.dropout_seed, w.scale)
-    dq, dk, dv = _run_bwd(dev, w, o, lse)
-    dq_r, dk_r, dv_r, _ = oracle.backward(val["q"], val["k"], val["v"], val["do"], w.scale, w.causal,
-                                          w.dropout_p, w.dropout_seed)
-    # Causal: every query sees the first keys, whose dV reaches |5.4| over
-    # these 100+ heads. bf16 stores such values only to within 0.0156, and
-    # the bf16 rounding of P in the dV product adds about 0.01 (the same
-    # errors as with one block per work-group), so these cases take the
-    # magnitude-relative bar.
-    assert_close("dQ", dq, dq_r, w.dtype, scaled=True)
-    assert_close("dK", dk, dk_r, w.dtype, scaled=True)
-    assert_close("dV", dv, dv_r, w.dtype, scaled=True)
-
-
 def test_preprocess_matches_definition():
     w = _case(3, B=2, H=3, N=77)
     inp = make_inputs(w, with_grad=True)
