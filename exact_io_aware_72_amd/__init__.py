@@ -129,26 +129,29 @@ def _code(t) -> int:
 
 
 def _shape(q, *others):
+    # Checked on every call, so kept cheap: dtype objects are singletons and
+    # get_device() is an int (torch.device comparisons cost microseconds).
     if q.dim() != 4:
         raise ValueError("expected tensors of shape (batch, seq_len, num_heads, head_dim)")
+    s, dt, dev = q.shape, q.dtype, q.get_device()
     for t in (q,) + others:
-        if t.shape != q.shape:
-            raise ValueError(f"shape mismatch: {tuple(t.shape)} vs {tuple(q.shape)}")
-        if t.dtype != q.dtype:
+        if t.shape != s:
+            raise ValueError(f"shape mismatch: {tuple(t.shape)} vs {tuple(s)}")
+        if t.dtype is not dt:
             raise TypeError("q, k, v (and o, dout) must share one dtype")
-        if t.device != q.device or t.device.type != "cuda":
+        if not t.is_cuda or t.get_device() != dev:
             raise ValueError("tensors must live on the same GPU")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
-    B, N, H, d = q.shape
+    B, N, H, d = s
     return B, N, H, d
 
 
 def _buf(t, shape, dtype, like, name):
     """A caller-supplied buffer: the kernels trust its size, so shape, dtype,
     device and contiguity are checked here."""
-    if (tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != like.device
-            or not t.is_contiguous()):
+    if (t.shape != tuple(shape) or t.dtype is not dtype or not t.is_cuda
+            or t.get_device() != like.get_device() or not t.is_contiguous()):
         raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
                          f"on {like.device} (got {tuple(t.shape)}, {t.dtype}, {t.device})")
     return t
@@ -162,8 +165,12 @@ def _out(t, shape, dtype, like, name):
 
 
 def _stream(t):
+    """The current HIP stream of t's device, as an integer handle."""
     torch = _torch()
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(t.get_device())
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _scale(scale, d):
