@@ -42,9 +42,12 @@ int check_problem(int B, int H, int N, int d, int dtype) {
   const int64_t rows = bn * H;
   if ((rows + 15) / 16 > (int64_t)INT32_MAX) return FA_ERR_SHAPE;
   if ((int64_t)((N + 31) / 32) * B * H > (int64_t)INT32_MAX) return FA_ERR_SHAPE;
-  // The kernels address one batch item's rows with 32-bit byte offsets.
-  const int64_t esize = dtype == FA_BF16 ? 2 : 4;
-  if ((int64_t)N * H * d * esize >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  // The kernels read rows through buffer resources based at each block,
+  // tile or window start, with 32-bit offsets from there (a row is at most
+  // H * d * 4 <= 2^22 bytes), and per-row statistics with 32-bit offsets
+  // (N * 4 < 2^32). A batch item itself may exceed 4 GiB.
+  if (N >= (1 << 30)) return FA_ERR_SHAPE;
+  if ((int64_t)H * d > (1 << 20)) return FA_ERR_SHAPE;
   return FA_OK;
 }
 

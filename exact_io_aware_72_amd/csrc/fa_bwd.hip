@@ -303,7 +303,7 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdP
 
   // The block's V rows into LDS (rows >= N arrive as zeros).
   {
-    const BufRes rvb = make_bufres(Vg + (int64_t)k0 * rs, (uint32_t)(N - k0) * rs2);
+    const BufRes rvb = rows_bufres(Vg, k0, N, C::BK, rs2);
 #pragma unroll
     for (int m = 0; m < C::VLPW; ++m) {
       const int i = wv + C::NW * m;
@@ -315,11 +315,11 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdP
     }
   }
   // This lane's K row (B operand of S = Q K^T); zeros past N.
-  const BufRes rk = make_bufres(Kg, (uint32_t)N * rs2);
+  const BufRes rk = rows_bufres(Kg, k0, N, C::BK, rs2);
   u32x4 kreg[C::NKC];
 #pragma unroll
   for (int c = 0; c < C::NKC; ++c)
-    kreg[c] = buf_load_128(rk, (uint32_t)mykey * rs2 + (16 * c + 8 * hf) * 2);
+    kreg[c] = buf_load_128(rk, (uint32_t)(mykey - k0) * rs2 + (16 * c + 8 * hf) * 2);
   // This lane's V row in LDS (B operand of dP = dO V^T).
   const int vr = wv * 32 + l32;
   const int vx = hf ^ VB::sw(vr);
@@ -400,9 +400,8 @@ __global__ __launch_bounds__(DkdvCfg<D>::NT * QG) void bwd_dkdv_bf16_kernel(BwdP
     }
   };
   auto issue = [&](char* stage, int qt0) {
-    const uint32_t left = (uint32_t)(N - qt0) * rs2;
-    const BufRes rq = make_bufres(Qg + (int64_t)qt0 * rs, left);
-    const BufRes ro = make_bufres(dOg + (int64_t)qt0 * rs, left);
+    const BufRes rq = rows_bufres(Qg, qt0, N, C::BQ, rs2);
+    const BufRes ro = rows_bufres(dOg, qt0, N, C::BQ, rs2);
 #pragma unroll
     for (int m = 0; m < C::LPW; ++m) {
       const int i = wv + C::NW * m;
@@ -731,8 +730,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdParams p) {
   const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + base;
   const uint16_t* dOg = static_cast<const uint16_t*>(p.dout) + base;
   const uint32_t rs2 = (uint32_t)(H * D * 2);
-  const uint32_t nbytes = (uint32_t)N * rs2;
-  const BufRes rq = make_bufres(Qg, nbytes), rdo = make_bufres(dOg, nbytes);
+  const BufRes rq = rows_bufres(Qg, q0, N, C::BQ, rs2), rdo = rows_bufres(dOg, q0, N, C::BQ, rs2);
   const int64_t statoff = sr.stat;
   const BufRes rl = make_bufres(p.lse + statoff, (uint32_t)N * 4);
   const BufRes rd = make_bufres(p.dsum + statoff, (uint32_t)N * 4);
@@ -741,7 +739,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdParams p) {
   u32x4 qreg[C::NKC], doreg[C::NKC];
 #pragma unroll
   for (int c = 0; c < C::NKC; ++c) {
-    const uint32_t off = (uint32_t)myq * rs2 + (16 * c + 8 * hf) * 2;
+    const uint32_t off = (uint32_t)(myq - q0) * rs2 + (16 * c + 8 * hf) * 2;
     qreg[c] = buf_load_128(rq, off);
     doreg[c] = buf_load_128(rdo, off);
   }
@@ -785,9 +783,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdParams p) {
     dlds[m] = off;
   }
   auto issue = [&](char* stage, uint32_t* bc, int k0) {
-    const uint32_t left = (uint32_t)(N - k0) * rs2;
-    const BufRes rk = make_bufres(Kg + (int64_t)k0 * rs, left);
-    const BufRes rv = make_bufres(Vg + (int64_t)k0 * rs, left);
+    const BufRes rk = rows_bufres(Kg, k0, N, C::BK, rs2);
+    const BufRes rv = rows_bufres(Vg, k0, N, C::BK, rs2);
 #pragma unroll
     for (int m = 0; m < C::LPW; ++m) {
       const int i = wave + NW * m;

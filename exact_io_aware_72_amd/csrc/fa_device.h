@@ -87,6 +87,18 @@ __device__ __forceinline__ BufRes make_bufres(const void* base, uint32_t bytes) 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
+// Buffer resource over rows [row0, row0 + cap) of a (batch, head) slice
+// whose rows lie `stride` bytes apart, cut at row n: reads of rows at or past
+// n return zeros. Offsets are bytes from row row0, and the range is at most
+// cap * stride bytes, so offsets stay 32-bit for slices of any size.
+__device__ __forceinline__ BufRes rows_bufres(const void* slice, int row0, int n, int cap,
+                                              uint32_t stride) {
+  // readfirstlane: the clamp may be selected as a vector instruction, and a
+  // resource held in vector registers would need a waterfall loop per load.
+  const int rows = __builtin_amdgcn_readfirstlane(min(max(n - row0, 0), cap));
+  return make_bufres(static_cast<const char*>(slice) + (int64_t)row0 * stride,
+                     (uint32_t)rows * stride);
+}
 __device__ __forceinline__ u32x4 buf_load_128(BufRes r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }

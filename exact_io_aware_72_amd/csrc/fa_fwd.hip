@@ -174,21 +174,21 @@ __attribute__((amdgpu_waves_per_eu(1, ((D == 64 && !FP8) || NW == 16) ? 4 : 2)))
     u32x4 qreg[C::NKC];
     float qsc = 1.f;  // FP8: this query block's scale
     if constexpr (FP8) {
-      const BufRes rq = make_bufres(p.q8 + base, (uint32_t)N * rsk);
+      const BufRes rq = rows_bufres(p.q8 + base, q0, N, C::BM, rsk);
   #pragma unroll
       for (int c = 0; c < NK8; ++c)
   #pragma unroll
         for (int u = 0; u < 2; ++u) {
           // chunks past D (D = 80) read as zeros through an out-of-range offset
           const int ch = 4 * c + 2 * hf + u;
-          qreg[2 * c + u] = buf_load_128(rq, ch < KT::VALID ? (uint32_t)myq * rsk + 16 * ch : 0x80000000u);
+          qreg[2 * c + u] = buf_load_128(rq, ch < KT::VALID ? (uint32_t)(myq - q0) * rsk + 16 * ch : 0x80000000u);
         }
       qsc = p.q_scale[((int64_t)b * H + h) * nqb + qb];
     } else {
-      const BufRes rq = make_bufres(Qg, (uint32_t)N * rs2);
+      const BufRes rq = rows_bufres(Qg, q0, N, C::BM, rs2);
   #pragma unroll
       for (int c = 0; c < C::NKC; ++c)
-        qreg[c] = buf_load_128(rq, (uint32_t)myq * rs2 + (16 * c + 8 * hf) * 2);
+        qreg[c] = buf_load_128(rq, (uint32_t)(myq - q0) * rs2 + (16 * c + 8 * hf) * 2);
     }
     // FP8: the key tiles' scales, one per 64 keys; the next tile's is loaded
     // with its tile (and so has arrived when that tile's loads have).
@@ -250,8 +250,8 @@ __attribute__((amdgpu_waves_per_eu(1, ((D == 64 && !FP8) || NW == 16) ? 4 : 2)))
     }
     auto issue = [&](char* stage, uint32_t* ck, int k0) {
       // Resources start at row k0 and end at row N: rows past N arrive as zeros.
-      const BufRes rk = make_bufres(Kb + (int64_t)k0 * rsk, (uint32_t)(Nk - k0) * rsk);
-      const BufRes rv = make_bufres(Vg + (int64_t)k0 * rs, (uint32_t)(Nk - k0) * rs2);
+      const BufRes rk = rows_bufres(Kb, k0, Nk, C::BN, rsk);
+      const BufRes rv = rows_bufres(Vg, k0, Nk, C::BN, rs2);
       if constexpr (FP8) ksn = buf_load_f32(rks, (uint32_t)(k0 >> 6) * 4);
   #pragma unroll
       for (int m = 0; m < C::LPW; ++m) {
@@ -573,17 +573,19 @@ __global__ __launch_bounds__(64 * kF32Waves) void fwd_f32_kernel(FwdParamsF p) {
   const float* Kg = p.k + sr.base;
   const float* Vg = p.v + sr.base;
 
-  // Buffer resources over the (batch, head) rows: reads of rows at or past N
-  // return zeros (hardware range check), so no load needs a branch.
+  // Buffer resources over this block's rows and each tile's rows: reads of
+  // rows at or past N return zeros (hardware range check), so no load needs a
+  // branch.
   const uint32_t rs4 = (uint32_t)rs * 4u;
-  const BufRes rq = make_bufres(Qg, (uint32_t)N * rs4);
-  const BufRes rk = make_bufres(Kg, (uint32_t)N * rs4);
-  const BufRes rv = make_bufres(Vg, (uint32_t)N * rs4);
+  const BufRes rq = rows_bufres(Qg, q0, N, BM, rs4);
+  // Rows per K/V resource window: the largest power of two with
+  // win * rs4 <= 2^30 (rs4 <= 2^22 at the boundary, so win >= 128).
+  const int win = 1 << (30 - (32 - __builtin_clz(rs4)));
   // This lane's query row, dimensions hf * DH .. hf * DH + DH - 1.
   float qf[DH];
 #pragma unroll
   for (int c = 0; c < DH; c += 4) {
-    const u32x4 x = buf_load_128(rq, (uint32_t)myq * rs4 + (uint32_t)(hf * DH + c) * 4u);
+    const u32x4 x = buf_load_128(rq, (uint32_t)l32 * rs4 + (uint32_t)(hf * DH + c) * 4u);
     qf[c] = __uint_as_float(x[0]), qf[c + 1] = __uint_as_float(x[1]);
     qf[c + 2] = __uint_as_float(x[2]), qf[c + 3] = __uint_as_float(x[3]);
   }
@@ -612,10 +614,18 @@ __global__ __launch_bounds__(64 * kF32Waves) void fwd_f32_kernel(FwdParamsF p) {
     // dimensions as its query row. V: step c of O^T += V^T P^T takes key
     // k0 + c_row(c, hf), column 32 db + l32 (columns past D, only for
     // D = 80, read zeros through an offset beyond the range).
+    // K and V resources start at row kb, the start of the window of `win`
+    // rows holding k0: offsets from there stay below 2^30 + 2^28 for slices
+    // of any size, and in the usual case (the whole slice in one window,
+    // kb = 0) they are the slice's own offsets, which depend on the tile and
+    // are computed per tile rather than held across the loop.
+    const int kb = k0 & -win, kr = k0 - kb;
+    const BufRes rk = rows_bufres(Kg, kb, N, win + BN, rs4);
+    const BufRes rv = rows_bufres(Vg, kb, N, win + BN, rs4);
     float kf[DH];
 #pragma unroll
     for (int c = 0; c < DH; c += 4) {
-      const u32x4 x = buf_load_128(rk, (uint32_t)(k0 + l32) * rs4 + (uint32_t)(hf * DH + c) * 4u);
+      const u32x4 x = buf_load_128(rk, (uint32_t)(kr + l32) * rs4 + (uint32_t)(hf * DH + c) * 4u);
       kf[c] = __uint_as_float(x[0]), kf[c + 1] = __uint_as_float(x[1]);
       kf[c + 2] = __uint_as_float(x[2]), kf[c + 3] = __uint_as_float(x[3]);
     }
@@ -624,7 +634,7 @@ __global__ __launch_bounds__(64 * kF32Waves) void fwd_f32_kernel(FwdParamsF p) {
       const int col = 32 * db + l32;
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
-        const uint32_t off = (uint32_t)(k0 + c_row(c, hf)) * rs4 + (uint32_t)col * 4u;
+        const uint32_t off = (uint32_t)(kr + c_row(c, hf)) * rs4 + (uint32_t)col * 4u;
         va[db][c] = buf_load_f32(rv, col < D ? off : 0x80000000u);
       }
     };

@@ -25,8 +25,8 @@
  *     "enqueued". Device faults surface at the caller's next synchronisation.
  *   - Arguments are validated before any HIP call; on any error nothing is
  *     launched and nothing is written. No C++ exception crosses this ABI.
- *   - Supported: d in {64, 80, 128}; any N >= 1 (tails handled by masks)
- *     with N*H*d*sizeof(element) < 2^31 (one batch item below 2 GiB);
+ *   - Supported: d in {64, 80, 128}; 1 <= N < 2^30 (tails handled by
+ *     masks), H*d <= 2^20, B*N*H <= 2^36; a batch item may exceed 4 GiB;
  *     dtype FA_BF16 (bf16 storage, fp32 accumulation, bf16 matrix cores) or
  *     FA_F32 (fp32 throughout). Causal masking keeps key j for query i iff
  *     j <= i (queries and keys share positions 0..N-1).
@@ -55,8 +55,8 @@ typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,        /* a required pointer is NULL                         */
-  FA_ERR_SHAPE = -2,       /* B, H or N < 1, a batch item of 2 GiB or more, or
-                              a size that overflows                             */
+  FA_ERR_SHAPE = -2,       /* B, H or N < 1, N >= 2^30, H*d > 2^20, or a size
+                              that overflows                                    */
   FA_ERR_HEADDIM = -3,     /* d not in {64, 80, 128}                             */
   FA_ERR_DTYPE = -4,       /* dtype not FA_F32 / FA_BF16                         */
   FA_ERR_DROPOUT = -5,     /* dropout_p NaN, outside [0, 1) or in (0, 2^-16)     */

@@ -83,7 +83,7 @@ def _fwd(**kw):
     (dict(q=0), NULL), (dict(k=0), NULL), (dict(v=0), NULL), (dict(o=0), NULL), (dict(lse=0), NULL),
     (dict(q=P + 8), ALIGN), (dict(o=P + 2), ALIGN), (dict(lse=P + 4), ALIGN),
     (dict(B=0), SHAPE), (dict(H=-1), SHAPE), (dict(N=0), SHAPE), (dict(B=1 << 20, H=1 << 10, N=1 << 20), SHAPE),
-    (dict(N=1 << 20, H=8, d=128), SHAPE), (dict(N=1 << 19, H=16, d=128, dtype=0), SHAPE),
+    (dict(N=1 << 30), SHAPE), (dict(N=1 << 30, dtype=0), SHAPE), (dict(H=(1 << 13) + 1, d=128), SHAPE),
     (dict(d=32), HEADDIM), (dict(d=96), HEADDIM), (dict(d=256), HEADDIM),
     (dict(dtype=2), DTYPE), (dict(dtype=-1), DTYPE),
     (dict(p=1.0), DROPOUT), (dict(p=-0.1), DROPOUT), (dict(p=float("nan")), DROPOUT), (dict(p=1.5), DROPOUT),

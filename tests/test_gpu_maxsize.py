@@ -1,9 +1,12 @@
-"""The largest batch item the kernels address with 32-bit byte offsets: B=1,
-H=64, N=131071, d=128 bf16 (N*H*d*2 = 2^31 - 16384 bytes per tensor item;
-one more row is rejected at the boundary). Causal forward and backward on
-the GPU; O, LSE and dQ checked at sampled rows (the last row included)
+"""Batch items above 4 GiB: the kernels read rows through buffer resources
+based at each block, tile or window start, so no byte offset spans a whole
+item. bf16 B=1, H=256, N=66001, d=128 (N*H*d*2 = 4.33e9 bytes per tensor
+item, past 2^32): causal forward and backward, O, LSE and dQ checked at
+sampled rows (the last row and rows past 2^32 / (H*d*2) = 65536 included)
 against the oracle's formulas on those rows, dK and dV through the exact
-column-sum identities."""
+column-sum identities. fp32 B=1, H=256, N=33001, d=128 (4.33e9 bytes;
+the fp32 forward's K/V windows hold 4096 rows at this row size): causal
+forward at sampled rows."""
 import numpy as np
 import pytest
 
@@ -16,8 +19,6 @@ pytestmark = pytest.mark.gpu
 
 import exact_io_aware_72_amd as fa  # noqa: E402
 
-B, H, N, D = 1, 64, 131071, 128
-
 
 @pytest.fixture(autouse=True)
 def _need_gpu():
@@ -27,33 +28,42 @@ def _need_gpu():
     torch.cuda.empty_cache()
 
 
-def test_largest_item_sampled_rows_and_invariants():
-    assert N * H * D * 2 < 2 ** 31 <= (N + 1) * H * D * 2
-    scale = float(np.float32(1.0 / np.sqrt(D)))
-    q, k, v, do = (device_normal((B, N, H, D), 7100 + i) for i in range(4))
-    print(f"max-size item: B={B} H={H} N={N} d={D}", flush=True)
-    o, lse = fa.forward(q, k, v, True, 0.0, 0, scale)
-    dq, dk, dv = fa.backward(q, k, v, o, do, lse, True, 0.0, 0, scale)
-    torch.cuda.synchronize()
-    rows = np.unique(np.r_[0, 1, 127, 128, 65535, 65536, N - 129, N - 2, N - 1,
-                           np.random.default_rng(9).integers(0, N, 6)])
-    for h in (0, H - 1):
-        qh, kh, vh, doh = (x[0, :, h].to(torch.float64).cpu().numpy() for x in (q, k, v, do))
-        o_r, l_r, dq_r = [], [], []
-        for r in rows:
-            s = A.attention_scores(qh[r:r + 1], kh[:r + 1], scale, True, r)
-            _, _, l_ = A.softmax_stats(s)
-            p = A.attention_probs(s, l_)
-            o_row = p @ vh[:r + 1]
+def _rows_reference(q, k, v, do, h, rows, scale):
+    """O, LSE and (with do) dQ of the given causal rows of head h, row by row."""
+    qh, kh, vh = (x[0, :, h].to(torch.float64).cpu().numpy() for x in (q, k, v))
+    doh = None if do is None else do[0, :, h].to(torch.float64).cpu().numpy()
+    o_r, l_r, dq_r = [], [], []
+    for r in rows:
+        s = A.attention_scores(qh[r:r + 1], kh[:r + 1], scale, True, r)
+        _, _, l_ = A.softmax_stats(s)
+        p = A.attention_probs(s, l_)
+        o_row = p @ vh[:r + 1]
+        o_r.append(o_row[0])
+        l_r.append(l_[0])
+        if doh is not None:
             d_row = np.sum(doh[r] * o_row[0])
             dp = doh[r:r + 1] @ vh[:r + 1].T
             dq_r.append((scale * (p * (dp - d_row)) @ kh[:r + 1])[0])
-            o_r.append(o_row[0])
-            l_r.append(l_[0])
-        idx = torch.from_numpy(rows).cuda()
-        assert_close(f"O[h={h}]", o[0, idx, h].double().cpu().numpy(), np.array(o_r), "bf16")
-        assert_close(f"LSE[h={h}]", lse[0, h, idx].double().cpu().numpy(), np.array(l_r), "bf16")
-        assert_close(f"dQ[h={h}]", dq[0, idx, h].double().cpu().numpy(), np.array(dq_r), "bf16")
+    return np.array(o_r), np.array(l_r), (np.array(dq_r) if doh is not None else None)
+
+
+def test_bf16_item_over_4gib_sampled_rows_and_invariants():
+    B, H, N, D = 1, 256, 66001, 128
+    assert N * H * D * 2 > 2 ** 32
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    q, k, v, do = (device_normal((B, N, H, D), 7100 + i) for i in range(4))
+    print(f"bf16 item over 4 GiB: B={B} H={H} N={N} d={D}", flush=True)
+    o, lse = fa.forward(q, k, v, True, 0.0, 0, scale)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, True, 0.0, 0, scale)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[0, 1, 127, 128, 32767, 32768, 65535, 65536, 65537,
+                           N - 129, N - 2, N - 1, np.random.default_rng(9).integers(0, N, 6)])
+    idx = torch.from_numpy(rows).cuda()
+    for h in (0, H - 1):
+        o_r, l_r, dq_r = _rows_reference(q, k, v, do, h, rows, scale)
+        assert_close(f"O[h={h}]", o[0, idx, h].double().cpu().numpy(), o_r, "bf16")
+        assert_close(f"LSE[h={h}]", lse[0, h, idx].double().cpu().numpy(), l_r, "bf16")
+        assert_close(f"dQ[h={h}]", dq[0, idx, h].double().cpu().numpy(), dq_r, "bf16")
     # sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i per (h, column), within the
     # random-walk bound of bf16 storage (each value carries 2^-9 relative).
     for name, x, ref in (("sum dK", dk, None), ("sum dV", dv, do)):
@@ -64,3 +74,20 @@ def test_largest_item_sampled_rows_and_invariants():
         err = (s - r).abs()
         assert bool((err <= bound).all()), f"{name}: worst excess {(err - bound).max().item():.3e}"
         del x64
+
+
+def test_f32_item_over_4gib_sampled_rows():
+    B, H, N, D = 1, 256, 33001, 128
+    assert N * H * D * 4 > 2 ** 32
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    q, k, v = (device_normal((B, N, H, D), 7200 + i, dtype="f32") for i in range(3))
+    print(f"fp32 item over 4 GiB: B={B} H={H} N={N} d={D}", flush=True)
+    o, lse = fa.forward(q, k, v, True, 0.0, 0, scale)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[0, 31, 32, 4095, 4096, 16383, 16384, 32767, 32768, N - 33, N - 2, N - 1,
+                           np.random.default_rng(10).integers(0, N, 5)])
+    idx = torch.from_numpy(rows).cuda()
+    for h in (0, H - 1):
+        o_r, l_r, _ = _rows_reference(q, k, v, None, h, rows, scale)
+        assert_close(f"O[h={h}]", o[0, idx, h].double().cpu().numpy(), o_r, "f32")
+        assert_close(f"LSE[h={h}]", lse[0, h, idx].double().cpu().numpy(), l_r, "f32")
