@@ -41,7 +41,17 @@ CASES = [
     # work-groups), with sequences shorter than one such group beside it
     _vw("bf16-d64-causal-long", [8300, 0, 300, 1], 1, 64, "bf16", True, 0.0, seed=3109),
     _vw("bf16-d80-full-long-drop", [257, 8200], 1, 80, "bf16", False, 0.1, amp=0.5, seed=3110),
+    # a causal grid past what the device holds at once: each work-group takes
+    # a pair of one sequence's blocks (the second over descending key tiles);
+    # odd and even block counts, empty and one-row sequences
+    _vw("bf16-d128-causal-pairs", [1100, 0, 1, 900, 257, 1024, 640, 129, 1000, 3, 768, 512], 32, 128,
+        "bf16", True, 0.0, seed=3111),
+    _vw("bf16-d64-causal-pairs-drop", [1024, 700, 5, 1100, 300, 999, 1, 64], 48, 64, "bf16", True, 0.1,
+        seed=3112),
 ]
+
+
+PAIR_CASES = {"bf16-d128-causal-pairs", "bf16-d64-causal-pairs-drop"}
 
 
 def _device(cu, inp, dtype):
@@ -66,9 +76,14 @@ def test_varlen_forward_backward_match_oracle(w):
                                              w.causal, w.dropout_p, w.dropout_seed)
     assert_close("O", to_host(o), o_r, w.dtype)
     assert_close("LSE", to_host(lse), lse_r, w.dtype)
-    assert_close("dQ", to_host(dq), dq_r, w.dtype)
-    assert_close("dK", to_host(dk), dk_r, w.dtype)
-    assert_close("dV", to_host(dv), dv_r, w.dtype)
+    # The block-pair cases run 32-48 heads: every query sees its sequence's
+    # first keys, whose dV then reaches |5| somewhere, where bf16 stores values
+    # only to within 0.0156 and the bf16 rounding of P in the dV product adds
+    # about 0.01; their gradients take the magnitude-relative bar.
+    scaled = w.name in PAIR_CASES
+    assert_close("dQ", to_host(dq), dq_r, w.dtype, scaled=scaled)
+    assert_close("dK", to_host(dk), dk_r, w.dtype, scaled=scaled)
+    assert_close("dV", to_host(dv), dv_r, w.dtype, scaled=scaled)
 
 
 @pytest.mark.parametrize("dtype,d,causal,p", [("bf16", 128, True, 0.1), ("bf16", 80, False, 0.0),
