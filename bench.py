@@ -249,9 +249,11 @@ def run_gpu_varlen(wv, steps, warmup, torch, fa):
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
-    ms_step = evs[0][0].elapsed_time(evs[-1][2]) / steps
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # medians over the timed steps (the mean step beside them)
+    ms_step = float(np.median([e[0].elapsed_time(e[2]) for e in evs]))
+    ms_step_mean = evs[0][0].elapsed_time(evs[-1][2]) / steps
+    fwd_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
     fwd_f, bwd_f = counted_flops_varlen(lengths, wv.H, wv.d, wv.causal, True)
     del dev, q, k, v, do, o, dq, dk, dv
     torch.cuda.empty_cache()
@@ -261,8 +263,8 @@ def run_gpu_varlen(wv, steps, warmup, torch, fa):
     return {
         "workload": wv.name, "num_seqs": len(lengths), "total_tokens": int(total),
         "max_seqlen": maxlen, "tflops": (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12,
-        "ms_per_step": ms_step, "pct_of_peak": 100.0 * (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
-        / PEAK_BF16_TFLOPS,
+        "ms_per_step": ms_step, "ms_per_step_mean": ms_step_mean,
+        "pct_of_peak": 100.0 * (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "fwd_tflops": fwd_f / (fwd_ms * 1e-3) / 1e12, "bwd_tflops": bwd_f / (bwd_ms * 1e-3) / 1e12,
         "padded_fixed_length_ms_per_step": rp["ms_per_step"],
         "roofline": _mfma_roofline((fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12),
@@ -314,9 +316,11 @@ def run_gpu_sparse(name, steps, warmup, torch, fa):
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
-    ms_step = evs[0][0].elapsed_time(evs[-1][2]) / steps
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # medians over the timed steps (the mean step beside them)
+    ms_step = float(np.median([e[0].elapsed_time(e[2]) for e in evs]))
+    ms_step_mean = evs[0][0].elapsed_time(evs[-1][2]) / steps
+    fwd_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
     elems = kept_score_elements(mask_np, w.N, w.causal) * w.B * w.H
     fwd_f = 4.0 * w.d * elems
     bwd_f = 2.5 * fwd_f
@@ -326,8 +330,8 @@ def run_gpu_sparse(name, steps, warmup, torch, fa):
     return {
         "workload": w.name, "mask": f"local window +-{kw['window']} blocks + {kw['n_global']} global key blocks",
         "density": float(np.mean(mask_np != 0)), "tflops": (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12,
-        "ms_per_step": ms_step, "pct_of_peak": 100.0 * (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
-        / PEAK_BF16_TFLOPS,
+        "ms_per_step": ms_step, "ms_per_step_mean": ms_step_mean,
+        "pct_of_peak": 100.0 * (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "fwd_tflops": fwd_f / (fwd_ms * 1e-3) / 1e12, "bwd_tflops": bwd_f / (bwd_ms * 1e-3) / 1e12,
         "dense_ms_per_step": rd["ms_per_step"],
         "roofline": _mfma_roofline((fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12),
