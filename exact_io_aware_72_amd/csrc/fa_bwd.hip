@@ -47,6 +47,7 @@ struct BwdParams {
   uint32_t drop_t;
   float drop_r;
   uint64_t seed;
+  int pair_blocks;  // dQ, causal: complementary query block pairs per work-group
 };
 
 BwdParams make_params(const AttnArgs& a) {
@@ -73,6 +74,7 @@ BwdParams make_params(const AttnArgs& a) {
   p.drop_t = a.drop_threshold;
   p.drop_r = a.drop_rescale;
   p.seed = a.seed;
+  p.pair_blocks = 0;  // set by the dQ launcher
   return p;
 }
 
@@ -714,188 +716,216 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_bf16_kernel(BwdParams p) {
   const int l32 = lane & 31, hf = lane >> 5;
   const int H = p.H;
   const int nqb = (p.N + C::BQ - 1) / C::BQ;
-  const BlockMap bm = map_block(blockIdx.x, nqb, p.B * H);
-  const int qb = CAUSAL ? (nqb - 1 - bm.rank) : bm.rank;
+  // Causal, eight-wave groups without dropout (long sequences), with
+  // p.pair_blocks: the pair of query blocks (nqb - 1 - j, j) per
+  // work-group, the second over descending key tiles, so that the
+  // work-groups of a head sweep the same K/V tiles together. Other
+  // instances take one block per work-group (heaviest first) and compile
+  // to a single pass.
+  constexpr int kPasses = (NW == 8 && CAUSAL && !DROP && !SPARSE) ? 2 : 1;
+  const bool paired = kPasses == 2 && p.pair_blocks;
+  const BlockMap bm = paired ? map_block_pair(blockIdx.x, (nqb + 1) / 2, p.B * H)
+                             : map_block(blockIdx.x, nqb, p.B * H);
   const int b = bm.bh / H, h = bm.bh - b * H;
   const SeqRows sr = seq_rows(p.cu, p.total, b, h, H, D, p.N);
   const int N = sr.n;
-  const int q0 = qb * C::BQ;
-  if (q0 >= N) return;  // block past the end of a shorter sequence
-  const int qw0 = q0 + wave * 32;
-  const int myq = qw0 + l32;
-  const int64_t rs = (int64_t)H * D;
-  const int64_t base = sr.base;
-  const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + base;
-  const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + base;
-  const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + base;
-  const uint16_t* dOg = static_cast<const uint16_t*>(p.dout) + base;
-  const uint32_t rs2 = (uint32_t)(H * D * 2);
-  const BufRes rq = rows_bufres(Qg, q0, N, C::BQ, rs2), rdo = rows_bufres(dOg, q0, N, C::BQ, rs2);
-  const int64_t statoff = sr.stat;
-  const BufRes rl = make_bufres(p.lse + statoff, (uint32_t)N * 4);
-  const BufRes rd = make_bufres(p.dsum + statoff, (uint32_t)N * 4);
-
-  // Rows past N: zero Q, dO, LSE and D give dS = 0 (never stored anyway).
-  u32x4 qreg[C::NKC], doreg[C::NKC];
-#pragma unroll
-  for (int c = 0; c < C::NKC; ++c) {
-    const uint32_t off = (uint32_t)(myq - q0) * rs2 + (16 * c + 8 * hf) * 2;
-    qreg[c] = buf_load_128(rq, off);
-    doreg[c] = buf_load_128(rdo, off);
-  }
-  const float lse2 = buf_load_f32(rl, (uint32_t)myq * 4) * kLog2e;
-  const float dq_d = buf_load_f32(rd, (uint32_t)myq * 4);
-  uint64_t kbh = 0;
-  uint32_t arow = 0;
-  if constexpr (DROP) {
-    kbh = head_key(p.seed, b, h, H);
-    arow = row_key(kbh, myq);
-  }
-
-  const int kend = CAUSAL ? min(N, q0 + C::BQ) : N;
-  int ntiles;
-  if constexpr (SPARSE) {
-    const int nb = (N + kSparseBlock - 1) / kSparseBlock;
-    const uint8_t* mrow = p.bmask + b * p.msb + h * p.msh + (int64_t)qb * nb;
-    const KeptBlocks kb =
-        collect_blocks(mrow, 1, 0, (kend + kSparseBlock - 1) / kSparseBlock, kept, lane, wave == 0);
-    ntiles = kept_tiles<C::BK>(kb, kend);
-    __syncthreads();
+  int qb_first, qb_second = -1;
+  if (paired) {
+    const int nb = (N + C::BQ - 1) / C::BQ;
+    if (bm.rank >= (nb + 1) / 2) return;
+    qb_first = nb - 1 - bm.rank;
+    if (bm.rank < qb_first) qb_second = bm.rank;
   } else {
-    ntiles = (kend + C::BK - 1) / C::BK;
+    qb_first = CAUSAL ? (nqb - 1 - bm.rank) : bm.rank;
   }
-  auto tile_start = [&](int t) { return SPARSE ? kept_tile_start<C::BK>(kept, t) : t * C::BK; };
+#pragma unroll 1
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int qb = pass == 0 ? qb_first : qb_second;
+    if (qb < 0) break;
+    const bool rev = pass > 0;  // the key tiles in descending order
+    // The previous block's last tile may still be read from a stage.
+    if (pass > 0) __syncthreads();
+    const int q0 = qb * C::BQ;
+    if (q0 >= N) break;  // block past the end of a shorter sequence
+    const int qw0 = q0 + wave * 32;
+    const int myq = qw0 + l32;
+    const int64_t rs = (int64_t)H * D;
+    const int64_t base = sr.base;
+    const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + base;
+    const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + base;
+    const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + base;
+    const uint16_t* dOg = static_cast<const uint16_t*>(p.dout) + base;
+    const uint32_t rs2 = (uint32_t)(H * D * 2);
+    const BufRes rq = rows_bufres(Qg, q0, N, C::BQ, rs2), rdo = rows_bufres(dOg, q0, N, C::BQ, rs2);
+    const int64_t statoff = sr.stat;
+    const BufRes rl = make_bufres(p.lse + statoff, (uint32_t)N * 4);
+    const BufRes rd = make_bufres(p.dsum + statoff, (uint32_t)N * 4);
 
-  // This wave's share of the tile loads: K instructions, then V.
-  uint32_t dsrc[C::LPW];
-  int dlds[C::LPW];
-#pragma unroll
-  for (int m = 0; m < C::LPW; ++m) {
-    const int i = wave + NW * m;
-    int off = 0, row = 0, ch = 0;
-    if (i < KT::NLOAD) {
-      KT::load_slot(i, lane, off, row, ch);
-    } else if (i < C::NLOAD) {
-      VT::load_slot(i - KT::NLOAD, lane, off, row, ch);
-      off += KT::BYTES;
+    // Rows past N: zero Q, dO, LSE and D give dS = 0 (never stored anyway).
+    u32x4 qreg[C::NKC], doreg[C::NKC];
+  #pragma unroll
+    for (int c = 0; c < C::NKC; ++c) {
+      const uint32_t off = (uint32_t)(myq - q0) * rs2 + (16 * c + 8 * hf) * 2;
+      qreg[c] = buf_load_128(rq, off);
+      doreg[c] = buf_load_128(rdo, off);
     }
-    dsrc[m] = (uint32_t)row * rs2 + 16 * ch;
-    dlds[m] = off;
-  }
-  auto issue = [&](char* stage, uint32_t* bc, int k0) {
-    const BufRes rk = rows_bufres(Kg, k0, N, C::BK, rs2);
-    const BufRes rv = rows_bufres(Vg, k0, N, C::BK, rs2);
-#pragma unroll
+    const float lse2 = buf_load_f32(rl, (uint32_t)myq * 4) * kLog2e;
+    const float dq_d = buf_load_f32(rd, (uint32_t)myq * 4);
+    uint64_t kbh = 0;
+    uint32_t arow = 0;
+    if constexpr (DROP) {
+      kbh = head_key(p.seed, b, h, H);
+      arow = row_key(kbh, myq);
+    }
+
+    const int kend = CAUSAL ? min(N, q0 + C::BQ) : N;
+    int ntiles;
+    if constexpr (SPARSE) {
+      const int nb = (N + kSparseBlock - 1) / kSparseBlock;
+      const uint8_t* mrow = p.bmask + b * p.msb + h * p.msh + (int64_t)qb * nb;
+      const KeptBlocks kb =
+          collect_blocks(mrow, 1, 0, (kend + kSparseBlock - 1) / kSparseBlock, kept, lane, wave == 0);
+      ntiles = kept_tiles<C::BK>(kb, kend);
+      __syncthreads();
+    } else {
+      ntiles = (kend + C::BK - 1) / C::BK;
+    }
+    auto tile_start = [&](int t) {
+      if (rev) t = ntiles - 1 - t;
+      return SPARSE ? kept_tile_start<C::BK>(kept, t) : t * C::BK;
+    };
+
+    // This wave's share of the tile loads: K instructions, then V.
+    uint32_t dsrc[C::LPW];
+    int dlds[C::LPW];
+  #pragma unroll
     for (int m = 0; m < C::LPW; ++m) {
       const int i = wave + NW * m;
-      if (i < C::NLOAD) lds_dma_16(i < KT::NLOAD ? rk : rv, stage + dlds[m], dsrc[m]);
-    }
-    if constexpr (DROP) {
-      if (tid < C::BK / 2) bc[tid] = pair_key(kbh, (k0 >> 1) + tid);
-    }
-  };
-
-  Both32<D> ofs;
-  ofs.init(lane);
-  const int vx = hf ^ VT::sw(l32);
-  int vrow[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) vrow[u] = KT::BYTES + l32 * 128 + (((2 * u) ^ vx) << 4);
-  const int vrow_tail = KT::BYTES + VT::TAIL + l32 * 32 + ((hf ^ VT::swt(l32)) << 4);
-
-  f32x16 dqacc[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) dqacc[db] = f32x16{};
-  f32x16 negd;  // -D of this lane's query: start of the dP^T accumulator (no dropout)
-#pragma unroll
-  for (int r = 0; r < 16; ++r) negd[r] = -dq_d;
-
-  auto step = [&](const char* cur, const uint32_t* bcc, char* nxt, uint32_t* bcn, int t) {
-    wait_vmem();
-    __syncthreads();
-    if constexpr (kLdsPoison) poison_stage(nxt, C::STAGE, tid, C::NT);
-    const int k0 = tile_start(t);
-    if (t + 1 < ntiles) issue(nxt, bcn, tile_start(t + 1));
-    if (CAUSAL && k0 > qw0 + 31) return;
-    // Phase 1. S^T = K Q^T : lane = query, register r -> key k0 + c_row(r, hf).
-    f32x16 s = f32x16{};
-#pragma unroll
-    for (int c = 0; c < C::NKC; ++c) s = mfma32x32x16(ld_lds_128(cur, ofs.row_off(c)), qreg[c], s);
-    sched_lds_ahead<C::NKC, 1, 1>();
-    __builtin_amdgcn_sched_barrier(0);  // the later phases are ordered on their own
-    if ((k0 + C::BK > N) || (CAUSAL && k0 + C::BK - 1 > qw0)) {
-      // tail or diagonal tile: keys past N or after the query get exp2(-inf) = 0
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + c_row(r, hf);
-        s[r] = (key >= N || (CAUSAL && key > myq)) ? -INFINITY : s[r];
+      int off = 0, row = 0, ch = 0;
+      if (i < KT::NLOAD) {
+        KT::load_slot(i, lane, off, row, ch);
+      } else if (i < C::NLOAD) {
+        VT::load_slot(i - KT::NLOAD, lane, off, row, ch);
+        off += KT::BYTES;
       }
+      dsrc[m] = (uint32_t)row * rs2 + 16 * ch;
+      dlds[m] = off;
     }
-    // Phase 2. dP^T = V dO^T on the matrix cores while the vector ALUs form
-    // P^T; without dropout the accumulator starts at -D of this lane's query.
-    f32x16 dp = DROP ? f32x16{} : negd;
-#pragma unroll
-    for (int c = 0; c < C::NKC; ++c) {
-      const int vo = (2 * c < 8 * VT::NG) ? (c >> 2) * VT::GBYTES + vrow[c & 3] : vrow_tail;
-      dp = mfma32x32x16(ld_lds_128(cur, vo), doreg[c], dp);
-    }
-    float pv[16];
-    // Registers 4g + e hold keys 8g + 4hf + e; keys (e, e + 1), e = 0, 2, are
-    // a pair and share one dropout hash.
-    uint32_t yd[DROP ? 4 : 1][2];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    auto issue = [&](char* stage, uint32_t* bc, int k0) {
+      const BufRes rk = rows_bufres(Kg, k0, N, C::BK, rs2);
+      const BufRes rv = rows_bufres(Vg, k0, N, C::BK, rs2);
+  #pragma unroll
+      for (int m = 0; m < C::LPW; ++m) {
+        const int i = wave + NW * m;
+        if (i < C::NLOAD) lds_dma_16(i < KT::NLOAD ? rk : rv, stage + dlds[m], dsrc[m]);
+      }
       if constexpr (DROP) {
-        const u32x2 bc = *reinterpret_cast<const u32x2*>(bcc + 4 * g + 2 * hf);
-        yd[g][0] = pair_mix(arow, bc[0]);
-        yd[g][1] = pair_mix(arow, bc[1]);
+        if (tid < C::BK / 2) bc[tid] = pair_key(kbh, (k0 >> 1) + tid);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pv[4 * g + e] = exp2_hw(fmaf(s[4 * g + e], p.c2, -lse2));
-    }
-    // Phase 3. dS^T = P^T (dP^T - D) per 16-key step, and dQ^T += K^T dS^T.
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      float dsv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * kt + i, g = r >> 2, e = r & 3;
-        if constexpr (DROP) {
-          const uint32_t y = yd[DROP ? g : 0][e >> 1];
-          const bool kp = (e & 1) ? keep_odd(y, p.drop_t) : keep_even(y, p.drop_t);
-          dsv[i] = pv[r] * ((kp ? dp[r] * p.drop_r : 0.f) - dq_d);
-        } else {
-          dsv[i] = pv[r] * dp[r];
+    };
+
+    Both32<D> ofs;
+    ofs.init(lane);
+    const int vx = hf ^ VT::sw(l32);
+    int vrow[4];
+  #pragma unroll
+    for (int u = 0; u < 4; ++u) vrow[u] = KT::BYTES + l32 * 128 + (((2 * u) ^ vx) << 4);
+    const int vrow_tail = KT::BYTES + VT::TAIL + l32 * 32 + ((hf ^ VT::swt(l32)) << 4);
+
+    f32x16 dqacc[C::NDB];
+  #pragma unroll
+    for (int db = 0; db < C::NDB; ++db) dqacc[db] = f32x16{};
+    f32x16 negd;  // -D of this lane's query: start of the dP^T accumulator (no dropout)
+  #pragma unroll
+    for (int r = 0; r < 16; ++r) negd[r] = -dq_d;
+
+    auto step = [&](const char* cur, const uint32_t* bcc, char* nxt, uint32_t* bcn, int t) {
+      wait_vmem();
+      __syncthreads();
+      if constexpr (kLdsPoison) poison_stage(nxt, C::STAGE, tid, C::NT);
+      const int k0 = tile_start(t);
+      if (t + 1 < ntiles) issue(nxt, bcn, tile_start(t + 1));
+      if (CAUSAL && k0 > qw0 + 31) return;
+      // Phase 1. S^T = K Q^T : lane = query, register r -> key k0 + c_row(r, hf).
+      f32x16 s = f32x16{};
+  #pragma unroll
+      for (int c = 0; c < C::NKC; ++c) s = mfma32x32x16(ld_lds_128(cur, ofs.row_off(c)), qreg[c], s);
+      sched_lds_ahead<C::NKC, 1, 1>();
+      __builtin_amdgcn_sched_barrier(0);  // the later phases are ordered on their own
+      if ((k0 + C::BK > N) || (CAUSAL && k0 + C::BK - 1 > qw0)) {
+        // tail or diagonal tile: keys past N or after the query get exp2(-inf) = 0
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + c_row(r, hf);
+          s[r] = (key >= N || (CAUSAL && key > myq)) ? -INFINITY : s[r];
         }
       }
-      const u32x4 sop = {pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3]),
-                         pack_bf16x2(dsv[4], dsv[5]), pack_bf16x2(dsv[6], dsv[7])};
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-        dqacc[db] = mfma32x32x16(ofs.tr_frag(cur, db, kt), sop, dqacc[db]);
-    }
-    sched_dq_phases<C::NKC, C::NDB, DROP>();
-  };
-
-  if constexpr (kLdsPoison) poison_stage(st0, C::STAGE, tid, C::NT);
-  if (ntiles > 0) issue(st0, bc0, tile_start(0));
-  for (int t = 0; t < ntiles; t += 2) {
-    step(st0, bc0, st1, bc1, t);
-    if (t + 1 < ntiles) step(st1, bc1, st0, bc0, t + 1);
-  }
-
-  if (myq < N) {
-    uint16_t* dqrow = static_cast<uint16_t*>(p.dq) + base + (int64_t)myq * rs;
-    const float sc = p.scale;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
+      // Phase 2. dP^T = V dO^T on the matrix cores while the vector ALUs form
+      // P^T; without dropout the accumulator starts at -D of this lane's query.
+      f32x16 dp = DROP ? f32x16{} : negd;
+  #pragma unroll
+      for (int c = 0; c < C::NKC; ++c) {
+        const int vo = (2 * c < 8 * VT::NG) ? (c >> 2) * VT::GBYTES + vrow[c & 3] : vrow_tail;
+        dp = mfma32x32x16(ld_lds_128(cur, vo), doreg[c], dp);
+      }
+      float pv[16];
+      // Registers 4g + e hold keys 8g + 4hf + e; keys (e, e + 1), e = 0, 2, are
+      // a pair and share one dropout hash.
+      uint32_t yd[DROP ? 4 : 1][2];
+  #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = db * 32 + 8 * g + 4 * hf;
-        if (d0 < D) {
-          const u32x2 w = {pack_bf16x2(dqacc[db][4 * g] * sc, dqacc[db][4 * g + 1] * sc),
-                           pack_bf16x2(dqacc[db][4 * g + 2] * sc, dqacc[db][4 * g + 3] * sc)};
-          st_global_64(dqrow + d0, w);
+        if constexpr (DROP) {
+          const u32x2 bc = *reinterpret_cast<const u32x2*>(bcc + 4 * g + 2 * hf);
+          yd[g][0] = pair_mix(arow, bc[0]);
+          yd[g][1] = pair_mix(arow, bc[1]);
+        }
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) pv[4 * g + e] = exp2_hw(fmaf(s[4 * g + e], p.c2, -lse2));
+      }
+      // Phase 3. dS^T = P^T (dP^T - D) per 16-key step, and dQ^T += K^T dS^T.
+  #pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        float dsv[8];
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * kt + i, g = r >> 2, e = r & 3;
+          if constexpr (DROP) {
+            const uint32_t y = yd[DROP ? g : 0][e >> 1];
+            const bool kp = (e & 1) ? keep_odd(y, p.drop_t) : keep_even(y, p.drop_t);
+            dsv[i] = pv[r] * ((kp ? dp[r] * p.drop_r : 0.f) - dq_d);
+          } else {
+            dsv[i] = pv[r] * dp[r];
+          }
+        }
+        const u32x4 sop = {pack_bf16x2(dsv[0], dsv[1]), pack_bf16x2(dsv[2], dsv[3]),
+                           pack_bf16x2(dsv[4], dsv[5]), pack_bf16x2(dsv[6], dsv[7])};
+  #pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+          dqacc[db] = mfma32x32x16(ofs.tr_frag(cur, db, kt), sop, dqacc[db]);
+      }
+      sched_dq_phases<C::NKC, C::NDB, DROP>();
+    };
+
+    if constexpr (kLdsPoison) poison_stage(st0, C::STAGE, tid, C::NT);
+    if (ntiles > 0) issue(st0, bc0, tile_start(0));
+    for (int t = 0; t < ntiles; t += 2) {
+      step(st0, bc0, st1, bc1, t);
+      if (t + 1 < ntiles) step(st1, bc1, st0, bc0, t + 1);
+    }
+
+    if (myq < N) {
+      uint16_t* dqrow = static_cast<uint16_t*>(p.dq) + base + (int64_t)myq * rs;
+      const float sc = p.scale;
+  #pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = db * 32 + 8 * g + 4 * hf;
+          if (d0 < D) {
+            const u32x2 w = {pack_bf16x2(dqacc[db][4 * g] * sc, dqacc[db][4 * g + 1] * sc),
+                             pack_bf16x2(dqacc[db][4 * g + 2] * sc, dqacc[db][4 * g + 3] * sc)};
+            st_global_64(dqrow + d0, w);
+          }
         }
       }
     }
@@ -1173,12 +1203,21 @@ hipError_t launch_dq_ds(const BwdParams& prm, bool causal, bool drop, dim3 grid,
   // A block-mask row covers 128 queries: block-sparse runs keep four waves.
   if constexpr (!SPARSE) {
     if (prm.N >= 32768) {
-      const dim3 grid8((unsigned)((prm.N + 255) / 256 * prm.B * prm.H)), block8(512);
+      const int nq8 = (prm.N + 255) / 256;
+      const dim3 grid8((unsigned)(nq8 * prm.B * prm.H)), block8(512);
       if (causal) {
-        if (drop)
+        if (drop) {
           hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, true, true, false, 8>), grid8, block8, 0, s, prm);
-        else
-          hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, true, false, false, 8>), grid8, block8, 0, s, prm);
+        } else {
+          // Query block pairs per work-group (see the kernel). Measured at
+          // N = 32768, d = 80: 2.50 -> 0.93 GB fetched from beyond L2 per
+          // launch at the same time (3.700 / 3.704 ms); four-wave dQ at
+          // N = 8192 and the dropout kernels were slower paired.
+          BwdParams pp = prm;
+          pp.pair_blocks = prm.cu == nullptr;
+          const dim3 gridp((unsigned)((pp.pair_blocks ? (nq8 + 1) / 2 : nq8) * prm.B * prm.H));
+          hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, true, false, false, 8>), gridp, block8, 0, s, pp);
+        }
       } else {
         if (drop)
           hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, false, true, false, 8>), grid8, block8, 0, s, prm);
