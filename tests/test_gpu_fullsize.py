@@ -95,16 +95,18 @@ def test_full_size_whole_heads(cfg, heads):
         print(f"  head ({b},{h}) ok", flush=True)
 
 
-@pytest.mark.parametrize("d,causal", [(80, False), (64, True)])
-def test_long_sequence_wide_groups(d, causal):
+@pytest.mark.parametrize("d,causal,N", [(80, False, 32768), (64, True, 32768), (64, True, 32800)])
+def test_long_sequence_wide_groups(d, causal, N):
     """N = 32768 runs the sixteen-wave forward groups (head dims up to 80, no
-    dropout) and the eight-wave dQ groups. Shapes the workloads do not cover
-    (full mask at d = 80, causal at d = 64), at sampled rows and columns of
-    one head against the oracle."""
-    w = WORKLOADS[4].with_(H=2, d=d, causal=causal)
+    dropout) and the eight-wave dQ groups; causal ones pair their blocks
+    per work-group. Shapes the workloads do not cover (full mask at d = 80,
+    causal at d = 64, and N = 32800: odd block counts, 65 forward and 129
+    dQ blocks, with a ragged last block), at sampled rows and columns of one
+    head against the oracle."""
+    w = WORKLOADS[4].with_(H=2, d=d, causal=causal, N=N)
     inp = make_inputs(w, with_grad=True)
     dev = {k: to_device(v[0], w.dtype) for k, v in inp.items()}
-    print(f"N=32768 d={d} causal={causal}", flush=True)
+    print(f"N={N} d={d} causal={causal}", flush=True)
     args = (w.causal, 0.0, 0, w.scale)
     o, lse = fa.forward(dev["q"], dev["k"], dev["v"], *args)
     dq, dk, dv = fa.backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, *args)
