@@ -765,14 +765,22 @@ bool fwd_sixteen_waves(int N) {
 // of the online softmax's updates (results equal up to fp32 rounding order),
 // and which work-group computes which block changes no result. Measured: the
 // N = 32768 d = 80 forward fetches 0.52 GB per launch from beyond L2
-// instead of 2.19 GB, the N = 8192 d = 128 one 0.25 GB instead of 0.82.
+// instead of 2.19 GB (the N = 8192 d = 128 one 0.25 GB instead of 0.82,
+// but slower there, see below).
 // A packed batch pairs each sequence's own blocks (the resident pairing
 // across work-groups needs equal block counts and is not used there): the
 // 16-sequence batch of 512..8192 tokens runs 12% faster.
 template <auto Kernel>
 hipError_t launch_fwd_grid(int nblocks, int threads, bool causal, const FwdParams& prm, hipStream_t s) {
   const int BH = prm.B * prm.H;
-  const BlockPairing bp = plan_block_pairs<Kernel>(nblocks / BH, BH, threads, causal, prm.cu == nullptr);
+  // Pairs per work-group for packed batches and from N = 32768: measured
+  // inside the benchmark's full training step (forward after the previous
+  // step's backward), they made the N = 8192 d = 128 forward 3% slower
+  // (0.514 against 0.497 ms), the N = 32768 d = 80 one 2% faster, the
+  // N = 65536 dropout one no different, and the packed 16-sequence batch 6%
+  // faster.
+  const BlockPairing bp = plan_block_pairs<Kernel>(nblocks / BH, BH, threads, causal, prm.cu == nullptr,
+                                                   prm.cu != nullptr || prm.N >= 32768);
   FwdParams p = prm;
   p.pair_slots = bp.pair_slots;
   p.cus_per_xcd = bp.cus_per_xcd;

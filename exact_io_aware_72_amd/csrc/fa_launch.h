@@ -42,8 +42,9 @@ int resident_per_cu(int threads) {
 // - a grid that the device holds at once, as an even number of work-groups
 //   per CU: the work-groups of each CU take complementary blocks
 //   (pair_slots, map_block_pairs), so every CU gets equal work;
-// - a larger grid, when the paired grid still fills the device: each
-//   work-group takes a complementary pair (pair_blocks, map_block_pair),
+// - with group_mode, a larger grid, when the paired grid still fills the
+//   device: each work-group takes a complementary pair (pair_blocks,
+//   map_block_pair),
 //   one block over ascending tiles and the other over descending ones.
 //   Every work-group then does the same work, and at any moment the
 //   work-groups of one head read only two tiles of the streamed operands
@@ -57,7 +58,8 @@ struct BlockPairing {
 };
 
 template <auto Kernel>
-BlockPairing plan_block_pairs(int nblk, int BH, int threads, bool eligible, bool resident_mode) {
+BlockPairing plan_block_pairs(int nblk, int BH, int threads, bool eligible, bool resident_mode,
+                              bool group_mode) {
   BlockPairing r{nblk * BH, 0, 0, 0};
   if (!eligible) return r;
   const int ncu = device_cus();
@@ -69,7 +71,7 @@ BlockPairing plan_block_pairs(int nblk, int BH, int threads, bool eligible, bool
       r.pair_slots = n / ncu;
       r.cus_per_xcd = ncu / 8;
     }
-  } else if ((nblk + 1) / 2 * BH >= cap) {
+  } else if (group_mode && (nblk + 1) / 2 * BH >= cap) {
     r.pair_blocks = 1;
     r.grid = (nblk + 1) / 2 * BH;
   }

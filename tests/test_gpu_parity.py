@@ -102,12 +102,13 @@ def test_forward_resident_grid_pairs(w):
     assert_close("LSE", lse, lse_ref, w.dtype)
 
 
-# Causal grids larger than the device holds at once, whose paired grid still
-# fills it: each work-group takes blocks (nqb - 1 - j, j), the second over
-# descending key tiles. Four-wave groups at d = 128 (two per CU), d = 64
-# (four per CU) and d = 80, with dropout, and with an odd block count, a
-# ragged tail and a head count that is not a multiple of 8 (the
-# non-XCD-aware mapping).
+# Causal grids several times larger than the device holds at once (one
+# block per work-group, heaviest first, at these lengths; block pairs per
+# work-group, taken from N = 32768 and by packed batches, are checked in
+# test_gpu_fullsize.py and test_gpu_varlen.py). Four-wave groups at d = 128
+# (two per CU), d = 64 (four per CU) and d = 80, with dropout, and with an
+# odd block count, a ragged tail and a head count that is not a multiple of
+# 8 (the non-XCD-aware mapping).
 SWEEP_PAIR_CASES = [
     _case(3, B=2, H=64, N=1024),
     _case(2, B=4, H=64, N=1024),
@@ -118,7 +119,7 @@ SWEEP_PAIR_CASES = [
 
 
 @pytest.mark.parametrize("w", SWEEP_PAIR_CASES, ids=_ids(SWEEP_PAIR_CASES))
-def test_forward_block_pairs_per_group(w):
+def test_forward_large_causal_grids(w):
     inp = make_inputs(w, with_grad=False)
     dev, val = device_inputs(inp, w.dtype)
     o, lse = _run_fwd(dev, w)
@@ -128,10 +129,9 @@ def test_forward_block_pairs_per_group(w):
     assert_close("LSE", lse, lse_ref, w.dtype)
 
 
-def test_eight_wave_block_pairs_heads():
+def test_eight_wave_large_grid_heads():
     """Eight-wave forward groups (d = 80, N = 8192) over a grid twice the
-    device's: paired blocks per group. Three whole heads, on different XCDs,
-    against the oracle."""
+    device's. Three whole heads, on different XCDs, against the oracle."""
     w = _case(4, B=1, H=32, N=8192)
     inp = make_inputs(w, with_grad=False)
     dev, val = device_inputs(inp, w.dtype)
