@@ -35,6 +35,10 @@ Definitions followed ("FlashAttention for Efficient Training" unless noted):
         dP~ = dO V^T,  dP = dP~ * Z / (1 - p),  D_i = sum_j P_ij dP_ij,
         dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
     D_i also equals sum_c dO_ic O_ic; both are computed and must agree.
+    A recompute backward that is handed the forward's output reads D from
+    that stored O, not from P * dP; with backward(..., o=stored), D_i is
+    sum_c dO_ic o_ic of the given o, and dQ, dK (linear in D) are what that
+    backward computes exactly. dV does not depend on D.
     (The explicit dQ formulas printed in sections 2.1, 2.2, 4.1 and 5.1 of
     that page drop the D term and the K factor and are not used.)
 
@@ -140,9 +144,10 @@ def head_forward(qh, kh, vh, scale, causal, dropout_p, seed, b, h, H, panel=_PAN
 
 
 def head_backward(qh, kh, vh, doh, scale, causal, dropout_p, seed, b, h, H, panel=_PANEL,
-                  check_d=True, bmask=None):
+                  check_d=True, bmask=None, oh=None):
     """One head of one sequence ([n, d] float64 arrays). Returns
-    (dQ, dK, dV, D) with D = rowsum(P * dP) of length n."""
+    (dQ, dK, dV, D) with D = rowsum(P * dP) of length n, or, with a given
+    output oh [n, d], D = rowsum(dO * oh)."""
     n = qh.shape[0]
     dq = np.zeros_like(qh)
     dk = np.zeros_like(kh)
@@ -168,7 +173,9 @@ def head_backward(qh, kh, vh, doh, scale, causal, dropout_p, seed, b, h, H, pane
         dpt = doh[r0:r1] @ vh[:nc].T
         dp = dpt * z * keep_r if z is not None else dpt
         d_row = np.sum(p * dp, axis=1)
-        if check_d:
+        if oh is not None:
+            d_row = np.sum(doh[r0:r1] * oh[r0:r1], axis=1)
+        elif check_d:
             o_rows = pt @ vh[:nc]
             d_alt = np.sum(doh[r0:r1] * o_rows, axis=1)
             if not np.allclose(d_row, d_alt, rtol=1e-9, atol=1e-9):
@@ -220,10 +227,12 @@ def forward_cross(q, k, v, scale, causal, panel=_PANEL):
 
 
 def backward(q, k, v, do, scale, causal, dropout_p=0.0, seed=0, heads=None, panel=_PANEL,
-             check_d=True, block_mask=None):
+             check_d=True, block_mask=None, o=None):
     """Returns (dQ, dK, dV, D) for L = sum(dO * O), float64.
     D is [B,H,N] = rowsum(P * dP). With check_d, also checks D against
-    rowsum(dO * O) computed from this module's own forward output."""
+    rowsum(dO * O) computed from this module's own forward output. With o
+    ([B,N,H,d], e.g. the forward output as stored in a narrower type), D is
+    rowsum(dO * o) instead and the check is skipped."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -233,11 +242,13 @@ def backward(q, k, v, do, scale, causal, dropout_p=0.0, seed=0, heads=None, pane
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     dd = np.zeros((B, H, N), np.float64)
+    o = None if o is None else np.asarray(o, np.float64)
     for b, h in _heads(B, H, heads):
         dq[b, :, h, :], dk[b, :, h, :], dv[b, :, h, :], dd[b, h, :] = head_backward(
             q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], do[b, :, h, :], scale, causal,
             dropout_p, seed, b, h, H, panel, check_d,
-            None if block_mask is None else block_mask[b][h])
+            None if block_mask is None else block_mask[b][h],
+            None if o is None else o[b, :, h, :])
     return dq, dk, dv, dd
 
 

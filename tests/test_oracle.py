@@ -113,6 +113,72 @@ def test_finite_difference_gradients(causal, p_drop):
 
 
 # --------------------------------------------------------------------------
+# Pin: D read from a given (stored) forward output. D moves by
+# dD_i = rowsum(dO_i * (o_i - O_i)); since dLSE_i/dS_ij = P_ij, dQ and dK
+# become the gradients of sum(dO * O) - sum_i dD_i LSE_i with dD held fixed,
+# and dV is unchanged. Finite differences of the forward check all three.
+def _num_grad(loss, args, name, step=1e-6):
+    x = args[name]
+    num = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        idx = it.multi_index
+        vals = []
+        for sgn in (1, -1):
+            xs = x.copy()
+            xs[idx] += sgn * step
+            vals.append(loss(**{**args, name: xs}))
+        num[idx] = (vals[0] - vals[1]) / (2 * step)
+    return num
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("p_drop", [0.0, 0.1])
+def test_given_output_gradients_by_finite_differences(causal, p_drop):
+    rng = np.random.default_rng(321)
+    B, N, H, d = 1, 10, 2, 3
+    q, k, v, do = (rng.standard_normal((B, N, H, d)) for _ in range(4))
+    scale, seed = 0.7, 99
+    o_exact, _ = oracle.forward(q, k, v, scale, causal, p_drop, seed)
+    o_given = o_exact + 0.05 * rng.standard_normal(o_exact.shape)
+    shift = np.einsum("bnhd,bnhd->bhn", do, o_given - o_exact)
+    dq, dk, dv, _ = oracle.backward(q, k, v, do, scale, causal, p_drop, seed, o=o_given)
+
+    def loss(q, k, v):
+        o, lse = oracle.forward(q, k, v, scale, causal, p_drop, seed)
+        return float(np.sum(do * o) - np.sum(shift * lse))
+
+    args = {"q": q, "k": k, "v": v}
+    for name, g in (("q", dq), ("k", dk), ("v", dv)):
+        num = _num_grad(loss, args, name)
+        err = np.max(np.abs(num - g)) / max(np.max(np.abs(g)), 1e-30)
+        assert err <= 1e-6, (name, err)
+    # and the move is not zero: the given output does change dQ and dK
+    dq0, dk0, dv0, _ = oracle.backward(q, k, v, do, scale, causal, p_drop, seed)
+    assert np.max(np.abs(dq - dq0)) > 1e-3 and np.max(np.abs(dk - dk0)) > 1e-3
+    assert np.max(np.abs(dv - dv0)) == 0.0
+
+
+def test_given_output_single_key_and_exact_output():
+    # one key: P = 1 and dP = dO . V, so dS = -dO . (o - V)
+    q, k, v, do = (_rand(2, 1, 3, 5) for _ in range(4))
+    e = 0.1 * _rand(2, 1, 3, 5)
+    scale = 0.4
+    dq, dk, dv, _ = oracle.backward(q, k, v, do, scale, True, o=v + e)
+    ds = -np.sum(do * e, axis=3, keepdims=True)
+    assert np.max(np.abs(dq - scale * ds * k)) <= 1e-14
+    assert np.max(np.abs(dk - scale * ds * q)) <= 1e-14
+    assert np.array_equal(dv, do)
+    # the exact output gives the default gradients
+    q, k, v, do = (_rand(1, 40, 2, 6) for _ in range(4))
+    o, _ = oracle.forward(q, k, v, 0.5, True, 0.2, 5)
+    a = oracle.backward(q, k, v, do, 0.5, True, 0.2, 5)
+    b = oracle.backward(q, k, v, do, 0.5, True, 0.2, 5, o=o)
+    for x, y in zip(a, b):
+        assert np.max(np.abs(x - y)) <= 1e-12
+
+
+# --------------------------------------------------------------------------
 # Closed forms and special cases.
 @pytest.mark.parametrize("causal", [False, True])
 def test_zero_query_gives_uniform_attention(causal):
