@@ -28,6 +28,7 @@ from .attention import (  # noqa: F401
     forward,
     forward_cross,
     head_forward,
+    head_backward,
     backward,
     sampled_head,
 )

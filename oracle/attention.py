@@ -144,10 +144,14 @@ def head_forward(qh, kh, vh, scale, causal, dropout_p, seed, b, h, H, panel=_PAN
 
 
 def head_backward(qh, kh, vh, doh, scale, causal, dropout_p, seed, b, h, H, panel=_PANEL,
-                  check_d=True, bmask=None, oh=None):
-    """One head of one sequence ([n, d] float64 arrays). Returns
-    (dQ, dK, dV, D) with D = rowsum(P * dP) of length n, or, with a given
-    output oh [n, d], D = rowsum(dO * oh)."""
+                  check_d=True, bmask=None, oh=None, row_offset=0, hash_row_offset=0):
+    """One head of one sequence (qh, doh [n, d], kh, vh [m, d] float64
+    arrays). Returns (dQ, dK, dV, D) with D = rowsum(P * dP) of length n, or,
+    with a given output oh [n, d], D = rowsum(dO * oh). Query i sits at key
+    position row_offset + i and is row hash_row_offset + i of the dropout
+    hash and the block mask, as in head_forward: a panel of rows cut from a
+    larger problem gets its own rows of dQ and D exactly, and those rows'
+    share of dK and dV."""
     n = qh.shape[0]
     dq = np.zeros_like(qh)
     dk = np.zeros_like(kh)
@@ -156,10 +160,10 @@ def head_backward(qh, kh, vh, doh, scale, causal, dropout_p, seed, b, h, H, pane
     keep_r = 1.0 / (1.0 - float(np.float32(dropout_p)))
     for r0 in range(0, n, panel):
         r1 = min(r0 + panel, n)
-        rows = np.arange(r0, r1)
-        nc = _panel_cols(causal, r1, kh.shape[0])
+        rows = np.arange(hash_row_offset + r0, hash_row_offset + r1)
+        nc = _panel_cols(causal, row_offset + r1, kh.shape[0])
         cols = np.arange(nc)
-        s = attention_scores(qh[r0:r1], kh[:nc], scale, causal, r0)
+        s = attention_scores(qh[r0:r1], kh[:nc], scale, causal, row_offset + r0)
         s = apply_block_mask(s, bmask, rows, cols)
         _, _, l_ = softmax_stats(s)
         p = attention_probs(s, l_)

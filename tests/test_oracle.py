@@ -315,6 +315,30 @@ def test_row_panel_with_offsets_matches_full(causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_backward_row_panels_with_offsets_match_full(causal):
+    """The backward over row panels computed alone: each panel's dQ and D are
+    those rows of the whole problem, and the panels' shares of dK and dV add
+    up to the whole dK and dV (dropout included)."""
+    B, N, H, d = 1, 50, 2, 4
+    q, k, v, do = (_rand(B, N, H, d) for _ in range(4))
+    scale, p_drop, seed = 0.5, 0.3, 21
+    dq, dk, dv, dd = oracle.backward(q, k, v, do, scale, causal, p_drop, seed)
+    for h in range(H):
+        sk = np.zeros((N, d))
+        sv = np.zeros((N, d))
+        for r0, r1 in ((0, 7), (7, 29), (29, 44), (44, 50)):
+            pq, pk, pv, pd = oracle.head_backward(q[0, r0:r1, h], k[0, :, h], v[0, :, h], do[0, r0:r1, h],
+                                                  scale, causal, p_drop, seed, 0, h, H,
+                                                  row_offset=r0, hash_row_offset=r0)
+            assert np.max(np.abs(pq - dq[0, r0:r1, h])) <= 1e-12
+            assert np.max(np.abs(pd - dd[0, h, r0:r1])) <= 1e-12
+            sk += pk
+            sv += pv
+        assert np.max(np.abs(sk - dk[0, :, h])) <= 1e-12
+        assert np.max(np.abs(sv - dv[0, :, h])) <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("p_drop", [0.0, 0.15])
 def test_sampled_head_matches_full(causal, p_drop):
     B, N, H, d = 2, 45, 3, 5
