@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from helpers import assert_close
-from oracle import attention as A
+import oracle
 from workloads import device_normal
 
 torch = pytest.importorskip("torch")
@@ -29,22 +29,26 @@ def _need_gpu():
 
 
 def _rows_reference(q, k, v, do, h, rows, scale):
-    """O, LSE and (with do) dQ of the given causal rows of head h, row by row."""
-    qh, kh, vh = (x[0, :, h].to(torch.float64).cpu().numpy() for x in (q, k, v))
-    doh = None if do is None else do[0, :, h].to(torch.float64).cpu().numpy()
+    """O, LSE and (with do) dQ of the given causal rows of head h: each row
+    alone through the oracle (query at key position r, keys 0..r), which is
+    exact because a causal row's softmax, O, D and dQ involve only its own
+    row of S."""
+    qh, kh, vh = (x[0, :, h] for x in (q, k, v))
+    H = q.shape[2]
     o_r, l_r, dq_r = [], [], []
-    for r in rows:
-        s = A.attention_scores(qh[r:r + 1], kh[:r + 1], scale, True, r)
-        _, _, l_ = A.softmax_stats(s)
-        p = A.attention_probs(s, l_)
-        o_row = p @ vh[:r + 1]
-        o_r.append(o_row[0])
+    for r in (int(x) for x in rows):
+        qr = qh[r:r + 1].to(torch.float64).cpu().numpy()
+        kr = kh[:r + 1].to(torch.float64).cpu().numpy()
+        vr = vh[:r + 1].to(torch.float64).cpu().numpy()
+        o_, l_ = oracle.head_forward(qr, kr, vr, scale, True, 0.0, 0, 0, h, H, row_offset=r, hash_row_offset=r)
+        o_r.append(o_[0])
         l_r.append(l_[0])
-        if doh is not None:
-            d_row = np.sum(doh[r] * o_row[0])
-            dp = doh[r:r + 1] @ vh[:r + 1].T
-            dq_r.append((scale * (p * (dp - d_row)) @ kh[:r + 1])[0])
-    return np.array(o_r), np.array(l_r), (np.array(dq_r) if doh is not None else None)
+        if do is not None:
+            dor = do[0, r:r + 1, h].to(torch.float64).cpu().numpy()
+            dq_, _, _, _ = oracle.head_backward(qr, kr, vr, dor, scale, True, 0.0, 0, 0, h, H,
+                                                row_offset=r, hash_row_offset=r)
+            dq_r.append(dq_[0])
+    return np.array(o_r), np.array(l_r), (np.array(dq_r) if do is not None else None)
 
 
 def test_bf16_item_over_4gib_sampled_rows_and_invariants():

@@ -190,13 +190,16 @@ def test_backward_matches_oracle(w):
     assert_close("dV", dv, dv_r, w.dtype)
 
 
-def test_preprocess_matches_definition():
+def test_preprocess_matches_oracle():
+    # The preprocess reads O as stored; it is handed the oracle's O in bf16,
+    # and the oracle's backward reads D from that same O.
     w = _case(3, B=2, H=3, N=77)
     inp = make_inputs(w, with_grad=True)
     dev, val = device_inputs(inp, w.dtype)
-    o, _ = fa.forward(dev["q"], dev["k"], dev["v"], w.causal, 0.0, 0, w.scale)
-    dd = to_host(fa.backward_preprocess(o, dev["do"]))
-    ref = np.einsum("bnhd,bnhd->bhn", to_host(o), val["do"])
+    o_r, _ = oracle.forward(val["q"], val["k"], val["v"], w.scale, w.causal)
+    o_st = torch.from_numpy(o_r).to(torch.bfloat16).cuda()
+    dd = to_host(fa.backward_preprocess(o_st, dev["do"]))
+    ref = oracle.backward(val["q"], val["k"], val["v"], val["do"], w.scale, w.causal, o=to_host(o_st))[3]
     assert np.max(np.abs(dd - ref)) <= 1e-4 * max(1.0, np.max(np.abs(ref)))
 
 
