@@ -541,6 +541,112 @@ def cpu_baseline(w, seconds, gpu_out=None):
         }
     return res
 
+# Power and clock sampler for --power-sample: a separate process, started
+# before this process touches the GPU, that reads the power cap once
+# (`rocm-smi --showmaxpower`), then polls `amd-smi metric` (socket power,
+# shader clock of each XCD) and appends "time power_w mean_clock_mhz" lines
+# to a file until a stop file appears.
+_SAMPLER = r"""
+import json, os, subprocess, sys, time
+out, stop = sys.argv[1], sys.argv[2]
+def smi(tool, args):
+    try:
+        r = subprocess.run([tool] + args, capture_output=True, text=True, timeout=20)
+        return json.loads(r.stdout) if r.returncode == 0 else None
+    except Exception:
+        return None
+with open(out, "w") as f:
+    cap = smi("rocm-smi", ["--showmaxpower", "--json"]) or {}
+    lim = {k: float(v) for c in cap.values() if isinstance(c, dict) for k, v in c.items()
+           if "power" in k.lower() and v.replace(".", "", 1).isdigit()}
+    f.write("#limits " + json.dumps(lim) + "\n")
+    f.flush()
+    while not os.path.exists(stop):
+        t = time.time()
+        m = smi("amd-smi", ["metric", "-g", "0", "-p", "-c", "--json"])
+        try:
+            g = m["gpu_data"][0]
+            pw = float(g["power"]["socket_power"]["value"])
+            clk = [float(v["clk"]["value"]) for k, v in g["clock"].items() if k.startswith("gfx_")]
+            f.write(f"{(t + time.time()) / 2:.3f} {pw:.1f} {sum(clk) / len(clk):.1f}\n")
+            f.flush()
+        except Exception:
+            time.sleep(0.5)
+        time.sleep(0.05)
+"""
+
+
+def power_sample_leg(seconds, sampler, torch, fa):
+    """Socket power and shader clock (amd-smi, sampled by a separate
+    process) while the headline step runs back to back for `seconds` on its
+    random inputs and then on constant inputs (every element of Q, K, V and
+    dO equal to 1), after an idle interval. Returns one dict per phase."""
+    proc, out, stop = sampler
+    t_wait = time.time()
+    while time.time() - t_wait < 60:  # first sample (amd-smi starts slowly)
+        with open(out) as f:
+            if any(not ln.startswith("#") for ln in f):
+                break
+        time.sleep(0.2)
+    w = WORKLOADS[3]
+    dev = _device_inputs(w, torch)
+    ones = {k: torch.ones_like(v) for k, v in dev.items()}
+    o = torch.empty_like(dev["q"])
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = (torch.empty_like(dev["q"]) for _ in range(3))
+    args = (w.causal, w.dropout_p, w.dropout_seed, w.scale)
+    fwd_f, bwd_f = counted_flops(w.B, w.H, w.N, w.d, w.causal, True)
+
+    def step(x):
+        fa.forward(x["q"], x["k"], x["v"], *args, out=o, lse=lse)
+        fa.backward(x["q"], x["k"], x["v"], o, x["do"], lse, *args, dq=dq, dk=dk, dv=dv)
+
+    phases = []
+    torch.cuda.synchronize()
+    t0 = time.time()
+    time.sleep(min(5.0, seconds / 2))
+    phases.append({"phase": "idle", "t0": t0, "t1": time.time(), "steps": 0})
+    for name, x in (("random inputs", dev), ("constant inputs", ones)):
+        for _ in range(20):
+            step(x)
+        torch.cuda.synchronize()
+        t0 = time.time()
+        n = 0
+        while time.time() - t0 < seconds:
+            for _ in range(50):
+                step(x)
+            torch.cuda.synchronize()
+            n += 50
+        t1 = time.time()
+        print(f"power leg: {name}: {n} steps in {t1 - t0:.1f} s", file=sys.stderr, flush=True)
+        phases.append({"phase": name, "t0": t0, "t1": t1, "steps": n})
+    with open(stop, "w"):
+        pass
+    proc.wait(timeout=60)
+    limits, samples = {}, []
+    with open(out) as f:
+        for ln in f:
+            if ln.startswith("#limits "):
+                limits = json.loads(ln[len("#limits "):])
+            elif ln.strip():
+                t, pw, clk = (float(x) for x in ln.split())
+                samples.append((t, pw, clk))
+    res = []
+    for ph in phases:
+        # skip the first second of each phase (clock and power settle)
+        sel = [(pw, clk) for t, pw, clk in samples if ph["t0"] + 1.0 <= t <= ph["t1"]]
+        d = {"phase": ph["phase"], "seconds": round(ph["t1"] - ph["t0"], 2), "samples": len(sel),
+             "socket_power_w": float(np.median([p for p, _ in sel])) if sel else None,
+             "gfx_clock_mhz": float(np.median([c for _, c in sel])) if sel else None}
+        if ph["steps"]:
+            ms = (ph["t1"] - ph["t0"]) * 1e3 / ph["steps"]
+            d.update({"steps": ph["steps"], "ms_per_step": ms, "tflops": (fwd_f + bwd_f) / (ms * 1e-3) / 1e12})
+        res.append(d)
+    return {"power_sample": {"workload": w.name, "phases": res, "power_limits_w": limits,
+                             "source": "amd-smi metric (socket power, mean GFX clock over the XCDs), "
+                                       "medians over each phase after its first second"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -557,7 +663,20 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes (three times), "
                          "the reference kernel for scaling HBM traffic counters, and exit")
+    ap.add_argument("--power-sample", type=float, default=0.0, metavar="SECONDS",
+                    help="only run the headline step back to back for SECONDS on random and then on "
+                         "constant inputs while a separate process samples socket power and shader "
+                         "clock with amd-smi, print one JSON line, and exit")
     a = ap.parse_args()
+    sampler = None
+    if a.power_sample:
+        # Started before anything here touches the GPU.
+        import subprocess
+        import tempfile
+        tmp = tempfile.mkdtemp(prefix="fa_power_")
+        out, stop = os.path.join(tmp, "samples.txt"), os.path.join(tmp, "stop")
+        open(out, "w").close()
+        sampler = (subprocess.Popen([sys.executable, "-c", _SAMPLER, out, stop]), out, stop)
     if a.gpus != 1:
         print("bench.py measures one GPU: the attention kernels run on a single device and this build "
               "has no multi-GPU path (heads or sequence chunks would be sharded across GPUs); "
@@ -571,6 +690,10 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     fa.lib()  # fails loudly if the HIP library is missing
+
+    if sampler is not None:
+        print(json.dumps(power_sample_leg(a.power_sample, sampler, torch, fa)), flush=True)
+        return
 
     if a.copy_calibration:
         n = a.copy_calibration << 20
