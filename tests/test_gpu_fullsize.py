@@ -64,13 +64,30 @@ def test_full_size_sampled_parity(cfg):
             assert_close(f"dV[{b},{h}]", to_host(dv[b, cols, h]), g[f"h{hi}_dv"], w.dtype)
 
 
-@pytest.mark.parametrize("cfg,heads", [(4, [(0, 0), (0, 9)]), (5, [(0, 3)])])
+def test_full_size_forward_whole_tensor_n2048():
+    """The B = 4, H = 16, N = 2048, d = 64 causal forward, whole: every row of
+    O and LSE of all 64 heads from the full-size launch against the oracle,
+    element by element, the mean bar taken over the whole tensor."""
+    w = WORKLOADS[2]
+    inp = make_inputs(w)
+    dev = {k: to_device(v[0], w.dtype) for k, v in inp.items()}
+    print(f"config 2: {w.name}", flush=True)
+    o, lse = fa.forward(dev["q"], dev["k"], dev["v"], w.causal, w.dropout_p, w.dropout_seed, w.scale)
+    torch.cuda.synchronize()
+    val = {k: v[1] for k, v in inp.items()}
+    ro, rl = oracle.forward(val["q"], val["k"], val["v"], w.scale, w.causal, w.dropout_p, w.dropout_seed)
+    assert_close("O", to_host(o), ro, w.dtype)
+    assert_close("LSE", to_host(lse), rl, w.dtype)
+
+
+@pytest.mark.parametrize("cfg,heads", [(3, [(0, 0), (1, 15)]), (4, [(0, 0), (0, 9)]), (5, [(0, 3)])])
 def test_full_size_whole_heads(cfg, heads):
-    """Whole heads of the N = 32768 (d = 80) and N = 65536 (dropout 0.1)
-    workloads, element by element at the bar: every row of O, LSE and dQ and
-    every key row of dK and dV, from the full-size launches, against the
-    oracle run on those heads (about 10 s per head at N = 32768 and 50 s at
-    N = 65536 on 16 host cores)."""
+    """Whole heads of the N = 8192 (d = 128), N = 32768 (d = 80) and
+    N = 65536 (dropout 0.1) workloads, element by element at the bar: every
+    row of O, LSE and dQ and every key row of dK and dV, from the full-size
+    launches, against the oracle run on those heads (a few seconds per head
+    at N = 8192, about 10 s at N = 32768 and 50 s at N = 65536 on 16 host
+    cores)."""
     w = WORKLOADS[cfg]
     inp = make_inputs(w, with_grad=True)
     dev = {k: to_device(v[0], w.dtype) for k, v in inp.items()}
