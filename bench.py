@@ -81,7 +81,7 @@ class ClockStamps:
 
     MIN_REGION_MS = 2.0
 
-    def __init__(self, torch, blocks=8):
+    def __init__(self, torch, blocks=64):
         import ctypes
         self.torch = torch
         self.blocks = blocks
@@ -93,7 +93,7 @@ class ClockStamps:
             self.lib.fa_clock_stamp.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
         except OSError as e:
             self.lib, self.error = None, f"{path}: {e}"
-        self.bufs = [torch.zeros(3 * blocks, dtype=torch.int64, device="cuda") for _ in range(2)]
+        self.bufs = [torch.zeros(4 * blocks, dtype=torch.int64, device="cuda") for _ in range(2)]
         self._ctypes = ctypes
 
     def stamp(self, i):
@@ -107,12 +107,18 @@ class ClockStamps:
         """Call after synchronising."""
         if self.lib is None or self.error:
             return {"mhz": None, "error": self.error}
-        a, b = (x.cpu().numpy().reshape(-1, 3).astype(np.int64) for x in self.bufs)
-        per = {}
+        a, b = (x.cpu().numpy().reshape(-1, 4).astype(np.int64) for x in self.bufs)
+        # Stamps of the two sides taken on the same CU (XCD and HW_ID CU
+        # fields): each XCD's reading is the median over its matched CUs.
+        end = {}
+        for r1 in b:
+            end.setdefault((int(r1[0]), int(r1[3])), r1)
+        pairs = {}
         for r0 in a:
-            for r1 in b:
-                if r1[0] == r0[0] and int(r0[0]) not in per and r1[2] > r0[2]:
-                    per[int(r0[0])] = 100.0 * float(r1[1] - r0[1]) / float(r1[2] - r0[2])
+            r1 = end.get((int(r0[0]), int(r0[3])))
+            if r1 is not None and r1[2] > r0[2]:
+                pairs.setdefault(int(r0[0]), []).append(100.0 * float(r1[1] - r0[1]) / float(r1[2] - r0[2]))
+        per = {x: float(np.median(v)) for x, v in sorted(pairs.items())}
         region_ms = float(np.median([(r1[2] - r0[2]) / 1e5 for r0, r1 in zip(a, b)]))
         # An XCD that idles between the stamps can stop or reset its cycle
         # counter (seen on sub-millisecond regions), so short regions are not
@@ -121,12 +127,15 @@ class ClockStamps:
         if region_ms < self.MIN_REGION_MS:
             return {"mhz": None, "per_xcd_mhz": per, "region_ms": region_ms,
                     "error": f"timed region shorter than {self.MIN_REGION_MS} ms"}
-        ok = [v for v in per.values() if 100.0 < v < 2450.0]
+        ok = {x: v for x, v in per.items() if 100.0 < v < 2450.0}
+        bad = {x: v for x, v in per.items() if x not in ok}
         if not ok:
             return {"mhz": None, "per_xcd_mhz": per, "error": "no plausible per-XCD reading"}
-        return {"mhz": float(np.median(ok)), "per_xcd_mhz": per, "xcds_used": len(ok),
-                "source": "s_memtime cycles / s_memrealtime (100 MHz) ticks per XCD between "
-                          "stamps enqueued before the first and after the last timed step",
+        return {"mhz": float(np.median(list(ok.values()))), "per_xcd_mhz": ok, "xcds_used": len(ok),
+                "excluded_xcd_readings": bad,
+                "source": "s_memtime cycles / s_memrealtime (100 MHz) ticks between stamps enqueued "
+                          "before the first and after the last timed step, matched by XCD and CU; "
+                          "median over each XCD's CUs, then over the XCDs",
                 "region_ms": region_ms}
 
 
