@@ -44,12 +44,15 @@ def forward_varlen(q, k, v, cu_seqlens, scale, causal, dropout_p=0.0, seed=0):
     return o, lse
 
 
-def backward_varlen(q, k, v, do, cu_seqlens, scale, causal, dropout_p=0.0, seed=0):
-    """Returns (dQ, dK, dV [total, H, d], D [H, total]) for L = sum(dO * O)."""
+def backward_varlen(q, k, v, do, cu_seqlens, scale, causal, dropout_p=0.0, seed=0, o=None):
+    """Returns (dQ, dK, dV [total, H, d], D [H, total]) for L = sum(dO * O).
+    With o ([total, H, d], the forward output as a backward is handed it), D
+    is rowsum(dO * o), as in attention.backward."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     do = np.asarray(do, np.float64)
+    o = None if o is None else np.asarray(o, np.float64)
     total, H, _ = q.shape
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
@@ -61,5 +64,5 @@ def backward_varlen(q, k, v, do, cu_seqlens, scale, causal, dropout_p=0.0, seed=
         for h in range(H):
             dq[a:e, h], dk[a:e, h], dv[a:e, h], dd[h, a:e] = head_backward(
                 q[a:e, h], k[a:e, h], v[a:e, h], do[a:e, h], scale, causal, dropout_p, seed, s, h,
-                H)
+                H, oh=None if o is None else o[a:e, h])
     return dq, dk, dv, dd

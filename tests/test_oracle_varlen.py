@@ -173,6 +173,38 @@ def test_finite_difference_gradients_packed(causal, p_drop):
 
 # --------------------------------------------------------------------------
 # The packed-batch input recipe.
+@pytest.mark.parametrize("p_drop", [0.0, 0.2])
+def test_given_output_per_sequence(p_drop):
+    """backward_varlen(o=...) reads D from the given output: with the varlen
+    oracle's own O it returns the default gradients, and with a perturbed O
+    each sequence's gradients are the dense oracle's on that sequence alone
+    (batch slot = sequence index) with the same O."""
+    lengths = [5, 0, 13, 1, 8]
+    H, d = 2, 4
+    cu, q, k, v, do = _packed(lengths, H, d, 77)
+    scale, seed = 0.6, 9
+    o, _ = V.forward_varlen(q, k, v, cu, scale, True, p_drop, seed)
+    ref = V.backward_varlen(q, k, v, do, cu, scale, True, p_drop, seed)
+    same = V.backward_varlen(q, k, v, do, cu, scale, True, p_drop, seed, o=o)
+    for x, y in zip(ref, same):
+        assert np.max(np.abs(x - y)) <= 1e-12
+    og = o + 0.05 * np.random.default_rng(5).standard_normal(o.shape)
+    got = V.backward_varlen(q, k, v, do, cu, scale, True, p_drop, seed, o=og)
+    B = len(lengths)
+    for s, (a, e) in enumerate(zip(cu[:-1], cu[1:])):
+        if e == a:
+            continue
+        n = e - a
+        pad = lambda x: np.zeros((B, n) + x.shape[1:])  # noqa: E731
+        qq, kk, vv, dd, oo = (pad(x) for x in (q, k, v, do, og))
+        for x, src in ((qq, q), (kk, k), (vv, v), (dd, do), (oo, og)):
+            x[s] = src[a:e]
+        dq, dk, dv, _ = oracle.backward(qq, kk, vv, dd, scale, True, p_drop, seed, heads=[(s, h) for h in range(H)],
+                                        o=oo)
+        for name, full, part in (("dQ", got[0], dq), ("dK", got[1], dk), ("dV", got[2], dv)):
+            assert np.max(np.abs(full[a:e] - part[s])) <= 1e-12, (name, s)
+
+
 def test_varlen_inputs_recipe():
     w = VarlenWorkload("t", 5, 2, 64, "bf16", True, 0.0, min_len=1, max_len=40, seed=4)
     cu, inp = make_varlen_inputs(w)
