@@ -108,3 +108,40 @@ def test_fp8_scores_stay_close_to_exact():
     o, lse = fp8.forward_fp8(q, k, v, 128 ** -0.5, True)
     o2, lse2 = oracle.forward(q, k, v, 128 ** -0.5, True)
     assert np.max(np.abs(o - o2)) < 0.1 and np.max(np.abs(lse - lse2)) < 0.1
+
+
+def _bf16(x):
+    """Round-to-nearest-even to bf16 (8 significant bits), in float64."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).double().numpy()
+
+
+@pytest.mark.parametrize("amp,N,d,causal", [(1.0, 300, 128, False), (8.0, 127, 80, True)])
+def test_bf16_probability_rounding_error_bound(amp, N, d, causal):
+    """The tolerance of the random-shape FP8 test: an otherwise exact forward
+    that rounds P to bf16 before P V (with the row sum on the rounded values)
+    and stores O in bf16 is off by at most 2^-8 * sum_j P_ij |V_j| + 2^-8 |O_i|
+    per element (relative rounding 2^-9 per value, 2^-9 more through the
+    row sum), well within 2e-2 * max(1, sum_j P_ij |V_j|). On the inputs of
+    that test's amplitude-8 draw of N = 127, d = 80 it misses
+    2e-2 * max(1, |O|): there |O| does not set the scale."""
+    from workloads import Workload, make_inputs
+    w = Workload(65, "f8r", 2, 1, N, d, "bf16", causal, 0.0, False, amp=amp)
+    inp = make_inputs(w, with_grad=False)
+    q, k, v = (inp[n][1].astype(np.float64) for n in ("q", "k", "v"))
+    o, _ = fp8.forward_fp8(q, k, v, w.scale, causal)
+    mag = fp8.forward_fp8(q, k, np.abs(v), w.scale, causal)[0]
+    qd = fp8.dequantize(*fp8.quantize(q, fp8.Q_BLOCK), fp8.Q_BLOCK)
+    kd = fp8.dequantize(*fp8.quantize(k, fp8.K_BLOCK), fp8.K_BLOCK)
+    worst_o = 0.0
+    for b in range(w.B):
+        s = oracle.attention_scores(qd[b, :, 0], kd[b, :, 0], w.scale, causal)
+        p = _bf16(np.exp(s - s.max(axis=1, keepdims=True)))
+        emu = _bf16((p @ v[b, :, 0]) / p.sum(axis=1, keepdims=True))
+        ob, mb = o[b, :, 0], mag[b, :, 0]
+        err = np.abs(emu - ob)
+        assert np.all(err <= 2.0 ** -8 * (mb + np.abs(ob)) + 1e-12)
+        assert np.max(err / (2e-2 * np.maximum(1.0, mb))) <= 0.5
+        worst_o = max(worst_o, float(np.max(err / (2e-2 * np.maximum(1.0, np.abs(ob))))))
+    if amp == 8.0:
+        assert worst_o > 1.0
