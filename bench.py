@@ -430,14 +430,17 @@ def run_gpu_fp8(cfg, steps, warmup, torch, fa):
 
 
 def kernel_source_digest():
-    """SHA-256 over the kernel sources (comments and blank lines removed, so
-    that only code counts) and the build flags: HBM traffic figures recorded
-    under profiles/ are valid only for this digest."""
+    """SHA-256 over the attention library's sources (comments and blank lines
+    removed, so that only code counts; the benchmark's clock-stamp source is
+    not part of it) and the build flags: HBM traffic figures recorded under
+    profiles/ are valid only for this digest."""
     import hashlib
     import re
     from exact_io_aware_72_amd import build as fa_build
     h = hashlib.sha256()
     for name in sorted(os.listdir(fa_build.CSRC)):
+        if name in fa_build.CLOCK_SOURCES:
+            continue
         with open(os.path.join(fa_build.CSRC, name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
