@@ -69,7 +69,8 @@ def test_bf16_item_over_4gib_sampled_rows_and_invariants():
         assert_close(f"LSE[h={h}]", lse[0, h, idx].double().cpu().numpy(), l_r, "bf16")
         assert_close(f"dQ[h={h}]", dq[0, idx, h].double().cpu().numpy(), dq_r, "bf16")
     # sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i per (h, column), within the
-    # random-walk bound of bf16 storage (each value carries 2^-9 relative).
+    # random-walk bound of bf16 storage (each value is off by up to 2^-8 of
+    # itself, far less on average; 8 * 2^-9 * root-sum-square is several sigma).
     for name, x, ref in (("sum dK", dk, None), ("sum dV", dv, do)):
         x64 = x[0].to(torch.float64)
         s = x64.sum(dim=0)

@@ -10,7 +10,11 @@ case, a constant 40 in one key column, x8 scaling), and dQ = scale dS K,
 dK = scale dS^T Q multiply any error of D by those norms. D is formed from the
 stored bf16 O, so dQ and dK are held to the bf16 bar plus the bound that this
 rounding propagates to them (see _stored_o_bounds); O, LSE and dV to the bar
-scaled by magnitude above 1."""
+scaled by magnitude above 1. The backward is also run alone, handed the
+oracle's stored O and LSE, against the oracle's backward reading D from that
+same O: there dQ, dK and dV are held to the scaled bar plus the bound of the
+bf16 rounding of the products' inputs (see _input_rounding_bounds), which an
+fp64 emulation shows to be the error these inputs produce."""
 import numpy as np
 import pytest
 
@@ -38,8 +42,8 @@ def _bf16(x):
 def _stored_o_bounds(q, k, v, do, scale, causal):
     """Extra error of dQ and dK that comes from forming D = rowsum(dO * O)
     from the stored bf16 O (as fa_backward does, O being its input) instead of
-    the exact O: each stored O element is off by up to 2^-9 of itself
-    (2^-8 taken, to cover the forward's own rounding), so D_i is off by
+    the exact O: each stored O element is off by up to 2^-8 of itself
+    (bf16 keeps 8 significant bits), so D_i is off by
     dD_i <= 2^-8 sum_c |dO_ic O_ic|; dS_ij = P_ij (dP_ij - D_i) then carries
     -P_ij dD_i, which gives dQ_i an error up to scale dD_i |(P K)_i| and dK_j
     one up to scale sum_i P_ij dD_i |Q_i|. Computed from oracle values only."""
@@ -57,6 +61,33 @@ def _stored_o_bounds(q, k, v, do, scale, causal):
             eq[b, :, h] = scale * dd[:, None] * np.abs(p @ kh)
             ek[b, :, h] = scale * (p * dd[:, None]).T @ np.abs(qh)
     return eq, ek
+
+
+def _input_rounding_bounds(q, k, v, do, o_st, scale, causal):
+    """Error that the bf16 rounding of the backward's matrix-product inputs
+    can add when D is read from the same stored O on both sides: dS is
+    rounded to bf16 (relative error up to 2^-8, the unit roundoff of 8
+    significant bits) before dQ = scale dS K and
+    dK = scale dS^T Q, and P to bf16 before dV = P^T dO. Per element:
+    scale 2^-8 (|dS| |K|) for dQ, scale 2^-8 (|dS|^T |Q|) for dK and
+    2^-8 (|P|^T |dO|) for dV, from oracle values (P, dP, D of o_st). An fp64
+    emulation of the dS rounding alone reproduces the kernel's dQ errors on
+    these inputs (max 0.0552 / 0.0563 / 0.0783 against 0.0552 / 0.0562 /
+    0.0783 for the monotone d = 64 and d = 128 and the shifted cases)."""
+    q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
+    B, N, H, d = q.shape
+    eq, ek, ev = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh, doh = q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h]
+            s = oracle.attention_scores(qh, kh, scale, causal)
+            _, _, lse = oracle.softmax_stats(s)
+            p = oracle.attention_probs(s, lse)
+            ds = np.abs(p * (doh @ vh.T - np.sum(doh * o_st[b, :, h], axis=1)[:, None]))
+            eq[b, :, h] = scale * 2.0 ** -8 * (ds @ np.abs(kh))
+            ek[b, :, h] = scale * 2.0 ** -8 * (ds.T @ np.abs(qh))
+            ev[b, :, h] = 2.0 ** -8 * (p.T @ np.abs(doh))
+    return eq, ek, ev
 
 
 def _check(name, got, ref, extra):
@@ -82,6 +113,20 @@ def _run_and_check(q, k, v, do, scale, causal, dtype="bf16"):
     eq, ek = _stored_o_bounds(q[1], k[1], v[1], do[1], scale, causal)
     _check("dQ", to_host(dq), dq_r, eq)
     _check("dK", to_host(dk), dk_r, ek)
+    # The backward alone: handed the oracle's O (bf16) and LSE (fp32), against
+    # the oracle's backward reading D from that same O. The stored-O term
+    # drops out; what remains beyond the bar is the bf16 rounding of the
+    # products' inputs (dS and P), bounded from oracle values.
+    o_st = torch.from_numpy(o_r).to(torch.bfloat16).cuda()
+    lse_st = torch.from_numpy(lse_r).to(torch.float32).cuda()
+    dq2, dk2, dv2 = fa.backward(dev["q"], dev["k"], dev["v"], o_st, dev["do"], lse_st, causal, 0.0, 0, scale)
+    torch.cuda.synchronize()
+    o_h = to_host(o_st)
+    rq, rk, rv, _ = oracle.backward(q[1], k[1], v[1], do[1], scale, causal, o=o_h)
+    iq, ik, iv = _input_rounding_bounds(q[1], k[1], v[1], do[1], o_h, scale, causal)
+    _check("dQ (oracle O)", to_host(dq2), rq, iq)
+    _check("dK (oracle O)", to_host(dk2), rk, ik)
+    _check("dV (oracle O)", to_host(dv2), rv, iv)
 
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -426,3 +426,36 @@ def test_input_recipe_is_deterministic():
     rng = np.random.default_rng(1099)
     x = (rng.standard_normal((1, 10, 3, 8), dtype=np.float32) * np.float32(0.5)).astype(np.float32)
     assert np.max(np.abs(a["q"][1] - x)) <= np.max(np.abs(x)) * 2.0 ** -8
+
+
+# --------------------------------------------------------------------------
+# Tolerance reasoning of the large-norm GPU stress tests: a backward that is
+# exact except for rounding dS to bf16 before dQ = scale dS K (as the kernels
+# feed the matrix cores) is off by at most scale 2^-8 (|dS| |K|) per element
+# (2^-8: the unit roundoff of 8 significant bits), the allowance those tests
+# add; on keys of norm 40 that error exceeds 2e-2 max(1, |dQ|) while staying
+# within half of the bar plus the allowance.
+def test_bf16_ds_rounding_bound_on_shifted_logits():
+    import torch
+    w = Workload(71, "shift", 1, 2, 257, 64, "bf16", True, 0.0, True)
+    inp = make_inputs(w, with_grad=True)
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).double().numpy()  # noqa: E731
+    q, k = inp["q"][1].copy(), inp["k"][1].copy()
+    q[..., 0], k[..., 0] = 16.0, 40.0
+    q, k, v, do = bf(q), bf(k), inp["v"][1].astype(np.float64), inp["do"][1].astype(np.float64)
+    o, lse = oracle.forward(q, k, v, w.scale, True)
+    o_st = bf(o)
+    ref = oracle.backward(q, k, v, do, w.scale, True, o=o_st)[0]
+    worst_plain = worst_bound = 0.0
+    for h in range(w.H):
+        s = A.attention_scores(q[0, :, h], k[0, :, h], w.scale, True)
+        p = A.attention_probs(s, lse[0, h])
+        ds = p * (do[0, :, h] @ v[0, :, h].T - np.sum(do[0, :, h] * o_st[0, :, h], axis=1)[:, None])
+        emu = w.scale * bf(ds) @ k[0, :, h]
+        err = np.abs(emu - ref[0, :, h])
+        assert np.all(err <= w.scale * 2.0 ** -8 * (np.abs(ds) @ np.abs(k[0, :, h])) + 1e-12)
+        worst_plain = max(worst_plain, float(np.max(err / (2e-2 * np.maximum(1.0, np.abs(ref[0, :, h]))))))
+        allow = 2e-2 * np.maximum(1.0, np.abs(ref[0, :, h])) + w.scale * 2.0 ** -8 * (np.abs(ds) @ np.abs(k[0, :, h]))
+        worst_bound = max(worst_bound, float(np.max(err / allow)))
+    assert worst_plain > 1.0
+    assert worst_bound <= 0.5

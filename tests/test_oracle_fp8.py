@@ -120,9 +120,11 @@ def _bf16(x):
 def test_bf16_probability_rounding_error_bound(amp, N, d, causal):
     """The tolerance of the random-shape FP8 test: an otherwise exact forward
     that rounds P to bf16 before P V (with the row sum on the rounded values)
-    and stores O in bf16 is off by at most 2^-8 * sum_j P_ij |V_j| + 2^-8 |O_i|
-    per element (relative rounding 2^-9 per value, 2^-9 more through the
-    row sum), well within 2e-2 * max(1, sum_j P_ij |V_j|). On the inputs of
+    and stores O in bf16 is off by at most 2^-8 * sum_j P_ij |V_j| + 2^-7 |O_i|
+    per element to first order (bf16 keeps 8 significant bits, relative
+    rounding up to 2^-8: once on each P in P V, once through the row sum of
+    the rounded P, once on the stored O), well within
+    2e-2 * max(1, sum_j P_ij |V_j|). On the inputs of
     that test's amplitude-8 draw of N = 127, d = 80 it misses
     2e-2 * max(1, |O|): there |O| does not set the scale."""
     from workloads import Workload, make_inputs
@@ -140,7 +142,7 @@ def test_bf16_probability_rounding_error_bound(amp, N, d, causal):
         emu = _bf16((p @ v[b, :, 0]) / p.sum(axis=1, keepdims=True))
         ob, mb = o[b, :, 0], mag[b, :, 0]
         err = np.abs(emu - ob)
-        assert np.all(err <= 2.0 ** -8 * (mb + np.abs(ob)) + 1e-12)
+        assert np.all(err <= 2.0 ** -8 * mb + 2.0 ** -7 * np.abs(ob) + 1e-12)
         assert np.max(err / (2e-2 * np.maximum(1.0, mb))) <= 0.5
         worst_o = max(worst_o, float(np.max(err / (2e-2 * np.maximum(1.0, np.abs(ob))))))
     if amp == 8.0:
