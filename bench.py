@@ -614,27 +614,34 @@ def power_sample_leg(seconds, sampler, torch, fa):
         fa.backward(x["q"], x["k"], x["v"], o, x["do"], lse, *args, dq=dq, dk=dk, dv=dv)
 
     phases = []
-    torch.cuda.synchronize()
-    t0 = time.time()
-    time.sleep(min(5.0, seconds / 2))
-    phases.append({"phase": "idle", "t0": t0, "t1": time.time(), "steps": 0})
-    for name, x in (("random inputs", dev), ("constant inputs", ones)):
-        for _ in range(20):
-            step(x)
+    try:
         torch.cuda.synchronize()
         t0 = time.time()
-        n = 0
-        while time.time() - t0 < seconds:
-            for _ in range(50):
+        time.sleep(min(5.0, seconds / 2))
+        phases.append({"phase": "idle", "t0": t0, "t1": time.time(), "steps": 0})
+        for name, x in (("random inputs", dev), ("constant inputs", ones)):
+            for _ in range(20):
                 step(x)
             torch.cuda.synchronize()
-            n += 50
-        t1 = time.time()
-        print(f"power leg: {name}: {n} steps in {t1 - t0:.1f} s", file=sys.stderr, flush=True)
-        phases.append({"phase": name, "t0": t0, "t1": t1, "steps": n})
-    with open(stop, "w"):
-        pass
-    proc.wait(timeout=60)
+            t0 = time.time()
+            n = 0
+            while time.time() - t0 < seconds:
+                for _ in range(50):
+                    step(x)
+                torch.cuda.synchronize()
+                n += 50
+            t1 = time.time()
+            print(f"power leg: {name}: {n} steps in {t1 - t0:.1f} s", file=sys.stderr, flush=True)
+            phases.append({"phase": name, "t0": t0, "t1": t1, "steps": n})
+    finally:
+        # the sampler always stops, also when the GPU work raised
+        with open(stop, "w"):
+            pass
+        try:
+            proc.wait(timeout=60)
+        except Exception:
+            proc.kill()
+            proc.wait()
     limits, samples = {}, []
     with open(out) as f:
         for ln in f:
@@ -689,6 +696,18 @@ def main():
         out, stop = os.path.join(tmp, "samples.txt"), os.path.join(tmp, "stop")
         open(out, "w").close()
         sampler = (subprocess.Popen([sys.executable, "-c", _SAMPLER, out, stop]), out, stop)
+
+        def _stop_sampler(proc=sampler[0], stop=stop):
+            if proc.poll() is None:
+                open(stop, "w").close()
+                try:
+                    proc.wait(timeout=60)
+                except Exception:
+                    proc.kill()
+                    proc.wait()
+
+        import atexit
+        atexit.register(_stop_sampler)  # also on early exits (no GPU, library missing)
     if a.gpus != 1:
         print("bench.py measures one GPU: the attention kernels run on a single device and this build "
               "has no multi-GPU path (heads or sequence chunks would be sharded across GPUs); "
