@@ -631,8 +631,20 @@ def power_sample_leg(seconds, sampler, torch, fa):
                 torch.cuda.synchronize()
                 n += 50
             t1 = time.time()
+            # forward and backward separately: event-timed medians over 20
+            # more steps, right after the timed window (same clock regime)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(20)]
+            for e in ev:
+                e[0].record()
+                fa.forward(x["q"], x["k"], x["v"], *args, out=o, lse=lse)
+                e[1].record()
+                fa.backward(x["q"], x["k"], x["v"], o, x["do"], lse, *args, dq=dq, dk=dk, dv=dv)
+                e[2].record()
+            torch.cuda.synchronize()
+            fms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+            bms = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
             print(f"power leg: {name}: {n} steps in {t1 - t0:.1f} s", file=sys.stderr, flush=True)
-            phases.append({"phase": name, "t0": t0, "t1": t1, "steps": n})
+            phases.append({"phase": name, "t0": t0, "t1": t1, "steps": n, "fwd_ms": fms, "bwd_ms": bms})
     finally:
         # the sampler always stops, also when the GPU work raised
         with open(stop, "w"):
@@ -659,7 +671,9 @@ def power_sample_leg(seconds, sampler, torch, fa):
              "gfx_clock_mhz": float(np.median([c for _, c in sel])) if sel else None}
         if ph["steps"]:
             ms = (ph["t1"] - ph["t0"]) * 1e3 / ph["steps"]
-            d.update({"steps": ph["steps"], "ms_per_step": ms, "tflops": (fwd_f + bwd_f) / (ms * 1e-3) / 1e12})
+            d.update({"steps": ph["steps"], "ms_per_step": ms, "tflops": (fwd_f + bwd_f) / (ms * 1e-3) / 1e12,
+                      "fwd_ms": ph["fwd_ms"], "fwd_tflops": fwd_f / (ph["fwd_ms"] * 1e-3) / 1e12,
+                      "bwd_ms": ph["bwd_ms"], "bwd_tflops": bwd_f / (ph["bwd_ms"] * 1e-3) / 1e12})
         res.append(d)
     return {"power_sample": {"workload": w.name, "phases": res, "power_limits_w": limits,
                              "source": "amd-smi metric (socket power, mean GFX clock over the XCDs), "
