@@ -81,7 +81,7 @@ class ClockStamps:
 
     MIN_REGION_MS = 2.0
 
-    def __init__(self, torch, blocks=64):
+    def __init__(self, torch, blocks=256):
         import ctypes
         self.torch = torch
         self.blocks = blocks
