@@ -743,7 +743,8 @@ __global__ __launch_bounds__(64 * kF32Waves) void fwd_f32_kernel(FwdParamsF p) {
 // pay for head dims up to 80 from N = 8192 (d = 64: 16% faster at N = 8192;
 // d = 80: 5% at N = 8192, 11% at N = 32768) and for the vector-ALU-bound
 // dropout kernels at N >= 32768 (d = 128: 6% at N = 65536), and cost the
-// d = 128 kernels without dropout 7-10% (N = 8192..32768).
+// d = 128 kernels without dropout 6-10% (N = 8192..32768; 6-8% at N = 8192
+// in runs interleaved with the four-wave kernel).
 template <int D, bool DROP>
 bool fwd_eight_waves(int N) {
   return (D <= 80 && N >= 8192) || (DROP && N >= 32768);
@@ -753,7 +754,7 @@ bool fwd_eight_waves(int N) {
 // head dims up to 80 without dropout, whose kernels fit in 128 registers:
 // each K/V tile then serves twice the queries of the eight-wave group, which
 // halves the K/V bytes fetched from beyond L2 (N = 32768 d = 80: 4.2 to
-// 2.2 GB per launch, 1.8% faster). The d = 128 and dropout kernels need
+// 2.2 GB per launch, 2-2.5% faster). The d = 128 and dropout kernels need
 // more than 128 registers and keep eight waves.
 template <int D, bool DROP>
 bool fwd_sixteen_waves(int N) {
