@@ -111,3 +111,41 @@ def test_splitkv_and_fp8(monkeypatch):
         return o, lse, o8, lse8
 
     _same(*_both(run, monkeypatch))
+
+
+# Launch forms that reuse a work-group's LDS stages across two blocks (block
+# pairs per work-group: forward from N = 32768 and for packed batches, the
+# eight-wave dQ from N = 32768), the sixteen-wave forward groups, and the
+# resident pairs across the work-groups of a CU (a grid the device holds at
+# once).
+@pytest.mark.parametrize("B,H,N,d,causal,p", [
+    (1, 2, 32768, 80, True, 0.0),    # sixteen-wave forward with block pairs; paired eight-wave dQ
+    (1, 1, 32800, 128, True, 0.1),   # eight-wave dropout forward with block pairs, ragged last group
+    (1, 2, 32768, 64, False, 0.0),   # sixteen-wave forward without the causal mask
+    (4, 16, 2048, 64, True, 0.0),    # resident pairs (four work-groups per CU)
+])
+def test_paired_and_wide_launches(B, H, N, d, causal, p, monkeypatch):
+    q, k, v, do = (_rand((B, N, H, d), 500 + i) for i in range(4))
+
+    def run():
+        o, lse = fa.forward(q, k, v, causal, p, 13)
+        dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal, p, 13)
+        return o, lse, dq, dk, dv
+
+    _same(*_both(run, monkeypatch))
+
+
+def test_varlen_block_pairs(monkeypatch):
+    # a causal packed grid larger than the device holds: pairs of one
+    # sequence's blocks per work-group, with empty and one-row sequences
+    lens = [1100, 0, 1, 900, 257, 1024, 640, 129, 1000, 3, 768, 512]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32).cuda()
+    T, H, d = sum(lens), 32, 128
+    q, k, v, do = (_rand((T, H, d), 600 + i) for i in range(4))
+
+    def run():
+        o, lse = fa.forward_varlen(q, k, v, cu, max(lens), True, 0.0, 5)
+        dq, dk, dv = fa.backward_varlen(q, k, v, o, do, lse, cu, max(lens), True, 0.0, 5)
+        return o, lse, dq, dk, dv
+
+    _same(*_both(run, monkeypatch))
